@@ -1,0 +1,290 @@
+"""Benchmark of grouped convolution backward-weight (wgrad) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs c2,c5,...]
+
+One step is one pass of the whole path (the main kernel, plus the reduce /
+convert kernel when the plan splits the reduction) over one batch of
+synthetic, seeded input already resident in HBM. The headline workload is
+the dense split-K shape (G=1 N=32 56x56 C=64 K=64 3x3 s1 p1, bf16): value =
+its TFLOP/s over exactly K timed steps. Every other configuration is timed
+the same way and reported under "per_config".
+
+Honest memory: each configuration cycles through enough copies of its inputs
+(> 512 MB in total) that no step finds its inputs in the 256 MB MALL left
+behind by the previous steps. Steps are replayed from HIP graphs (captured
+through torch) so that the host's launch rate does not set the time.
+
+Dominant-kernel roofline: per-launch durations of the main kernel come from
+HIP events recorded on the launch stream around wgrad_run_stage(1) while the
+stream is kept busy ahead of the host (so events and kernels run back to
+back); achieved = algorithmic FLOPs or bytes per launch / that duration.
+
+cpu_baseline: the CPU oracle (fp64 direct loop, OpenMP) over the full
+headline dW, timed on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_16 = 2.5e15     # dense bf16/fp16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12         # HBM3E, B/s
+METRIC = "wgrad TFLOP/s (GB/s for depthwise) and % of roofline, 1 MI355X"
+HEADLINE = "c2"
+ROTATE_BYTES = 600 * 2 ** 20
+
+
+def algorithmic(cfg, info):
+    """FLOPs = 2*G*(K/G)*(C/G)*Y*X*N*Ho*Wo; bytes = |X| + |dY| + |dW|, each once."""
+    G = cfg["G"]
+    taps = 1
+    for f in cfg["filt_len"][: cfg["ndim"]]:
+        taps *= f
+    R = info["gemm_k"]
+    flops = 2 * G * (cfg["K"] // G) * (cfg["C"] // G) * taps * R
+    nx = cfg["N"] * math.prod(cfg["in_len"][: cfg["ndim"]]) * cfg["C"]
+    ndy = R * cfg["K"]
+    out_bytes = 4 if cfg["out_dtype"] == "fp32" else 2
+    nbytes = 2 * (nx + ndy) + out_bytes * cfg["K"] * taps * (cfg["C"] // G)
+    return flops, nbytes
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "grouped_convolution_backward_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".cpp", ".hpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel_prefix):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        e = t[workload]
+        if e.get("source_hash") != kernel_source_hash() or not e.get("kernel", "").startswith(kernel_prefix):
+            return None
+        return e["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+class Case:
+    def __init__(self, torch, gcb, workloads, name, cfg, overrides=None):
+        self.name, self.cfg = name, cfg
+        self.torch = torch
+        self.plan = gcb.Plan(cfg, **(overrides or {}))
+        x_bits, dy_bits = workloads.inputs(cfg)
+        dt = torch.bfloat16 if cfg["in_dtype"] == "bf16" else torch.float16
+        out_t = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[cfg["out_dtype"]]
+        import numpy as np
+        x0 = torch.from_numpy(x_bits.view(np.int16).reshape(-1).copy()).view(dt).cuda()
+        dy0 = torch.from_numpy(dy_bits.view(np.int16).reshape(-1).copy()).view(dt).cuda()
+        set_bytes = (x0.numel() + dy0.numel()) * 2
+        self.nsets = max(2, min(64, math.ceil(ROTATE_BYTES / max(1, set_bytes))))
+        self.xs = [x0] + [x0.clone() for _ in range(self.nsets - 1)]
+        self.dys = [dy0] + [dy0.clone() for _ in range(self.nsets - 1)]
+        self.dw = torch.empty(self.plan.dw_shape(), dtype=out_t, device="cuda")
+        self.ws = self.plan.new_workspace() if self.plan.workspace_bytes else None
+        self.flops, self.bytes = algorithmic(cfg, self.plan.info)
+
+    def step(self, i, stage=0):
+        j = i % self.nsets
+        self.plan.run(self.xs[j], self.dys[j], self.dw, self.ws, stage=stage)
+
+    def capture(self, nsteps):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(nsteps):
+                    self.step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        return g
+
+    def time_steps(self, steps, warmup, use_graphs=True):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        if use_graphs:
+            full = self.capture(self.nsets)
+            rem = steps % self.nsets
+            tail = self.capture(rem) if rem else None
+            full.replay()                      # untimed: graph upload
+            if tail is not None:
+                tail.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps // self.nsets):
+                full.replay()
+            if tail is not None:
+                tail.replay()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+        else:
+            t0 = time.perf_counter()
+            for i in range(steps):
+                self.step(i)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+        return (t1 - t0) / steps
+
+    def kernel_times(self, launches=100):
+        """Average per-launch durations (s) of stage 1 and stage 2 from HIP
+        events on the launch stream, with the stream kept busy ahead."""
+        torch = self.torch
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.002 * launches / 10 + 1e6))   # queue ahead of the GPU
+        for i in range(launches):
+            ev[i][0].record()
+            self.step(i, stage=1)
+            ev[i][1].record()
+            self.step(i, stage=2)
+            ev[i][2].record()
+        torch.cuda.synchronize()
+        main = sum(e[0].elapsed_time(e[1]) for e in ev) / launches * 1e-3
+        red = sum(e[1].elapsed_time(e[2]) for e in ev) / launches * 1e-3
+        return main, red
+
+    def row(self, sec_per_step, t_main, t_red):
+        flops, nbytes = self.flops, self.bytes
+        floor = max(flops / PEAK_MFMA_16, nbytes / PEAK_HBM)
+        return {
+            "kernel": self.plan.name,
+            "us_per_step": round(sec_per_step * 1e6, 3),
+            "tflops": round(flops / sec_per_step / 1e12, 3),
+            "gbps": round(nbytes / sec_per_step / 1e9, 1),
+            "frac_mfma_peak": round(flops / sec_per_step / PEAK_MFMA_16, 4),
+            "frac_hbm_peak": round(nbytes / sec_per_step / PEAK_HBM, 4),
+            "frac_attainable": round(floor / sec_per_step, 4),
+            "bound": "mfma" if flops / PEAK_MFMA_16 >= nbytes / PEAK_HBM else "hbm",
+            "main_kernel_us": round(t_main * 1e6, 3),
+            "reduce_kernel_us": round(t_red * 1e6, 3),
+            "split_k": self.plan.info["split_k"],
+            "group_merge": self.plan.info["group_merge"],
+            "input_sets": self.nsets,
+        }
+
+
+def cpu_baseline(workloads, cfg):
+    import oracle
+    x_bits, dy_bits = workloads.inputs(cfg)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    dw, _ = oracle.wgrad(cfg, x_bits, dy_bits)
+    dt = time.perf_counter() - t0
+    G = cfg["G"]
+    taps = math.prod(cfg["filt_len"][: cfg["ndim"]])
+    R = cfg["N"] * math.prod(cfg["out_len"][: cfg["ndim"]])
+    flops = 2 * G * (cfg["K"] // G) * (cfg["C"] // G) * taps * R
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"full dW of the headline workload ({dw.size} elements, {flops/2:.3g} MACs) in "
+                      f"{dt:.2f} s, fp64, {threads} OpenMP threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--configs", default="c1,c2,c3,c4a,c4b,c5")
+    ap.add_argument("--eager", action="store_true", help="launch steps one by one (for profilers)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-merge", action="store_true", help="also time the depthwise shape over Gm and S")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+    import grouped_convolution_backward_amd as gcb
+    import workloads
+
+    torch.cuda.init()
+    names = [n for n in args.configs.split(",") if n]
+    if HEADLINE not in names:
+        names.insert(0, HEADLINE)
+    per = {}
+    head = None
+    for name in names:
+        cfg = workloads.CONFIGS[name]
+        case = Case(torch, gcb, workloads, name, cfg)
+        sec = case.time_steps(args.steps, args.warmup, use_graphs=not args.eager)
+        t_main, t_red = case.kernel_times(min(args.steps, 100))
+        per[name] = case.row(sec, t_main, t_red)
+        print(f"[bench] {name}: {per[name]}", file=sys.stderr, flush=True)
+        if name == HEADLINE:
+            head = (case, sec, t_main)
+        else:
+            del case
+        torch.cuda.empty_cache()
+    sweep = {}
+    if args.sweep_merge:
+        cfg = workloads.CONFIGS["c5"]
+        for gm in (1, 2, 4, 8):
+            for s in (0, 8, 32, 128):
+                case = Case(torch, gcb, workloads, "c5", cfg, {"variant": gcb.VARIANT_MFMA, "group_merge": gm, "split_k": s})
+                sec = case.time_steps(max(20, args.steps // 4), 5, use_graphs=not args.eager)
+                sweep[f"mfma_gm{gm}_spk{case.plan.info['split_k']}"] = round(sec * 1e6, 2)
+                del case
+                torch.cuda.empty_cache()
+        print(f"[bench] c5 merge sweep (us): {sweep}", file=sys.stderr, flush=True)
+
+    case, sec, t_main = head
+    cfg = case.cfg
+    flops, nbytes = case.flops, case.bytes
+    hb = per[HEADLINE]
+    bound = hb["bound"]
+    if bound == "mfma":
+        achieved, peak, unit = flops / t_main / 1e12, PEAK_MFMA_16 / 1e12, "TFLOP/s"
+    else:
+        achieved, peak, unit = nbytes / t_main / 1e9, PEAK_HBM / 1e9, "GB/s"
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(HEADLINE, case.plan.name.split("_spk")[0]),
+            "kernel": case.plan.name, "kernel_us": round(t_main * 1e6, 3)}
+    out = {
+        "metric": METRIC,
+        "value": round(flops / sec / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dense split-K wgrad G=1 N=32 56x56 C=64 K=64 3x3 s1 p1 bf16 (NHWGC/NHWGK/GKYXC)",
+                   "G": 1, "N": 32, "C": 64, "K": 64, "H": 56, "W": 56, "filter": "3x3", "stride": 1, "pad": 1,
+                   "gemm": "M=64 N=576 K=100352", "parallelism": "single GPU"},
+        "roofline": roof,
+        "per_config": per,
+    }
+    if sweep:
+        out["c5_merge_sweep_us"] = sweep
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(workloads, cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

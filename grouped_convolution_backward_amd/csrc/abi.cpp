@@ -1,0 +1,146 @@
+// extern "C" entry points declared in include/wgrad.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "wgrad_internal.hpp"
+
+struct wgrad_plan_s {
+    wgrad::Plan plan;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int code, const std::string& msg) {
+    g_last_error = msg;
+    return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int wgrad_plan(const wgrad_problem* problem, const wgrad_overrides* overrides, int hip_device,
+               wgrad_plan_t** out) {
+    g_last_error.clear();
+    if (!problem || !out) return set_error(WGRAD_ERR_INVALID_ARG, "problem and out must not be NULL");
+    *out = nullptr;
+    wgrad::DeviceModel dev{256, 8};   // MI355X: 256 CUs in 8 XCDs
+    if (hip_device >= 0) {
+        hipDeviceProp_t prop;
+        hipError_t e = hipGetDeviceProperties(&prop, hip_device);
+        if (e != hipSuccess)
+            return set_error(WGRAD_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+        if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+            return set_error(WGRAD_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName +
+                                                        ", kernels are built for gfx950 only");
+        dev.num_cus = prop.multiProcessorCount;
+    }
+    std::string msg;
+    wgrad_plan_s* p = new (std::nothrow) wgrad_plan_s();
+    if (!p) return set_error(WGRAD_ERR_INVALID_ARG, "out of host memory");
+    int rc = wgrad::build_plan(*problem, overrides, dev, p->plan, &msg);
+    if (rc != WGRAD_OK) {
+        delete p;
+        return set_error(rc, msg);
+    }
+    *out = p;
+    return WGRAD_OK;
+}
+
+size_t wgrad_workspace_bytes(const wgrad_plan_t* plan) {
+    return plan ? static_cast<size_t>(plan->plan.info.workspace_bytes) : 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_stages(const wgrad_plan_t* plan, int first, int last, const void* x, const void* dy, void* dw,
+               void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (!plan) return set_error(WGRAD_ERR_INVALID_ARG, "plan is NULL");
+    const wgrad::Plan& P = plan->plan;
+    const bool empty_in = P.info.gemm_k == 0;
+    if (!dw) return set_error(WGRAD_ERR_INVALID_ARG, "dw is NULL");
+    if (!empty_in && (!x || !dy)) return set_error(WGRAD_ERR_INVALID_ARG, "x and dy must not be NULL");
+    if ((x && !aligned16(x)) || (dy && !aligned16(dy)) || !aligned16(dw))
+        return set_error(WGRAD_ERR_INVALID_ARG, "x, dy and dw must be 16-byte aligned");
+    const size_t need = static_cast<size_t>(P.info.workspace_bytes);
+    if (need) {
+        if (!ws) return set_error(WGRAD_ERR_INVALID_ARG, "workspace is NULL but the plan needs " + std::to_string(need) + " bytes");
+        if (ws_bytes < need)
+            return set_error(WGRAD_ERR_INVALID_ARG, "workspace of " + std::to_string(ws_bytes) +
+                                                        " bytes is smaller than the " + std::to_string(need) + " needed");
+        if (!aligned16(ws)) return set_error(WGRAD_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    }
+    int e = hipSuccess;
+    if (first <= 1) {
+        void* main_out = P.info.split_k > 1 ? ws : dw;
+        if (P.variant == WGRAD_VARIANT_DEPTHWISE) {
+            wgrad::DwArgs a = P.dwk;
+            a.x = static_cast<const uint16_t*>(x);
+            a.dy = static_cast<const uint16_t*>(dy);
+            a.out = main_out;
+            e = wgrad::launch_depthwise(P, a, stream);
+        } else {
+            wgrad::MfmaArgs a = P.mfma;
+            a.x = static_cast<const uint16_t*>(x);
+            a.dy = static_cast<const uint16_t*>(dy);
+            a.out = main_out;
+            e = wgrad::launch_mfma(P, a, stream);
+        }
+        if (e != hipSuccess)
+            return set_error(WGRAD_ERR_HIP, std::string("main kernel launch: ") + hipGetErrorString((hipError_t)e));
+    }
+    if (last >= 2 && P.info.split_k > 1) {
+        wgrad::ReduceArgs r = P.red;
+        r.ws = static_cast<const float*>(ws);
+        r.dw = dw;
+        e = wgrad::launch_reduce(r, P.info.grid_reduce, stream);
+        if (e != hipSuccess)
+            return set_error(WGRAD_ERR_HIP, std::string("reduce kernel launch: ") + hipGetErrorString((hipError_t)e));
+    }
+    return WGRAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wgrad_run(const wgrad_plan_t* plan, const void* x, const void* dy, void* dw, void* ws, size_t ws_bytes,
+              void* stream) {
+    return run_stages(plan, 1, 2, x, dy, dw, ws, ws_bytes, stream);
+}
+
+int wgrad_run_stage(const wgrad_plan_t* plan, int stage, const void* x, const void* dy, void* dw, void* ws,
+                    size_t ws_bytes, void* stream) {
+    if (stage != 1 && stage != 2) return set_error(WGRAD_ERR_INVALID_ARG, "stage must be 1 or 2");
+    return run_stages(plan, stage, stage, x, dy, dw, ws, ws_bytes, stream);
+}
+
+int wgrad_plan_query(const wgrad_plan_t* plan, wgrad_plan_info* info) {
+    g_last_error.clear();
+    if (!plan || !info) return set_error(WGRAD_ERR_INVALID_ARG, "plan and info must not be NULL");
+    *info = plan->plan.info;
+    return WGRAD_OK;
+}
+
+const char* wgrad_plan_describe(const wgrad_plan_t* plan) {
+    return plan ? plan->plan.name.c_str() : "";
+}
+
+void wgrad_plan_destroy(wgrad_plan_t* plan) { delete plan; }
+
+const char* wgrad_last_error(void) { return g_last_error.c_str(); }
+
+const char* wgrad_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,275 @@
+// Host planner: validation, output size, kernel family, tile, split-K degree
+// S, group-merge degree Gm and the kernel-argument blocks. Pure C++ (no HIP
+// calls), so it runs and is tested on machines without a GPU.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "wgrad_internal.hpp"
+
+namespace wgrad {
+
+const TileShape* find_tile(int id) {
+    for (const auto& t : kTiles)
+        if (t.id == id) return &t;
+    return nullptr;
+}
+
+namespace {
+
+constexpr int64_t kMax31 = (int64_t{1} << 31) - 1;
+
+int fail(std::string* msg, int code, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
+int fail(std::string* msg, int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (msg) *msg = buf;
+    return code;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+int64_t gcd64(int64_t a, int64_t b) { while (b) { int64_t t = a % b; a = b; b = t; } return a; }
+
+// Geometry with 1D folded into 2D (h axis of size 1).
+struct Geo {
+    int64_t Hi, Wi, Y, X, sh, sw, dh, dw, ph, pw, Ho, Wo;
+};
+
+// Split-K degree in the manner of a groups-aware occupancy target: enough
+// workgroups for `target` per CU across the whole grid, clamped to the number
+// of K tiles and a workspace budget, and only then snapped so that the grid is
+// a multiple of the XCD count (clamping after the snap would undo it).
+int64_t choose_split(int64_t base_grid, int64_t k_tiles, int64_t slice_bytes, int64_t input_bytes,
+                     const DeviceModel& dev, int64_t target_per_cu) {
+    int64_t want = ceil_div(target_per_cu * dev.num_cus, std::max<int64_t>(1, base_grid));
+    // the workspace round trip (write + read of S fp32 slices) should not
+    // exceed the unavoidable input traffic
+    int64_t ws_cap = std::max<int64_t>(1, (input_bytes / 2) / std::max<int64_t>(1, slice_bytes));
+    int64_t cap = std::max<int64_t>(1, std::min<int64_t>({k_tiles, ws_cap, 65535}));
+    int64_t s = std::max<int64_t>(1, std::min(want, cap));
+    if (s > 1) {
+        int64_t step = dev.num_xcds / gcd64(base_grid, dev.num_xcds);
+        int64_t up = ceil_div(s, step) * step;
+        int64_t down = (s / step) * step;
+        if (up <= cap) s = up;
+        else if (down >= 1) s = down;
+    }
+    return s;
+}
+
+}  // namespace
+
+int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceModel& dev, Plan& out,
+               std::string* msg) {
+    const int E = WGRAD_ERR_INVALID_ARG, U = WGRAD_ERR_UNSUPPORTED;
+    if (p.ndim != 1 && p.ndim != 2) return fail(msg, E, "ndim must be 1 or 2 (got %d)", p.ndim);
+    if (p.reserved != 0) return fail(msg, E, "reserved field must be 0");
+    if (p.in_dtype != WGRAD_BF16 && p.in_dtype != WGRAD_FP16)
+        return fail(msg, E, "in_dtype must be BF16 or FP16");
+    if (p.out_dtype != p.in_dtype && p.out_dtype != WGRAD_FP32)
+        return fail(msg, E, "out_dtype must equal in_dtype or be FP32");
+    if (p.G < 1 || p.C < 1 || p.K < 1 || p.N < 0)
+        return fail(msg, E, "need G, C, K >= 1 and N >= 0");
+    if (p.C % p.G || p.K % p.G)
+        return fail(msg, E, "C (%lld) and K (%lld) must be multiples of G (%lld)", (long long)p.C,
+                    (long long)p.K, (long long)p.G);
+    for (int i = 0; i < p.ndim; ++i) {
+        if (p.in_len[i] < 1 || p.filt_len[i] < 1 || p.stride[i] < 1 || p.dilation[i] < 1)
+            return fail(msg, E, "lengths, strides and dilations must be >= 1 (axis %d)", i);
+        if (p.pad_lo[i] < 0 || p.pad_hi[i] < 0) return fail(msg, E, "pads must be >= 0 (axis %d)", i);
+    }
+    Geo g{};
+    if (p.ndim == 2) {
+        g = Geo{p.in_len[0], p.in_len[1], p.filt_len[0], p.filt_len[1], p.stride[0], p.stride[1],
+                p.dilation[0], p.dilation[1], p.pad_lo[0], p.pad_lo[1], 0, 0};
+        int64_t nh = p.in_len[0] + p.pad_lo[0] + p.pad_hi[0] - p.dilation[0] * (p.filt_len[0] - 1) - 1;
+        int64_t nw = p.in_len[1] + p.pad_lo[1] + p.pad_hi[1] - p.dilation[1] * (p.filt_len[1] - 1) - 1;
+        if (nh < 0 || nw < 0) return fail(msg, E, "empty output: the dilated filter exceeds the padded input");
+        g.Ho = nh / p.stride[0] + 1;
+        g.Wo = nw / p.stride[1] + 1;
+    } else {
+        g = Geo{1, p.in_len[0], 1, p.filt_len[0], 1, p.stride[0], 1, p.dilation[0], 0, p.pad_lo[0], 1, 0};
+        int64_t nw = p.in_len[0] + p.pad_lo[0] + p.pad_hi[0] - p.dilation[0] * (p.filt_len[0] - 1) - 1;
+        if (nw < 0) return fail(msg, E, "empty output: the dilated filter exceeds the padded input");
+        g.Wo = nw / p.stride[0] + 1;
+    }
+    const int64_t cpg = p.C / p.G, kpg = p.K / p.G;
+    const int64_t R = p.N * g.Ho * g.Wo;
+    const int64_t nx = p.N * g.Hi * g.Wi * p.C;
+    const int64_t ndy = R * p.K;
+    const int64_t ndw = p.K * g.Y * g.X * cpg;
+    if (nx > kMax31 || ndy > kMax31 || ndw > kMax31 || R > kMax31 || g.Hi > kMax31 || g.Wi > kMax31)
+        return fail(msg, E, "tensor element offsets must fit in 31 bits");
+    // index arithmetic on the padded input also stays in 31 bits
+    if ((g.Ho * g.sh + g.Y * g.dh) > kMax31 || (g.Wo * g.sw + g.X * g.dw) > kMax31)
+        return fail(msg, E, "spatial index range must fit in 31 bits");
+
+    wgrad_overrides o{};
+    if (ov) o = *ov;
+    if (o.split_k < 0 || o.group_merge < 0 || o.variant < 0 || o.tile < 0)
+        return fail(msg, E, "overrides must be >= 0");
+
+    out = Plan{};
+    out.prob = p;
+    out.in_f16 = p.in_dtype == WGRAD_FP16;
+    wgrad_plan_info& info = out.info;
+    info.out_len[0] = p.ndim == 2 ? g.Ho : g.Wo;
+    info.out_len[1] = p.ndim == 2 ? g.Wo : 0;
+    info.gemm_m = kpg;
+    info.gemm_n = cpg * g.Y * g.X;
+    info.gemm_k = R;
+    info.num_cus = dev.num_cus;
+    const int out_final = p.out_dtype == WGRAD_BF16 ? OUT_BF16 : p.out_dtype == WGRAD_FP16 ? OUT_FP16 : OUT_FP32;
+    const int64_t in_bytes = 2 * (nx + ndy);
+    const char* dname = out.in_f16 ? "fp16" : "bf16";
+
+    // ---- kernel family
+    const bool dw_shape = cpg == 1 && kpg == 1 && p.C % 8 == 0;
+    const bool dw_filter = (g.Y == 3 && g.X == 3) || (g.Y == 1 && (g.X == 3 || g.X == 5));
+    int variant = o.variant;
+    if (variant == WGRAD_VARIANT_AUTO) variant = (dw_shape && dw_filter) ? WGRAD_VARIANT_DEPTHWISE : WGRAD_VARIANT_MFMA;
+    if (variant == WGRAD_VARIANT_DEPTHWISE && !(dw_shape && dw_filter))
+        return fail(msg, U, "depthwise variant needs C/G = K/G = 1, C %% 8 == 0 and a 3x3, 1x3 or 1x5 filter");
+    if (variant != WGRAD_VARIANT_MFMA && variant != WGRAD_VARIANT_DEPTHWISE)
+        return fail(msg, E, "unknown variant %d", variant);
+    out.variant = variant;
+    info.variant = variant;
+
+    char name[256];
+    if (variant == WGRAD_VARIANT_DEPTHWISE) {
+        if (o.group_merge > 1) return fail(msg, U, "group_merge applies to the MFMA variant only");
+        if (o.tile) return fail(msg, U, "tile applies to the MFMA variant only");
+        DwArgs& a = out.dwk;
+        a = DwArgs{};
+        a.C = (int32_t)p.C;
+        a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo;
+        a.Y = (int32_t)g.Y; a.Xf = (int32_t)g.X;
+        a.sh = (int32_t)g.sh; a.sw = (int32_t)g.sw; a.dh = (int32_t)g.dh; a.dw = (int32_t)g.dw;
+        a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
+        a.R = (int32_t)R;
+        int64_t vecs = p.C / 8;
+        int cl = 8;
+        while (vecs % cl) cl >>= 1;
+        a.cl = cl;
+        a.cblocks = (int32_t)(vecs / cl);
+        const int pl = 256 / cl;
+        int64_t S;
+        const int64_t slice_bytes = ndw * 4;
+        if (o.split_k) {
+            S = o.split_k;
+        } else {
+            int64_t max_s = std::max<int64_t>(1, ceil_div(R, pl));   // at least one position per lane
+            S = choose_split(a.cblocks, max_s, slice_bytes, in_bytes, dev, 4);
+        }
+        if (R == 0) S = 1;
+        int64_t kslice = std::max<int64_t>(1, ceil_div(R, S));
+        if (R > 0) S = ceil_div(R, kslice);
+        if (S > 65535) return fail(msg, U, "split_k too large");
+        a.S = (int32_t)S;
+        a.kslice = (int32_t)kslice;
+        a.total_wg = (int32_t)(a.cblocks * S);
+        a.out_mode = S == 1 ? out_final : OUT_WORKSPACE;
+        a.slice_elems = (int32_t)ndw;
+        a.mWo = make_magic((uint32_t)g.Wo);
+        a.mHo = make_magic((uint32_t)g.Ho);
+        out.dw_tile_y = (int)g.Y;
+        out.dw_tile_x = (int)g.X;
+        info.split_k = (int32_t)S;
+        info.group_merge = 8 * cl;   // channels (groups) one workgroup covers
+        info.vector_width = 8;
+        info.grid_main = a.total_wg;
+        info.workspace_bytes = S > 1 ? S * ndw * 4 : 0;
+        snprintf(name, sizeof name, "wgrad_dw_%s_%lldx%lld_cl%d_spk%lld_gm%d", dname, (long long)g.Y,
+                 (long long)g.X, cl, (long long)S, 8 * cl);
+    } else {
+        // ---- group merge degree
+        int64_t Gm = o.group_merge;
+        if (Gm) {
+            if (!is_pow2(Gm) || p.G % Gm)
+                return fail(msg, U, "group_merge %lld must be a power of two dividing G = %lld", (long long)Gm,
+                            (long long)p.G);
+        } else {
+            // fill the 16-row MFMA edge with adjacent groups, at most 8 of them
+            Gm = 1;
+            while (Gm * 2 <= 8 && Gm * kpg < 16 && p.G % (Gm * 2) == 0) Gm *= 2;
+        }
+        const int64_t Mm = Gm * kpg, Nm = Gm * cpg * g.Y * g.X;
+        if (Mm > kMax31 || Nm > kMax31) return fail(msg, E, "merged GEMM too large");
+        // ---- load vector width: a vector stays inside one channel run and
+        // every run starts on a multiple of it
+        int V = 8;
+        while (V > 1 && ((Gm * kpg) % V || (Gm * cpg) % V || p.K % V || p.C % V)) V >>= 1;
+        // ---- tile
+        int tile_id = o.tile;
+        if (!tile_id) tile_id = Mm <= 16 ? 5 : Mm <= 32 ? 4 : Mm <= 64 ? 2 : 3;
+        const TileShape* t = find_tile(tile_id);
+        if (!t) return fail(msg, U, "unknown tile id %d", tile_id);
+        const int64_t tiles_m = ceil_div(Mm, t->bm), tiles_n = ceil_div(Nm, t->bn);
+        const int64_t gblocks = p.G / Gm;
+        const int64_t base = tiles_m * tiles_n * gblocks;
+        const int64_t k_tiles = std::max<int64_t>(1, ceil_div(R, t->bk));
+        int64_t S = o.split_k ? o.split_k : choose_split(base, k_tiles, ndw * 4, in_bytes, dev, 2);
+        if (R == 0) S = 1;
+        // slices hold whole K tiles, so S slices may round to fewer non-empty
+        // ones; when choosing automatically, step down to a degree whose
+        // effective count keeps the grid a multiple of the XCD count
+        auto slice_len = [&](int64_t s) { return std::max<int64_t>(1, ceil_div(ceil_div(R, s), t->bk)) * t->bk; };
+        auto effective = [&](int64_t s) { return R > 0 ? ceil_div(R, slice_len(s)) : int64_t{1}; };
+        if (!o.split_k && S > 1) {
+            const int64_t step = dev.num_xcds / gcd64(base, dev.num_xcds);
+            for (int64_t s = S; s >= 2; --s) {
+                const int64_t e = effective(s);
+                if (e % step == 0) { S = s; break; }
+                if (s < S / 2) break;   // do not give up more than half the parallelism
+            }
+        }
+        int64_t kslice = slice_len(S);
+        S = effective(S);
+        if (S > 65535 || base * S > kMax31) return fail(msg, U, "grid too large");
+        MfmaArgs& a = out.mfma;
+        a = MfmaArgs{};
+        a.Ktot = (int32_t)p.K; a.Ctot = (int32_t)p.C;
+        a.kpg = (int32_t)kpg; a.cpg = (int32_t)cpg; a.Gm = (int32_t)Gm;
+        a.gkpg = (int32_t)(Gm * kpg); a.gcpg = (int32_t)(Gm * cpg);
+        a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo;
+        a.Xf = (int32_t)g.X;
+        a.sh = (int32_t)g.sh; a.sw = (int32_t)g.sw; a.dh = (int32_t)g.dh; a.dw = (int32_t)g.dw;
+        a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
+        a.R = (int32_t)R;
+        a.Mm = (int32_t)Mm; a.Nm = (int32_t)Nm;
+        a.row_len = (int32_t)(g.Y * g.X * cpg);
+        a.tiles_m = (int32_t)tiles_m; a.tiles_n = (int32_t)tiles_n; a.gblocks = (int32_t)gblocks;
+        a.S = (int32_t)S;
+        a.kslice = (int32_t)kslice;
+        a.total_wg = (int32_t)(base * S);
+        a.out_mode = S == 1 ? out_final : OUT_WORKSPACE;
+        a.slice_elems = (int32_t)ndw;
+        a.mWo = make_magic((uint32_t)g.Wo);
+        a.mHo = make_magic((uint32_t)g.Ho);
+        info.tile = tile_id;
+        info.tile_m = t->bm; info.tile_n = t->bn; info.tile_k = t->bk;
+        info.split_k = (int32_t)S;
+        info.group_merge = (int32_t)Gm;
+        info.vector_width = V;
+        info.grid_main = a.total_wg;
+        info.workspace_bytes = S > 1 ? S * ndw * 4 : 0;
+        snprintf(name, sizeof name, "wgrad_mfma_%s_t%d_%dx%dx%d_a%d_v%d_kouter_spk%lld_gm%lld", dname, tile_id,
+                 t->bm, t->bn, t->bk, t->atom, V, (long long)S, (long long)Gm);
+    }
+    out.name = name;
+    // ---- reduce / convert pass
+    out.red = ReduceArgs{nullptr, nullptr, (int32_t)ndw, info.split_k, out_final};
+    if (info.split_k > 1) {
+        int64_t threads = (ndw % 4 == 0) ? ndw / 4 : ndw;
+        info.grid_reduce = ceil_div(threads, 256);
+    }
+    return WGRAD_OK;
+}
+
+}  // namespace wgrad

@@ -1,0 +1,127 @@
+// Internal types shared by the host planner (plan.cpp), the C ABI (abi.cpp)
+// and the HIP kernels (kernels.hip). Not part of the public interface.
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/wgrad.h"
+
+namespace wgrad {
+
+// Unsigned division by a runtime-constant divisor d >= 1, for dividends
+// n < 2^31 (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, the round-up variant with a 32-bit multiplier):
+//   l = ceil(log2 d), mul = floor(2^32 * (2^l - d) / d) + 1,
+//   q = (mulhi(mul, n) + n) >> l.
+// The (n, ho, wo) decode of the reduction index uses it so that the inner
+// loop has no integer division.
+struct MagicU32 {
+    uint32_t mul;
+    uint32_t shift;
+};
+
+inline MagicU32 make_magic(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return MagicU32{static_cast<uint32_t>(m), l};
+}
+
+inline uint32_t magic_div_host(uint32_t n, MagicU32 m) {
+    uint32_t t = static_cast<uint32_t>((static_cast<uint64_t>(m.mul) * n) >> 32);
+    return (t + n) >> m.shift;
+}
+
+enum OutMode : int32_t { OUT_BF16 = 0, OUT_FP16 = 1, OUT_FP32 = 2, OUT_WORKSPACE = 3 };
+
+// Kernel arguments of the MFMA implicit-GEMM kernel. Every element offset
+// fits in 31 bits (checked by the planner).
+struct MfmaArgs {
+    const uint16_t* x;
+    const uint16_t* dy;
+    void* out;              // dW (out_mode < 3) or the fp32 workspace
+    int32_t Ktot, Ctot;     // channels per pixel of dY and X
+    int32_t kpg, cpg, Gm;   // per-group K, C and merge degree
+    int32_t gkpg, gcpg;     // Gm*kpg (merged M), Gm*cpg (merged channel run)
+    int32_t Hi, Wi, Ho, Wo; // 1D: Hi = Ho = 1
+    int32_t Xf;             // filter width
+    int32_t sh, sw, dh, dw, ph, pw;
+    int32_t R;              // N*Ho*Wo
+    int32_t Mm, Nm;         // merged GEMM sizes: Gm*kpg, Y*X*Gm*cpg
+    int32_t row_len;        // Y*X*cpg: length of one dW row
+    int32_t tiles_m, tiles_n, gblocks, S;
+    int32_t kslice;         // reduction elements per split, a multiple of the tile K
+    int32_t total_wg;
+    int32_t out_mode;
+    int32_t slice_elems;    // K*Y*X*cpg: elements of one workspace slice
+    MagicU32 mWo, mHo;
+};
+
+// Depthwise (C/G = K/G = 1) channel-vector kernel.
+struct DwArgs {
+    const uint16_t* x;
+    const uint16_t* dy;
+    void* out;
+    int32_t C;                   // = G = K
+    int32_t Hi, Wi, Ho, Wo;
+    int32_t Y, Xf, sh, sw, dh, dw, ph, pw;
+    int32_t R;                   // N*Ho*Wo
+    int32_t cl;                  // channel lanes per workgroup (each lane: 8 channels)
+    int32_t cblocks;             // C / (8*cl)
+    int32_t S, kslice;           // reduction splits and elements per split
+    int32_t total_wg;
+    int32_t out_mode;
+    int32_t slice_elems;         // C*Y*X
+    MagicU32 mWo, mHo;
+};
+
+struct ReduceArgs {
+    const float* ws;
+    void* dw;
+    int32_t elems;    // elements per slice
+    int32_t S;
+    int32_t out_mode; // OUT_BF16 / OUT_FP16 / OUT_FP32
+};
+
+// MFMA tile table (id -> shape). Ids are stable: tests and overrides use them.
+struct TileShape {
+    int id, bm, bn, bk, wm, wn, atom;
+};
+constexpr TileShape kTiles[] = {
+    {1, 64, 64, 32, 2, 2, 32},
+    {2, 64, 128, 32, 2, 2, 32},
+    {3, 128, 128, 32, 2, 2, 32},
+    {4, 32, 128, 32, 1, 4, 32},
+    {5, 16, 128, 32, 1, 4, 16},
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+const TileShape* find_tile(int id);
+
+struct DeviceModel {
+    int num_cus;
+    int num_xcds;
+};
+
+struct Plan {
+    wgrad_problem prob;
+    wgrad_plan_info info;
+    int variant;
+    int in_f16;          // 1 if inputs are fp16
+    MfmaArgs mfma;       // pointers filled at run time
+    DwArgs dwk;
+    ReduceArgs red;
+    int dw_tile_y, dw_tile_x;   // depthwise kernel filter instance
+    std::string name;
+};
+
+// Host planning (no HIP calls). Returns a wgrad_status and sets *msg on error.
+int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceModel& dev,
+               Plan& out, std::string* msg);
+
+// Kernel launchers (kernels.hip). Return a hipError_t value (0 = success).
+int launch_mfma(const Plan& plan, const MfmaArgs& a, void* stream);
+int launch_depthwise(const Plan& plan, const DwArgs& a, void* stream);
+int launch_reduce(const ReduceArgs& a, int64_t grid, void* stream);
+
+}  // namespace wgrad

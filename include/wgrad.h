@@ -1,0 +1,180 @@
+/*
+ * wgrad.h -- C ABI of the MI355X (gfx950) grouped convolution
+ * backward-weight library (libwgrad.so).
+ *
+ * Operation (Composable Kernel page "grouped_convolution_backward_weight_
+ * kernel.hpp": the 1D NWGC/GKXC/NWGK and 2D NHWGC/GKYXC/NHWGK argument
+ * constructors, their group strides, and operator()'s "Out * In = Weight"):
+ *
+ *   dW[g,k,y,x,c] = sum_{n,ho,wo} [0<=hi<Hi, 0<=wi<Wi] dY[n,ho,wo,g,k] * X[n,hi,wi,g,c]
+ *   hi = ho*stride_h - pad_lo_h + y*dilation_h
+ *   wi = wo*stride_w - pad_lo_w + x*dilation_w
+ *
+ * computed as a batched-over-groups implicit GEMM with M = K/G,
+ * N = (C/G)*Y*X and a reduction of length N*Ho*Wo. The pad_hi values only
+ * size the output: Ho = floor((Hi + pad_lo + pad_hi - dilation*(Y-1) - 1)/stride) + 1.
+ *
+ * Layouts (all dense, row-major, innermost index last):
+ *   X  : [N][Hi][Wi][C]        (1D: [N][Wi][C])      C = G * (C/G), group-major
+ *   dY : [N][Ho][Wo][K]        (1D: [N][Wo][K])      K = G * (K/G), group-major
+ *   dW : [K][Y][X][C/G]        (1D: [K][X][C/G])     i.e. GKYXC
+ * X and dY share one 16-bit element type (bf16 or fp16); dW is that type or
+ * fp32. A torch tensor [N,C,H,W] in channels_last memory order is exactly X;
+ * a grouped conv weight [K, C/G, Y, X] in channels_last is exactly dW.
+ *
+ * Ownership: the caller owns every device buffer and the stream. The library
+ * allocates no device memory; a plan owns only host memory.
+ *
+ * Errors: every entry point returns a wgrad_status. WGRAD_OK is 0. On error
+ * nothing is enqueued and wgrad_last_error() returns a reason string for the
+ * calling thread. No C++ exception crosses this boundary.
+ */
+#ifndef WGRAD_H
+#define WGRAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WGRAD_BF16 = 0,
+    WGRAD_FP16 = 1,
+    WGRAD_FP32 = 2  /* output only */
+} wgrad_dtype;
+
+typedef enum {
+    WGRAD_OK = 0,
+    WGRAD_ERR_INVALID_ARG = 1, /* bad shape, pointer, alignment or size */
+    WGRAD_ERR_UNSUPPORTED = 2, /* valid problem, but an override asks for something the kernels cannot do */
+    WGRAD_ERR_HIP = 3          /* a HIP runtime call or launch failed; the reason names it */
+} wgrad_status;
+
+/* The problem. C and K are totals over all G groups and must be multiples
+ * of G. ndim 1 uses index [0] of each array (the w axis); ndim 2 uses
+ * [0] = h and [1] = w. Lengths, strides and dilations are >= 1, pads >= 0.
+ * N may be 0 (dW is then all zeros). */
+typedef struct {
+    int32_t ndim;       /* 1 or 2 */
+    int32_t in_dtype;   /* wgrad_dtype of X and dY: BF16 or FP16 */
+    int32_t out_dtype;  /* wgrad_dtype of dW: in_dtype or FP32 */
+    int32_t reserved;   /* must be 0 */
+    int64_t G, N, C, K;
+    int64_t in_len[2];
+    int64_t filt_len[2];
+    int64_t stride[2];
+    int64_t dilation[2];
+    int64_t pad_lo[2];
+    int64_t pad_hi[2];
+} wgrad_problem;
+
+/* Kernel families a plan can use. */
+typedef enum {
+    WGRAD_VARIANT_AUTO = 0,
+    WGRAD_VARIANT_MFMA = 1,      /* MFMA implicit GEMM, optional group merge */
+    WGRAD_VARIANT_DEPTHWISE = 2  /* C/G = K/G = 1: channel-vector direct kernel */
+} wgrad_variant;
+
+/* Overrides for tests and benchmarks; 0 in a field means "the plan decides".
+ * Production callers pass NULL. */
+typedef struct {
+    int32_t split_k;      /* reduction slices S >= 1 */
+    int32_t group_merge;  /* Gm: power of two dividing G (MFMA variant) */
+    int32_t variant;      /* wgrad_variant */
+    int32_t tile;         /* MFMA tile id (see wgrad_plan_info.tile), 0 = auto */
+} wgrad_overrides;
+
+/* What a plan decided, for logging and tests. */
+typedef struct {
+    int64_t out_len[2];      /* Ho, Wo (1D: out_len[0] = Wo) */
+    int64_t gemm_m;          /* K/G */
+    int64_t gemm_n;          /* (C/G)*Y*X */
+    int64_t gemm_k;          /* N*Ho*Wo */
+    int32_t variant;         /* wgrad_variant actually used */
+    int32_t tile;            /* MFMA tile id or 0 */
+    int32_t tile_m, tile_n, tile_k;
+    int32_t split_k;         /* S */
+    int32_t group_merge;     /* Gm */
+    int32_t vector_width;    /* elements per global load */
+    int64_t grid_main;       /* workgroups of the main kernel */
+    int64_t grid_reduce;     /* workgroups of the reduce kernel (0 if none) */
+    int64_t workspace_bytes; /* as wgrad_workspace_bytes */
+    int32_t num_cus;         /* compute units the plan was sized for */
+    int32_t reserved;
+} wgrad_plan_info;
+
+typedef struct wgrad_plan_s wgrad_plan_t;
+
+/*
+ * Validate a problem and choose kernels, split-K degree S and merge degree
+ * Gm (host only, no device work). hip_device >= 0 sizes the plan for that
+ * device (it must be gfx950); -1 sizes it for an MI355X (256 CUs, 8 XCDs)
+ * without touching the HIP runtime, for host-side tests.
+ * Returns WGRAD_ERR_INVALID_ARG for: C or K not a multiple of G, a
+ * non-positive length/stride/dilation, a negative pad, an empty output
+ * (Ho or Wo < 1), ndim not 1 or 2, an unsupported dtype pair, or sizes whose
+ * element offsets do not fit in 31 bits. WGRAD_ERR_UNSUPPORTED for an
+ * override the kernels cannot honour (e.g. Gm not a power of two dividing G).
+ * On success *out owns host memory; free it with wgrad_plan_destroy.
+ */
+int wgrad_plan(const wgrad_problem* problem, const wgrad_overrides* overrides,
+               int hip_device, wgrad_plan_t** out);
+
+/* Bytes of device workspace wgrad_run needs: 0 when S = 1, otherwise
+ * S * K * Y * X * (C/G) * 4 (fp32 partials of the unmerged dW, so the size
+ * does not depend on Gm). */
+size_t wgrad_workspace_bytes(const wgrad_plan_t* plan);
+
+/*
+ * Enqueue dW = wgrad(X, dY) on stream (a hipStream_t; NULL = the null
+ * stream) and return without synchronising. dW is overwritten (no
+ * accumulation, no pre-zeroing needed). With S > 1 it runs two kernels: fp32
+ * partials into ws, then a reduce/convert kernel that sums the S slices in
+ * ascending order and rounds to the out dtype (round to nearest even); no
+ * atomics, so the same plan on the same inputs gives the same bits.
+ * x, dy, dw are device pointers aligned to 16 bytes; ws is a device pointer
+ * of at least wgrad_workspace_bytes(plan) bytes (may be NULL when that is 0).
+ * Runs on one stream may not share a workspace concurrently.
+ * Errors: WGRAD_ERR_INVALID_ARG (NULL or misaligned pointer, ws too small),
+ * WGRAD_ERR_HIP (launch failure).
+ */
+int wgrad_run(const wgrad_plan_t* plan, const void* x, const void* dy, void* dw,
+              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The two launches of wgrad_run, enqueued one at a time: stage 1 is the main
+ * kernel (with S > 1 it writes the fp32 partials into ws), stage 2 the
+ * reduce/convert kernel (a no-op when S = 1). Running stage 1 then stage 2
+ * on one stream equals wgrad_run; a caller may enqueue other work between
+ * them (for example the next layer's main kernel) or time them separately.
+ * Arguments, checks and errors as in wgrad_run; stage not 1 or 2 is
+ * WGRAD_ERR_INVALID_ARG. Stage 2 reads the workspace stage 1 wrote, so
+ * both must see the same ws and be ordered (same stream or an event).
+ */
+int wgrad_run_stage(const wgrad_plan_t* plan, int stage, const void* x, const void* dy, void* dw,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Fill *info with the plan's decisions. */
+int wgrad_plan_query(const wgrad_plan_t* plan, wgrad_plan_info* info);
+
+/* Kernel name with its flags (tile, atom, "kouter", "spk<S>", "gm<Gm>"),
+ * valid until the plan is destroyed. */
+const char* wgrad_plan_describe(const wgrad_plan_t* plan);
+
+/* Release a plan (NULL is allowed). A plan is immutable after creation and
+ * may be used from several threads at once. */
+void wgrad_plan_destroy(wgrad_plan_t* plan);
+
+/* Reason for the calling thread's last failed call ("" if none). */
+const char* wgrad_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* wgrad_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WGRAD_H */

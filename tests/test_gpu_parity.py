@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars:
+* exact-integer inputs (integers in {-2..2}): every product and partial sum is
+  an integer < 2^24, so fp32 accumulation is exact in any order and the GPU
+  must return RNE_out(oracle) bit for bit;
+* the configured random inputs: |gpu - oracle| <= tau*sum|dY*X| + 1e-6 with
+  tau = 2^-7 (bf16 out), 2^-10 (fp16 out), 1e-5 (fp32 out);
+* coverage: dW is prefilled with NaN and a guard band after it must be left
+  untouched; determinism: two runs give the same bits.
+Full-size configurations compare every dW element where the oracle finishes
+in seconds and a sample (first and last output-channel rows plus random
+elements) where it does not; reduced-size variants compare everything.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+gcb = pytest.importorskip("grouped_convolution_backward_amd")
+
+pytestmark = pytest.mark.gpu
+
+OUT_T = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+GUARD = 4096
+
+
+def to_dev(bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).reshape(-1).copy())
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
+
+
+def run_gpu(cfg, xb, dyb, **ov):
+    """Run through the C ABI; returns (dw as fp64 numpy, raw bits, plan)."""
+    p = gcb.Plan(cfg, **ov)
+    out_dtype = cfg.get("out_dtype", cfg["in_dtype"])
+    x = to_dev(xb, cfg["in_dtype"])
+    dy = to_dev(dyb, cfg["in_dtype"])
+    n = int(np.prod(p.dw_shape()))
+    # dW with a guard band; the whole buffer starts as NaN
+    buf = torch.full((n + GUARD,), float("nan"), dtype=OUT_T[out_dtype], device="cuda")
+    dw = buf[:n]
+    ws = None
+    if p.workspace_bytes:
+        ws = torch.full((p.workspace_bytes // 4 + GUARD,), float("nan"), dtype=torch.float32, device="cuda")
+    print(f"[gpu] {cfg.get('name', '?')} {p.name}", flush=True)
+    p.run(x, dy, dw, ws)
+    torch.cuda.synchronize()
+    guard = buf[n:].float().cpu().numpy()
+    assert np.all(np.isnan(guard)), "kernel wrote past the end of dW"
+    if ws is not None:
+        wguard = ws[p.workspace_bytes // 4:].cpu().numpy()
+        assert np.all(np.isnan(wguard)), "kernel wrote past the end of the workspace"
+    if out_dtype == "fp32":
+        vals = dw.cpu().numpy().astype(np.float64)
+        bits = dw.cpu().numpy().view(np.uint32)
+    else:
+        bits = dw.view(torch.int16).cpu().numpy().view(np.uint16)
+        vals = oracle.widen(bits, out_dtype)
+    return vals.reshape(p.dw_shape()), bits.reshape(p.dw_shape()), p
+
+
+def sample_idx(cfg, total):
+    per_k = total // cfg["K"]
+    rng = np.random.default_rng(1234)
+    return np.unique(np.concatenate([np.arange(per_k), total - per_k + np.arange(per_k),
+                                     rng.integers(0, total, 1024)]))
+
+
+# configs whose full dW the oracle computes in seconds
+FULL = ("c1", "c4a", "c4b", "c5")
+SAMPLED = ("c2", "c3")
+
+
+def oracle_ref(cfg, xb, dyb, idx=None):
+    if idx is None:
+        dw, ab = oracle.wgrad(cfg, xb, dyb)
+        return dw.reshape(-1), ab.reshape(-1)
+    return oracle.wgrad_sampled(cfg, xb, dyb, idx)
+
+
+def check_exact(cfg, gpu_bits_flat, dw64, idx=None):
+    out_dtype = cfg.get("out_dtype", cfg["in_dtype"])
+    sel = gpu_bits_flat if idx is None else gpu_bits_flat[idx]
+    if out_dtype == "fp32":
+        want = dw64.astype(np.float32).view(np.uint32)
+    else:
+        want = oracle.round_to_bits(dw64, out_dtype)
+    bad = np.nonzero(sel != want)[0]
+    assert bad.size == 0, f"{bad.size} elements differ, first at {bad[:5]}"
+
+
+def check_tol(cfg, gpu_vals_flat, dw64, ab64, idx=None):
+    out_dtype = cfg.get("out_dtype", cfg["in_dtype"])
+    sel = gpu_vals_flat if idx is None else gpu_vals_flat[idx]
+    bad = np.nonzero(oracle.violations(sel, dw64, ab64, out_dtype))[0]
+    assert bad.size == 0, (f"{bad.size} elements outside tau*sum|dY*X|+1e-6, e.g. gpu={sel[bad[:3]]} "
+                           f"ref={dw64[bad[:3]]}")
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_configs_exact_integer(name):
+    cfg = workloads.CONFIGS[name]
+    xb, dyb = workloads.inputs(cfg, "int")
+    vals, bits, p = run_gpu(cfg, xb, dyb)
+    idx = None if name in FULL else sample_idx(cfg, bits.size)
+    dw64, _ = oracle_ref(cfg, xb, dyb, idx)
+    check_exact(cfg, bits.reshape(-1), dw64, idx)
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_configs_random_within_tolerance(name):
+    cfg = workloads.CONFIGS[name]
+    xb, dyb = workloads.inputs(cfg)
+    vals, bits, p = run_gpu(cfg, xb, dyb)
+    idx = None if name in FULL else sample_idx(cfg, bits.size)
+    dw64, ab64 = oracle_ref(cfg, xb, dyb, idx)
+    check_tol(cfg, vals.reshape(-1), dw64, ab64, idx)
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_dense_reduced_batch_full_compare(name):
+    # the dense shapes at N=2: every element, several tiles and ragged M (c3)
+    cfg = workloads.problem(name, N=2)
+    for dist in ("int", None):
+        xb, dyb = workloads.inputs(cfg, dist)
+        vals, bits, _ = run_gpu(cfg, xb, dyb)
+        dw64, ab64 = oracle_ref(cfg, xb, dyb)
+        if dist == "int":
+            check_exact(cfg, bits.reshape(-1), dw64)
+        else:
+            check_tol(cfg, vals.reshape(-1), dw64, ab64)
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_configs_all_ones(name):
+    cfg = workloads.CONFIGS[name]
+    xb, dyb = workloads.inputs(cfg, "ones")
+    vals, bits, _ = run_gpu(cfg, xb, dyb)
+    idx = None if name in FULL else sample_idx(cfg, bits.size)
+    dw64, _ = oracle_ref(cfg, xb, dyb, idx)
+    check_exact(cfg, bits.reshape(-1), dw64, idx)
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 3, 5, 16])
+def test_split_k_sweep_bitwise_integer(split_k):
+    cfg = workloads.problem("c3", N=2)
+    xb, dyb = workloads.inputs(cfg, "int")
+    _, bits, p = run_gpu(cfg, xb, dyb, split_k=split_k)
+    assert p.info["split_k"] == min(split_k, p.info["split_k"])
+    dw64, _ = oracle_ref(cfg, xb, dyb)
+    check_exact(cfg, bits.reshape(-1), dw64)
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
+def test_every_tile_shape(tile):
+    cfg = workloads.problem("c3", N=1, out_dtype="fp32")
+    xb, dyb = workloads.inputs(cfg)
+    vals, _, p = run_gpu(cfg, xb, dyb, tile=tile, variant=gcb.VARIANT_MFMA)
+    assert p.info["tile"] == tile
+    dw64, ab64 = oracle_ref(cfg, xb, dyb)
+    check_tol(cfg, vals.reshape(-1), dw64, ab64)
+
+
+@pytest.mark.parametrize("gm", [1, 2, 4, 8])
+@pytest.mark.parametrize("split_k", [1, 4])
+def test_depthwise_group_merge_mfma(gm, split_k):
+    # the MFMA path with Gm merged groups: off-diagonal pairs must be masked
+    cfg = workloads.problem("c5", N=1, in_len=(20, 20), out_len=(20, 20))
+    xb, dyb = workloads.inputs(cfg, "int")
+    _, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_MFMA, group_merge=gm, split_k=split_k)
+    assert p.info["group_merge"] == gm
+    dw64, _ = oracle_ref(cfg, xb, dyb)
+    check_exact(cfg, bits.reshape(-1), dw64)
+
+
+def test_merge_with_single_merged_group():
+    # G == Gm: the merged problem has one group block
+    cfg = workloads.problem("c4a", G=4, C=32, K=32, N=2)
+    xb, dyb = workloads.inputs(cfg, "int")
+    _, bits, p = run_gpu(cfg, xb, dyb, group_merge=4)
+    dw64, _ = oracle_ref(cfg, xb, dyb)
+    check_exact(cfg, bits.reshape(-1), dw64)
+
+
+@pytest.mark.parametrize("split_k", [1, 3, 8])
+def test_depthwise_kernel_split_sweep(split_k):
+    cfg = workloads.problem("c5", N=2, in_len=(17, 23), out_len=(17, 23))
+    xb, dyb = workloads.inputs(cfg, "int")
+    _, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_DEPTHWISE, split_k=split_k)
+    dw64, _ = oracle_ref(cfg, xb, dyb)
+    check_exact(cfg, bits.reshape(-1), dw64)
+
+
+SHAPES = [
+    # odd channel counts (scalar loads), strides, dilations, asymmetric pads, 1D
+    dict(ndim=2, G=1, N=2, C=3, K=5, in_len=(9, 11), filt_len=(3, 3), stride=(1, 1), dilation=(1, 1),
+         pad_lo=(1, 1), pad_hi=(1, 1), in_dtype="bf16", out_dtype="bf16"),
+    dict(ndim=2, G=2, N=3, C=12, K=20, in_len=(13, 10), filt_len=(3, 2), stride=(2, 1), dilation=(1, 2),
+         pad_lo=(1, 0), pad_hi=(2, 1), in_dtype="fp16", out_dtype="fp16"),
+    dict(ndim=2, G=4, N=2, C=64, K=32, in_len=(15, 15), filt_len=(5, 5), stride=(3, 2), dilation=(2, 1),
+         pad_lo=(2, 0), pad_hi=(0, 2), in_dtype="bf16", out_dtype="fp32"),
+    dict(ndim=2, G=1, N=2, C=40, K=24, in_len=(7, 7), filt_len=(1, 1), stride=(1, 1), dilation=(1, 1),
+         pad_lo=(0, 0), pad_hi=(0, 0), in_dtype="fp16", out_dtype="fp32"),
+    dict(ndim=1, G=8, N=3, C=64, K=48, in_len=(100,), filt_len=(7,), stride=(2,), dilation=(3,),
+         pad_lo=(4,), pad_hi=(1,), in_dtype="bf16", out_dtype="bf16"),
+    dict(ndim=1, G=16, N=2, C=16, K=16, in_len=(77,), filt_len=(5,), stride=(1,), dilation=(1,),
+         pad_lo=(2,), pad_hi=(2,), in_dtype="fp16", out_dtype="fp16"),
+    dict(ndim=1, G=64, N=2, C=64, K=64, in_len=(50,), filt_len=(3,), stride=(1,), dilation=(1,),
+         pad_lo=(1,), pad_hi=(1,), in_dtype="bf16", out_dtype="bf16"),
+    dict(ndim=2, G=3, N=1, C=6, K=9, in_len=(6, 5), filt_len=(3, 3), stride=(1, 1), dilation=(1, 1),
+         pad_lo=(0, 0), pad_hi=(0, 0), in_dtype="bf16", out_dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SHAPES)))
+def test_edge_shapes(i):
+    cfg = dict(SHAPES[i], name=f"edge{i}")
+    ol = oracle.out_len(cfg)
+    cfg["out_len"] = ol
+    for dist, seed in (("int", 900 + i), ("uniform", 950 + i)):
+        xb = workloads.draw(workloads.x_shape(cfg), cfg["in_dtype"], dist, seed)
+        dyb = workloads.draw(workloads.dy_shape(cfg), cfg["in_dtype"], dist, seed + 1)
+        vals, bits, p = run_gpu(cfg, xb, dyb)
+        dw64, ab64 = oracle_ref(cfg, xb, dyb)
+        if dist == "int":
+            check_exact(cfg, bits.reshape(-1), dw64)
+        else:
+            check_tol(cfg, vals.reshape(-1), dw64, ab64)
+
+
+def test_empty_batch_gives_zeros():
+    cfg = workloads.problem("c2", N=0)
+    p = gcb.Plan(cfg)
+    x = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    dy = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    dw = torch.full(p.dw_shape(), float("nan"), dtype=torch.bfloat16, device="cuda")
+    p.run(x, dy, dw)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0)
+
+
+def test_deterministic_bits_across_runs():
+    cfg = workloads.CONFIGS["c2"]
+    xb, dyb = workloads.inputs(cfg)
+    _, b1, p = run_gpu(cfg, xb, dyb)
+    _, b2, _ = run_gpu(cfg, xb, dyb)
+    assert p.info["split_k"] > 1
+    assert np.array_equal(b1, b2)
+
+
+def test_misaligned_pointer_is_an_error_not_corruption():
+    cfg = workloads.CONFIGS["c1"]
+    p = gcb.Plan(cfg)
+    x = torch.zeros(p.x_shape(), dtype=torch.bfloat16, device="cuda").reshape(-1)
+    big = torch.zeros(x.numel() + 8, dtype=torch.bfloat16, device="cuda")
+    dy = torch.zeros(p.dy_shape(), dtype=torch.bfloat16, device="cuda").reshape(-1)
+    dw = torch.zeros(p.dw_shape(), dtype=torch.bfloat16, device="cuda")
+    rc = gcb.load_library().wgrad_run(p.handle, big.data_ptr() + 2, dy.data_ptr(), dw.data_ptr(), None, 0, None)
+    assert rc == gcb.ERR_INVALID_ARG
+    assert "aligned" in gcb.wgrad_last_error()

@@ -1,0 +1,216 @@
+"""Host-side tests of the C ABI (no GPU): the library loads and exports every
+symbol the header declares, plans validate and size problems correctly, and
+the split-K / merge choices respect their invariants. Plans are made with
+hip_device = -1 (sized for an MI355X without touching the HIP runtime)."""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+import grouped_convolution_backward_amd as gcb
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wgrad.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wgrad_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gcb.load_library()
+    declared = _declared_functions()
+    assert set(declared) == set(gcb.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", gcb.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b(wgrad_[a-z_]+)\b", out))
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert re.match(r"^\d+\.\d+\.\d+$", gcb.wgrad_version())
+
+
+def plan(cfg, **kw):
+    return gcb.Plan(cfg, hip_device=-1, **kw)
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_plan_sizes_for_configs(name):
+    cfg = workloads.CONFIGS[name]
+    p = plan(cfg)
+    info = p.info
+    nd = cfg["ndim"]
+    assert info["out_len"][:nd] == cfg["out_len"][:nd]
+    G = cfg["G"]
+    assert info["gemm_m"] == cfg["K"] // G
+    taps = 1
+    for f in cfg["filt_len"][:nd]:
+        taps *= f
+    assert info["gemm_n"] == cfg["C"] // G * taps
+    R = cfg["N"]
+    for o in cfg["out_len"][:nd]:
+        R *= o
+    assert info["gemm_k"] == R
+    S = info["split_k"]
+    ndw = cfg["K"] * taps * (cfg["C"] // G)
+    assert info["workspace_bytes"] == (S * ndw * 4 if S > 1 else 0)
+    assert p.workspace_bytes == info["workspace_bytes"]
+    assert info["num_cus"] == 256
+    assert ("spk%d" % S) in p.name
+
+
+def test_depthwise_config_uses_depthwise_kernel_and_dense_uses_mfma():
+    assert plan(workloads.CONFIGS["c5"]).info["variant"] == gcb.VARIANT_DEPTHWISE
+    for n in ("c1", "c2", "c3", "c4a", "c4b"):
+        assert plan(workloads.CONFIGS[n]).info["variant"] == gcb.VARIANT_MFMA
+
+
+def test_grid_and_xcd_snap():
+    # the main grid is tiles * groups/Gm * S and, whenever S > 1 and the clamp
+    # allows it, a multiple of the 8 XCDs
+    for name, cfg in workloads.CONFIGS.items():
+        info = plan(cfg).info
+        if info["variant"] != gcb.VARIANT_MFMA:
+            continue
+        Gm = info["group_merge"]
+        Mm = Gm * info["gemm_m"]
+        Nm = Gm * info["gemm_n"]
+        tiles = -(-Mm // info["tile_m"]) * -(-Nm // info["tile_n"])
+        assert info["grid_main"] == tiles * (cfg["G"] // Gm) * info["split_k"], name
+        if info["split_k"] > 1:
+            assert info["grid_main"] % 8 == 0, name
+
+
+def test_split_k_clamped_to_k_tiles_before_snap():
+    # a shallow reduction: R = 2*3*3 = 18 positions -> one K tile of 32, so S
+    # must be 1 whatever the occupancy target asks for
+    cfg = workloads.problem("c1", N=2, in_len=(3, 3))
+    info = plan(cfg).info
+    assert info["split_k"] == 1
+    # R = 4*8*8 = 256 -> 8 K tiles: S <= 8
+    info = plan(workloads.problem("c1", N=4)).info
+    assert 1 <= info["split_k"] <= 8
+
+
+def test_split_k_override_and_effective_slices():
+    cfg = workloads.CONFIGS["c1"]            # R = 64, tile K = 32
+    assert plan(cfg, split_k=2).info["split_k"] == 2
+    # more slices than K tiles collapse to the number of non-empty slices
+    assert plan(cfg, split_k=7).info["split_k"] == 2
+    info = plan(workloads.CONFIGS["c2"], split_k=5).info
+    assert info["split_k"] == 5
+    assert info["workspace_bytes"] == 5 * 64 * 9 * 64 * 4
+
+
+def test_group_merge_choices_are_admissible():
+    # auto Gm is a power of two dividing G, at most 8, and only merges when the
+    # per-group M leaves the 16-row MFMA edge unfilled
+    for name, cfg in workloads.CONFIGS.items():
+        info = plan(cfg, variant=gcb.VARIANT_MFMA).info
+        Gm = info["group_merge"]
+        assert Gm & (Gm - 1) == 0 and cfg["G"] % Gm == 0 and Gm <= 8, name
+        if info["gemm_m"] >= 16:
+            assert Gm == 1
+    assert plan(workloads.CONFIGS["c4a"]).info["group_merge"] == 2
+    assert plan(workloads.CONFIGS["c5"], variant=gcb.VARIANT_MFMA).info["group_merge"] == 8
+    for gm in (1, 2, 4, 8):
+        info = plan(workloads.CONFIGS["c5"], variant=gcb.VARIANT_MFMA, group_merge=gm).info
+        assert info["group_merge"] == gm
+        assert info["vector_width"] == gm
+        # workspace is sized from the unmerged dW, whatever Gm is
+        S = info["split_k"]
+        assert info["workspace_bytes"] == (S * 512 * 9 * 4 if S > 1 else 0)
+
+
+def _expect(code, cfg, **kw):
+    with pytest.raises(gcb.WgradError) as ei:
+        plan(cfg, **kw)
+    assert ei.value.code == code
+    assert gcb.wgrad_last_error() != ""
+    return str(ei.value)
+
+
+def test_invalid_problems_are_rejected_with_reasons():
+    c1 = workloads.CONFIGS["c1"]
+    assert "multiples of G" in _expect(gcb.ERR_INVALID_ARG, workloads.problem("c1", G=3))
+    _expect(gcb.ERR_INVALID_ARG, workloads.problem("c1", in_dtype="fp32"))
+    _expect(gcb.ERR_INVALID_ARG, workloads.problem("c1", out_dtype="fp16"))
+    _expect(gcb.ERR_INVALID_ARG, workloads.problem("c1", ndim=3, in_len=(8, 8, 8)))
+    assert "empty output" in _expect(gcb.ERR_INVALID_ARG, workloads.problem("c1", in_len=(1, 1), pad_lo=(0, 0), pad_hi=(0, 0)))
+    _expect(gcb.ERR_INVALID_ARG, workloads.problem("c1", stride=(0, 1)))
+    _expect(gcb.ERR_INVALID_ARG, workloads.problem("c1", dilation=(1, 0)))
+    _expect(gcb.ERR_INVALID_ARG, workloads.problem("c1", pad_lo=(-1, 1)))
+    _expect(gcb.ERR_INVALID_ARG, workloads.problem("c1", N=-1))
+    assert "31 bits" in _expect(gcb.ERR_INVALID_ARG, workloads.problem("c2", N=20000))
+    # overrides the kernels cannot honour
+    _expect(gcb.ERR_UNSUPPORTED, workloads.CONFIGS["c5"], variant=gcb.VARIANT_MFMA, group_merge=3)
+    _expect(gcb.ERR_UNSUPPORTED, workloads.CONFIGS["c4a"], group_merge=64)
+    _expect(gcb.ERR_UNSUPPORTED, c1, variant=gcb.VARIANT_DEPTHWISE)
+    _expect(gcb.ERR_UNSUPPORTED, c1, tile=99)
+
+
+def test_empty_batch_plans_one_slice():
+    info = plan(workloads.problem("c2", N=0)).info
+    assert info["gemm_k"] == 0 and info["split_k"] == 1 and info["workspace_bytes"] == 0
+
+
+def test_fp32_output_mode_plans():
+    p = plan(workloads.problem("c3", out_dtype="fp32"))
+    assert p.info["variant"] == gcb.VARIANT_MFMA
+
+
+def test_magic_division_exhaustive(tmp_path):
+    """The (n, ho, wo) decode divides by Wo and Ho with a multiply-high; check
+    the header's constants against real division for every dividend the
+    configurations use (and beyond), in a host program built from the same header."""
+    src = tmp_path / "magic.cpp"
+    src.write_text(r'''
+#include <cstdio>
+#include <cstdint>
+#include "grouped_convolution_backward_amd/csrc/wgrad_internal.hpp"
+int main() {
+    const uint32_t divs[] = {1, 2, 3, 5, 7, 8, 28, 56, 1024, 1000, 4095, 65537, 3000017u};
+    long bad = 0;
+    for (uint32_t d : divs) {
+        wgrad::MagicU32 m = wgrad::make_magic(d);
+        for (uint32_t n = 0; n < (1u << 22); ++n)
+            if (wgrad::magic_div_host(n, m) != n / d) ++bad;
+        for (uint32_t n = 0x7fffffffu; n > 0x7fffffffu - (1u << 20); --n)
+            if (wgrad::magic_div_host(n, m) != n / d) ++bad;
+    }
+    for (uint32_t d = 1; d < 5000; ++d) {
+        wgrad::MagicU32 m = wgrad::make_magic(d);
+        for (uint32_t n = 0; n < 200000; n += 7)
+            if (wgrad::magic_div_host(n, m) != n / d) ++bad;
+    }
+    printf("%ld\n", bad);
+    return bad != 0;
+}
+''')
+    exe = tmp_path / "magic"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", ROOT, "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "0"
+
+
+def test_run_rejects_null_plan_and_pointers_without_gpu():
+    lib = gcb.load_library()
+    assert lib.wgrad_run(None, None, None, None, None, 0, None) == gcb.ERR_INVALID_ARG
+    p = plan(workloads.CONFIGS["c1"])
+    # NULL dw is rejected before anything touches the device
+    assert lib.wgrad_run(p.handle, 16, 16, None, None, 0, None) == gcb.ERR_INVALID_ARG
+    assert "dw" in gcb.wgrad_last_error()
+    # misaligned pointers are rejected, not truncated
+    assert lib.wgrad_run(p.handle, 18, 16, 16, None, 0, None) == gcb.ERR_INVALID_ARG
+    assert "aligned" in gcb.wgrad_last_error()
+    # a plan that needs a workspace refuses a missing or short one
+    p2 = plan(workloads.CONFIGS["c2"])
+    assert p2.workspace_bytes > 0
+    assert lib.wgrad_run(p2.handle, 16, 16, 16, None, 0, None) == gcb.ERR_INVALID_ARG
+    assert lib.wgrad_run(p2.handle, 16, 16, 16, 16, p2.workspace_bytes - 1, None) == gcb.ERR_INVALID_ARG
+    assert "smaller" in gcb.wgrad_last_error()
