@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libwgrad.so")
 
 BF16, FP16, FP32 = 0, 1, 2
 DTYPES = {"bf16": BF16, "fp16": FP16, "fp32": FP32}
-VARIANT_AUTO, VARIANT_MFMA, VARIANT_DEPTHWISE = 0, 1, 2
+VARIANT_AUTO, VARIANT_MFMA, VARIANT_DEPTHWISE, VARIANT_ROWSLAB = 0, 1, 2, 3
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 
 

@@ -14,94 +14,17 @@
 //    one tile and stores only the diagonal group pairs (PR 12359). With S > 1
 //    each slice writes fp32 partials to a workspace (deterministic two-stage
 //    split-K; no atomics).
-// 2. reduce_kernel: dW = round(sum_z ws[z]) in ascending z.
+// 2. reduce_kernel: dW = round(sum_z ws[z]) in a fixed order.
 // 3. dw_kernel: depthwise (C/G = K/G = 1) direct kernel; one lane owns 8
 //    adjacent channels (8 merged groups, one 16-byte load per pixel).
 #include <hip/hip_runtime.h>
 
-#include "wgrad_internal.hpp"
+#include "device_common.hpp"
 
 namespace wgrad {
 namespace {
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-template <int V> struct VecT;
-template <> struct VecT<8> { typedef u32x4 T; };
-template <> struct VecT<4> { typedef u32x2 T; };
-template <> struct VecT<2> { typedef uint32_t T; };
-template <> struct VecT<1> { typedef uint16_t T; };
-
-__device__ __forceinline__ uint32_t magic_div(uint32_t n, MagicU32 m) {
-    return (__umulhi(m.mul, n) + n) >> m.shift;
-}
-
-// fp32 -> bf16, round to nearest even, NaN kept quiet.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ void store_out(void* out, int mode, int64_t e, float v) {
-    if (mode == OUT_BF16) {
-        static_cast<uint16_t*>(out)[e] = f32_to_bf16(v);
-    } else if (mode == OUT_FP16) {
-        static_cast<_Float16*>(out)[e] = (_Float16)v;
-    } else {
-        static_cast<float*>(out)[e] = v;
-    }
-}
-
-// Workgroups are dispatched to the 8 XCDs round-robin by id. Renumber them so
-// that each XCD receives one contiguous range of logical ids: logical
-// neighbours (same reduction slice, adjacent tiles or groups) then share an
-// L2 instead of being spread over eight.
-__device__ __forceinline__ int xcd_logical_id(int hw, int total) {
-    const int q = total >> 3, rem = total & 7;
-    const int xcd = hw & 7, slot = hw >> 3;
-    return xcd * q + min(xcd, rem) + slot;
-}
-
-template <bool F16>
-__device__ __forceinline__ void mfma_step32(const i16x8& a, const i16x8& b, f32x16& c) {
-    if constexpr (F16)
-        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    else
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-template <bool F16>
-__device__ __forceinline__ void mfma_step16(const i16x8& a, const i16x8& b, f32x4& c) {
-    if constexpr (F16)
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    else
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// Transposed LDS read: within each 16-lane group, lane i supplies the address
-// of 4 consecutive 16-bit elements and lane j receives element j%4 of lanes
-// j/4, j/4+4, j/4+8, j/4+12. With lane i pointing at row (i%16)/4, column
-// (i%4)*4 of a K-outer tile, lane j receives column j of 4 consecutive rows:
-// one MFMA operand run along the reduction axis.
-__device__ __forceinline__ i16x8 tr_frag(const uint16_t* p, int row_pitch) {
-    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * row_pitch));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// LDS row pad (elements): 32 elements = 64 bytes, which puts the four rows a
-// 16-lane group reads in one transposed read on disjoint bank ranges.
-constexpr int kLdsPad = 32;
+using namespace dev;
 
 template <int BM, int BN, int BK, int WM, int WN, int ATOM, int V, bool F16>
 __global__ __launch_bounds__(256) void mfma_kernel(const MfmaArgs a) {
@@ -279,21 +202,50 @@ __global__ __launch_bounds__(256) void mfma_kernel(const MfmaArgs a) {
     }
 }
 
-// dW[e] = round(sum_{z=0}^{S-1} ws[z][e]), z ascending, fp32 sums.
+// dW[e] = round(sum_z ws[z][e]) in fp32, in one fixed order: z-lane l of a
+// workgroup sums slices l, l+ZL, l+2ZL, ... in ascending order, then the ZL
+// lane sums are added in ascending l. The order depends only on (S, ZL), so
+// a plan always produces the same bits. Splitting the slices over ZL lanes
+// keeps the grid wide when dW is small and S is large.
 __global__ __launch_bounds__(256) void reduce_kernel(const ReduceArgs a) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if ((a.elems & 3) == 0) {
-        const int e = i * 4;
-        if (e >= a.elems) return;
-        f32x4 s = *reinterpret_cast<const f32x4*>(a.ws + e);
-        for (int z = 1; z < a.S; ++z) s += *reinterpret_cast<const f32x4*>(a.ws + (int64_t)z * a.elems + e);
+    __shared__ f32x4 part[256];
+    const int zl = a.zl;
+    const int eg = 256 / zl;                 // element vectors per workgroup
+    const int t = threadIdx.x;
+    const int lane_e = t % eg, lane_z = t / eg;
+    const int v = blockIdx.x * eg + lane_e;   // element vector index
+    const int nvec = a.vec4 ? a.elems / 4 : a.elems;
+    // four independent running sums (slices z, z+zl, z+2zl, z+3zl of each
+    // group of four) keep four loads in flight; they are added in a fixed order
+    f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0, p2 = p0, p3 = p0;
+    if (v < nvec) {
+        const int64_t stride = (int64_t)zl * a.elems;
+        if (a.vec4) {
+            const float* w = a.ws + (int64_t)lane_z * a.elems + 4 * v;
+            int z = lane_z;
+            for (; z + 3 * zl < a.S; z += 4 * zl, w += 4 * stride) {
+                p0 += *reinterpret_cast<const f32x4*>(w);
+                p1 += *reinterpret_cast<const f32x4*>(w + stride);
+                p2 += *reinterpret_cast<const f32x4*>(w + 2 * stride);
+                p3 += *reinterpret_cast<const f32x4*>(w + 3 * stride);
+            }
+            for (; z < a.S; z += zl, w += stride) p0 += *reinterpret_cast<const f32x4*>(w);
+        } else {
+            for (int z = lane_z; z < a.S; z += zl) p0[0] += a.ws[(int64_t)z * a.elems + v];
+        }
+    }
+    const f32x4 acc = (p0 + p1) + (p2 + p3);
+    part[t] = acc;
+    __syncthreads();
+    if (lane_z == 0 && v < nvec) {
+        f32x4 s = part[lane_e];
+        for (int l = 1; l < zl; ++l) s += part[l * eg + lane_e];
+        if (a.vec4) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) store_out(a.dw, a.out_mode, e + k, s[k]);
-    } else {
-        if (i >= a.elems) return;
-        float s = a.ws[i];
-        for (int z = 1; z < a.S; ++z) s += a.ws[(int64_t)z * a.elems + i];
-        store_out(a.dw, a.out_mode, i, s);
+            for (int k = 0; k < 4; ++k) store_out(a.dw, a.out_mode, 4 * v + k, s[k]);
+        } else {
+            store_out(a.dw, a.out_mode, v, s[0]);
+        }
     }
 }
 

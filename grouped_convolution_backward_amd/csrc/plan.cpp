@@ -63,6 +63,105 @@ int64_t choose_split(int64_t base_grid, int64_t k_tiles, int64_t slice_bytes, in
     return s;
 }
 
+
+// Row-slab plan: filter width 3 or 5, channel runs of 32 or 64 after merging,
+// 16-byte vectors everywhere. Returns false (with a reason) when the shape
+// does not fit the kernel.
+bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o, const DeviceModel& dev,
+                  int out_final, Plan& out, std::string* why) {
+    const int64_t cpg = p.C / p.G, kpg = p.K / p.G;
+    auto no = [&](const char* m) { if (why) *why = m; return false; };
+    if (g.X != 3 && g.X != 5) return no("row-slab needs a filter width of 3 or 5");
+    if (g.dw != 1) return no("row-slab needs a filter dilation of 1 along w");
+    if (2 * p.N * g.Hi * g.Wi * p.C >= (int64_t{1} << 31) || 2 * p.N * g.Ho * g.Wo * p.K >= (int64_t{1} << 31))
+        return no("row-slab needs X and dY below 2 GiB");
+    int64_t Gm = o.group_merge;
+    if (!Gm) {
+        Gm = 1;
+        while (Gm * cpg < 32 && Gm * 2 <= 8 && p.G % (Gm * 2) == 0) Gm *= 2;
+    }
+    if (!is_pow2(Gm) || p.G % Gm) return no("group_merge must be a power of two dividing G");
+    const int64_t gkpg = Gm * kpg, gcpg = Gm * cpg;
+    if (cpg % 4 || gkpg % 8 || p.K % 8 || p.C % 8) return no("row-slab needs 16-byte channel vectors");
+    // tile: 64 x 64 channel blocks when the merged runs allow it, else 32 x 32
+    int mb, cb;
+    if (g.X == 3 && gcpg % 64 == 0 && gkpg > 32) { mb = 64; cb = 64; }
+    else if (gcpg % 32 == 0) { mb = 32; cb = 32; }
+    else return no("row-slab needs a merged channel run that is a multiple of 32");
+    const int64_t NHo = p.N * g.Ho;
+    auto xw_of = [&](int64_t sw) { return (sw - 1) * g.sw + (g.X - 1) * g.dw + 1; };
+    // slab: PR output rows x SW output columns whose positions are one
+    // contiguous run of r (whole output rows, or a segment of one row). Pick
+    // the instance and slab with the largest useful fraction PR*SW/KS.
+    int inst = -1;
+    int64_t PR = 0, SW = 0;
+    double best = 0.0;
+    for (int i = 0; i < kNumRsInstances; ++i) {
+        const RsInstance& r = kRsInstances[i];
+        if (r.mb != mb || r.cb != cb || r.xf != g.X) continue;
+        if (r.stride != (g.sw == 2 ? 2 : 1)) continue;   // pitch tuned for the pixel step
+        if (4 * 2 * (int64_t)rs_wave_lds(r) > kRsLdsMax) continue;
+        const int64_t ks = 16 * r.nks, xwp = (int64_t)r.nxc * rs_pixels_per_chunk(r);
+        int64_t sw = std::min<int64_t>(g.Wo, ks);
+        while (sw > 1 && xw_of(sw) > xwp) --sw;
+        if (xw_of(sw) > xwp) continue;
+        int64_t pr = sw == g.Wo ? std::min<int64_t>({ks / sw, (int64_t)r.nxr, std::max<int64_t>(1, NHo)}) : 1;
+        const double eff = double(pr * sw) / double(ks);
+        if (eff > best + 1e-9) { best = eff; inst = i; PR = pr; SW = sw; }
+    }
+    if (inst < 0) return no("row-slab: no kernel instance fits this slab geometry");
+    const RsInstance& ri = kRsInstances[inst];
+    const int64_t XW = xw_of(SW);
+    const int64_t nseg = ceil_div(g.Wo, SW);
+    const int64_t nslabs = ceil_div(NHo, PR) * nseg;
+    const int64_t mblocks = ceil_div(gkpg, mb), cblocks = gcpg / cb, gblocks = p.G / Gm;
+    const int64_t tiles = gblocks * mblocks * cblocks * g.Y;
+    int64_t spw, S;
+    if (nslabs == 0) {
+        spw = 0; S = 1;
+    } else if (o.split_k) {
+        spw = ceil_div(nslabs, std::min<int64_t>(o.split_k, nslabs));
+        S = ceil_div(nslabs, spw);
+    } else {
+        // every wave gets the same number of slabs (the smallest that covers
+        // all slab-tile units with one workgroup per CU), then as few splits as
+        // that allows, which keeps the workspace small
+        const int64_t per_wave = ceil_div(tiles * nslabs, 4 * (int64_t)dev.num_cus);
+        spw = 4 * per_wave;
+        S = ceil_div(nslabs, spw);
+    }
+    if (tiles * S > kMax31 || S > 65535) return no("row-slab grid too large");
+    const int64_t ndw = p.K * g.Y * g.X * cpg;
+    RowSlabArgs& a = out.rs;
+    a = RowSlabArgs{};
+    a.Ktot = (int32_t)p.K; a.Ctot = (int32_t)p.C; a.kpg = (int32_t)kpg; a.cpg = (int32_t)cpg;
+    a.gkpg = (int32_t)gkpg; a.gcpg = (int32_t)gcpg;
+    a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo; a.Y = (int32_t)g.Y;
+    a.sh = (int32_t)g.sh; a.sw = (int32_t)g.sw; a.dh = (int32_t)g.dh; a.dw = (int32_t)g.dw;
+    a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
+    a.NHo = (int32_t)NHo; a.Mm = (int32_t)gkpg; a.row_len = (int32_t)(g.Y * g.X * cpg);
+    a.mblocks = (int32_t)mblocks; a.cblocks = (int32_t)cblocks; a.tiles = (int32_t)tiles;
+    a.PR = (int32_t)PR; a.SW = (int32_t)SW; a.XW = (int32_t)XW;
+    a.nseg = (int32_t)nseg; a.nslabs = (int32_t)nslabs; a.spw = (int32_t)spw;
+    a.S = (int32_t)S; a.total_wg = (int32_t)(tiles * S);
+    a.out_mode = S == 1 ? out_final : OUT_WORKSPACE;
+    a.slice_elems = (int32_t)ndw;
+    a.x_bytes = (uint32_t)(2 * p.N * g.Hi * g.Wi * p.C);
+    a.dy_bytes = (uint32_t)(2 * NHo * g.Wo * p.K);
+    a.mSW = make_magic((uint32_t)SW); a.mXW = make_magic((uint32_t)XW); a.mHo = make_magic((uint32_t)g.Ho);
+    out.rs_inst = inst;
+    out.lds_bytes = (int)std::max<int64_t>(4 * 2 * (int64_t)rs_wave_lds(ri), 4 * (int64_t)mb * (cb + 4) * 4);
+    wgrad_plan_info& info = out.info;
+    info.tile = 0;
+    info.tile_m = mb; info.tile_n = (int32_t)(g.X * cb); info.tile_k = 16 * ri.nks;
+    info.split_k = (int32_t)S;
+    info.group_merge = (int32_t)Gm;
+    info.vector_width = 8;
+    info.grid_main = a.total_wg;
+    info.workspace_bytes = S > 1 ? S * ndw * 4 : 0;
+    return true;
+}
+
 }  // namespace
 
 int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceModel& dev, Plan& out,
@@ -133,16 +232,28 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
     const bool dw_shape = cpg == 1 && kpg == 1 && p.C % 8 == 0;
     const bool dw_filter = (g.Y == 3 && g.X == 3) || (g.Y == 1 && (g.X == 3 || g.X == 5));
     int variant = o.variant;
-    if (variant == WGRAD_VARIANT_AUTO) variant = (dw_shape && dw_filter) ? WGRAD_VARIANT_DEPTHWISE : WGRAD_VARIANT_MFMA;
+    if (variant < WGRAD_VARIANT_AUTO || variant > WGRAD_VARIANT_ROWSLAB)
+        return fail(msg, E, "unknown variant %d", variant);
+    std::string rs_why;
+    if (variant == WGRAD_VARIANT_AUTO) {
+        if (dw_shape && dw_filter && !o.group_merge && !o.tile) variant = WGRAD_VARIANT_DEPTHWISE;
+        else if (!o.tile && plan_rowslab(p, g, o, dev, out_final, out, &rs_why)) variant = WGRAD_VARIANT_ROWSLAB;
+        else variant = WGRAD_VARIANT_MFMA;
+    }
     if (variant == WGRAD_VARIANT_DEPTHWISE && !(dw_shape && dw_filter))
         return fail(msg, U, "depthwise variant needs C/G = K/G = 1, C %% 8 == 0 and a 3x3, 1x3 or 1x5 filter");
-    if (variant != WGRAD_VARIANT_MFMA && variant != WGRAD_VARIANT_DEPTHWISE)
-        return fail(msg, E, "unknown variant %d", variant);
     out.variant = variant;
     info.variant = variant;
 
     char name[256];
-    if (variant == WGRAD_VARIANT_DEPTHWISE) {
+    if (variant == WGRAD_VARIANT_ROWSLAB) {
+        if (o.tile) return fail(msg, U, "tile applies to the flat-tile MFMA variant only");
+        if (!plan_rowslab(p, g, o, dev, out_final, out, &rs_why)) return fail(msg, U, "%s", rs_why.c_str());
+        const RowSlabArgs& a = out.rs;
+        const RsInstance& ri = kRsInstances[out.rs_inst];
+        snprintf(name, sizeof name, "wgrad_rowslab_%s_m%dc%dx%d_k%d_slab%dx%d_kouter_spk%d_gm%d", dname, ri.mb, ri.cb,
+                 ri.xf, 16 * ri.nks, a.PR, a.SW, a.S, info.group_merge);
+    } else if (variant == WGRAD_VARIANT_DEPTHWISE) {
         if (o.group_merge > 1) return fail(msg, U, "group_merge applies to the MFMA variant only");
         if (o.tile) return fail(msg, U, "tile applies to the MFMA variant only");
         DwArgs& a = out.dwk;
@@ -264,11 +375,13 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
     }
     out.name = name;
     // ---- reduce / convert pass
-    out.red = ReduceArgs{nullptr, nullptr, (int32_t)ndw, info.split_k, out_final};
-    if (info.split_k > 1) {
-        int64_t threads = (ndw % 4 == 0) ? ndw / 4 : ndw;
-        info.grid_reduce = ceil_div(threads, 256);
-    }
+    // slice lanes: the fewest that still give a few workgroups per CU
+    const int vec4 = ndw % 4 == 0;
+    const int64_t nvec = vec4 ? ndw / 4 : ndw;
+    int zl = 1;
+    while (zl < 64 && zl * 2 <= info.split_k && ceil_div(nvec, 256 / zl) < 2 * dev.num_cus) zl *= 2;
+    out.red = ReduceArgs{nullptr, nullptr, (int32_t)ndw, info.split_k, out_final, zl, vec4};
+    if (info.split_k > 1) info.grid_reduce = ceil_div(nvec, 256 / zl);
     return WGRAD_OK;
 }
 

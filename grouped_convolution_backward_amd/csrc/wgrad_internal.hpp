@@ -58,6 +58,59 @@ struct MfmaArgs {
     MagicU32 mWo, mHo;
 };
 
+// Row-slab kernel instances, shared by the planner and the kernels. Each
+// fixes the tile (M block mb, C block cb, filter width xf) and the slab
+// geometry at compile time: nks 16-position MFMA steps per slab, an X tile of
+// nxr rows x nxc load chunks (a chunk is 64 / (cb / 8) pixels). Fixed shapes
+// keep the slab loop free of runtime guards, so accumulators never need
+// merging copies and LDS stores are unconditional.
+// LDS layout: a 16-lane group of a transposed read fetches 4 rows x 16
+// columns (two 16-byte chunks per row). 64-wide dY rows (128 bytes) use an
+// XOR swizzle instead of padding: chunk c of row r is stored in slot
+// c ^ 4*((r >> 1) & 1), which puts the 4 rows of two groups on all 64 banks
+// once. X pixels use a padded pitch px: 48 words (96 elements) for stride 1,
+// 40 words (80 elements) for stride 2, where a read steps two pixels. 32-wide
+// rows need neither (four consecutive 64-byte rows already cover the banks).
+constexpr int kRsLdsMax = 160 * 1024;
+struct RsInstance {
+    int mb, cb, xf, nks, nxr, nxc, pa, px, aswz, stride;
+};
+constexpr RsInstance kRsInstances[] = {
+    {64, 64, 3, 7, 2, 8, 64, 96, 1, 1},   // two 56-wide output rows
+    {64, 64, 3, 4, 2, 8, 64, 80, 1, 2},   // two rows up to 32 wide, stride 2
+    {32, 32, 3, 7, 4, 2, 32, 32, 0, 1},   // four 28-wide rows
+    {32, 32, 3, 8, 2, 4, 32, 32, 0, 1},   // two rows up to 64 wide
+    {32, 32, 5, 8, 1, 9, 32, 32, 0, 1},   // one 128-wide row segment (1D)
+};
+constexpr int kNumRsInstances = sizeof(kRsInstances) / sizeof(kRsInstances[0]);
+inline int rs_pixels_per_chunk(const RsInstance& r) { return 64 / (r.cb / 8); }
+inline int rs_wave_lds(const RsInstance& r) {
+    return 16 * r.nks * r.pa + r.nxr * r.nxc * rs_pixels_per_chunk(r) * r.px;
+}
+
+// Row-slab MFMA kernel: a workgroup owns one filter row y of one
+// (group block, M block, C block) tile and all X taps of that row; the
+// reduction runs over slabs of PR output rows x SW output columns.
+struct RowSlabArgs {
+    const uint16_t* x;
+    const uint16_t* dy;
+    void* out;
+    int32_t Ktot, Ctot, kpg, cpg, gkpg, gcpg;
+    int32_t Hi, Wi, Ho, Wo, Y;
+    int32_t sh, sw, dh, dw, ph, pw;
+    int32_t NHo;            // N*Ho output rows
+    int32_t Mm;             // merged M = Gm*kpg
+    int32_t row_len;        // Y*X*cpg
+    int32_t mblocks, cblocks, tiles;
+    int32_t PR, SW;         // slab rows and columns (PR*SW <= the instance's positions)
+    int32_t XW;             // X tile columns: (SW-1)*sw + (X-1)*dw + 1
+    int32_t nseg, nslabs;   // column segments per row block, slabs in total
+    int32_t spw;            // slabs per workgroup (one split)
+    int32_t S, total_wg, out_mode, slice_elems;
+    uint32_t x_bytes, dy_bytes;   // buffer sizes for the bounds-checked loads
+    MagicU32 mSW, mXW, mHo;
+};
+
 // Depthwise (C/G = K/G = 1) channel-vector kernel.
 struct DwArgs {
     const uint16_t* x;
@@ -82,6 +135,8 @@ struct ReduceArgs {
     int32_t elems;    // elements per slice
     int32_t S;
     int32_t out_mode; // OUT_BF16 / OUT_FP16 / OUT_FP32
+    int32_t zl;       // slice lanes per workgroup (power of two, <= 64)
+    int32_t vec4;     // 1: elements handled 4 at a time (elems % 4 == 0)
 };
 
 // MFMA tile table (id -> shape). Ids are stable: tests and overrides use them.
@@ -110,6 +165,9 @@ struct Plan {
     int in_f16;          // 1 if inputs are fp16
     MfmaArgs mfma;       // pointers filled at run time
     DwArgs dwk;
+    RowSlabArgs rs;
+    int rs_inst;                 // index into kRsInstances
+    int lds_bytes;               // dynamic LDS of the main kernel
     ReduceArgs red;
     int dw_tile_y, dw_tile_x;   // depthwise kernel filter instance
     std::string name;
@@ -122,6 +180,7 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
 // Kernel launchers (kernels.hip). Return a hipError_t value (0 = success).
 int launch_mfma(const Plan& plan, const MfmaArgs& a, void* stream);
 int launch_depthwise(const Plan& plan, const DwArgs& a, void* stream);
+int launch_rowslab(const Plan& plan, const RowSlabArgs& a, void* stream);
 int launch_reduce(const ReduceArgs& a, int64_t grid, void* stream);
 
 }  // namespace wgrad

@@ -73,8 +73,11 @@ typedef struct {
 /* Kernel families a plan can use. */
 typedef enum {
     WGRAD_VARIANT_AUTO = 0,
-    WGRAD_VARIANT_MFMA = 1,      /* MFMA implicit GEMM, optional group merge */
-    WGRAD_VARIANT_DEPTHWISE = 2  /* C/G = K/G = 1: channel-vector direct kernel */
+    WGRAD_VARIANT_MFMA = 1,      /* MFMA implicit GEMM over flat K tiles, any shape, optional group merge */
+    WGRAD_VARIANT_DEPTHWISE = 2, /* C/G = K/G = 1: channel-vector direct kernel */
+    WGRAD_VARIANT_ROWSLAB = 3    /* MFMA implicit GEMM over slabs of output rows, one filter row per
+                                    tile, X staged once per row (filter width 3 or 5, w-dilation 1,
+                                    channel runs multiple of 32), optional group merge */
 } wgrad_variant;
 
 /* Overrides for tests and benchmarks; 0 in a field means "the plan decides".
@@ -132,7 +135,7 @@ size_t wgrad_workspace_bytes(const wgrad_plan_t* plan);
  * stream) and return without synchronising. dW is overwritten (no
  * accumulation, no pre-zeroing needed). With S > 1 it runs two kernels: fp32
  * partials into ws, then a reduce/convert kernel that sums the S slices in
- * ascending order and rounds to the out dtype (round to nearest even); no
+ * one fixed order and rounds to the out dtype (round to nearest even); no
  * atomics, so the same plan on the same inputs gives the same bits.
  * x, dy, dw are device pointers aligned to 16 bytes; ws is a device pointer
  * of at least wgrad_workspace_bytes(plan) bytes (may be NULL when that is 0).

@@ -263,3 +263,43 @@ def test_misaligned_pointer_is_an_error_not_corruption():
     rc = gcb.load_library().wgrad_run(p.handle, big.data_ptr() + 2, dy.data_ptr(), dw.data_ptr(), None, 0, None)
     assert rc == gcb.ERR_INVALID_ARG
     assert "aligned" in gcb.wgrad_last_error()
+
+
+ROWSLAB_CASES = [
+    # (base config, changes): slab tails, ragged M blocks, several splits
+    ("c2", dict(N=2)),
+    ("c2", dict(N=1, in_len=(13, 56), out_len=(13, 56))),       # odd number of output rows
+    ("c3", dict(N=2)),                                           # stride 2, M = 200 (ragged block)
+    ("c3", dict(N=1, K=96, in_len=(20, 30), out_len=(10, 15))),  # fp16, narrow rows
+    ("c4a", dict(N=3)),                                          # merged groups, Gm = 4
+    ("c4b", dict(N=2, in_len=(300,), out_len=(300,))),           # 1D, row segments with a tail
+    ("c2", dict(N=1, C=128, K=64, in_len=(10, 200), out_len=(10, 200))),   # wide rows: segments
+    ("c2", dict(N=2, pad_lo=(0, 0), pad_hi=(2, 2))),             # asymmetric pad
+]
+
+
+@pytest.mark.parametrize("i", range(len(ROWSLAB_CASES)))
+def test_rowslab_variant(i):
+    base, changes = ROWSLAB_CASES[i]
+    cfg = workloads.problem(base, **changes)
+    cfg["out_len"] = oracle.out_len(cfg)
+    cfg["name"] = f"rowslab{i}"
+    for dist in ("int", None):
+        xb = workloads.draw(workloads.x_shape(cfg), cfg["in_dtype"], dist or cfg["dist"], 700 + i)
+        dyb = workloads.draw(workloads.dy_shape(cfg), cfg["in_dtype"], dist or cfg["dist"], 750 + i)
+        vals, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_ROWSLAB)
+        assert p.info["variant"] == gcb.VARIANT_ROWSLAB
+        dw64, ab64 = oracle_ref(cfg, xb, dyb)
+        if dist == "int":
+            check_exact(cfg, bits.reshape(-1), dw64)
+        else:
+            check_tol(cfg, vals.reshape(-1), dw64, ab64)
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 7])
+def test_rowslab_split_sweep(split_k):
+    cfg = workloads.problem("c2", N=2)
+    xb, dyb = workloads.inputs(cfg, "int")
+    _, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_ROWSLAB, split_k=split_k)
+    dw64, _ = oracle_ref(cfg, xb, dyb)
+    check_exact(cfg, bits.reshape(-1), dw64)
