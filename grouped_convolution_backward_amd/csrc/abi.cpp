@@ -90,6 +90,18 @@ int run_stages(const wgrad_plan_t* plan, int first, int last, const void* x, con
             a.dy = static_cast<const uint16_t*>(dy);
             a.out = main_out;
             e = wgrad::launch_rowslab(P, a, stream);
+        } else if (P.variant == WGRAD_VARIANT_DEPTHWISE && P.dw3_ty) {
+            wgrad::Dw3Args a = P.dw3;
+            a.x = static_cast<const uint16_t*>(x);
+            a.dy = static_cast<const uint16_t*>(dy);
+            a.out = main_out;
+            e = wgrad::launch_depthwise3(P, a, stream);
+        } else if (P.variant == WGRAD_VARIANT_DEPTHWISE && P.dw2_ty) {
+            wgrad::Dw2Args a = P.dw2;
+            a.x = static_cast<const uint16_t*>(x);
+            a.dy = static_cast<const uint16_t*>(dy);
+            a.out = main_out;
+            e = wgrad::launch_depthwise2(P, a, stream);
         } else if (P.variant == WGRAD_VARIANT_DEPTHWISE) {
             wgrad::DwArgs a = P.dwk;
             a.x = static_cast<const uint16_t*>(x);

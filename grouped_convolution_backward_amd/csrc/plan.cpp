@@ -230,7 +230,10 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
 
     // ---- kernel family
     const bool dw_shape = cpg == 1 && kpg == 1 && p.C % 8 == 0;
-    const bool dw_filter = (g.Y == 3 && g.X == 3) || (g.Y == 1 && (g.X == 3 || g.X == 5));
+    // windowed depthwise kernel: width-3 filter, w-stride and w-dilation 1, height 1, 3 or 5
+    const bool dw2_ok = g.X == 3 && g.sw == 1 && g.dw == 1 && (g.Y == 1 || g.Y == 3 || g.Y == 5) &&
+                        2 * nx < (int64_t{1} << 31) && 2 * ndy < (int64_t{1} << 31);
+    const bool dw_filter = dw2_ok || (g.Y == 3 && g.X == 3) || (g.Y == 1 && (g.X == 3 || g.X == 5));
     int variant = o.variant;
     if (variant < WGRAD_VARIANT_AUTO || variant > WGRAD_VARIANT_ROWSLAB)
         return fail(msg, E, "unknown variant %d", variant);
@@ -255,7 +258,6 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
                  ri.xf, 16 * ri.nks, a.PR, a.SW, a.S, info.group_merge);
     } else if (variant == WGRAD_VARIANT_DEPTHWISE) {
         if (o.group_merge > 1) return fail(msg, U, "group_merge applies to the MFMA variant only");
-        if (o.tile) return fail(msg, U, "tile applies to the MFMA variant only");
         DwArgs& a = out.dwk;
         a = DwArgs{};
         a.C = (int32_t)p.C;
@@ -281,6 +283,84 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
         if (R == 0) S = 1;
         int64_t kslice = std::max<int64_t>(1, ceil_div(R, S));
         if (R > 0) S = ceil_div(R, kslice);
+        // kernel form: strip (3x3, unit stride and dilation), windowed (width 3), or generic
+        const bool dw3_ok = dw2_ok && g.Y == 3 && g.sh == 1 && g.dh == 1;
+        int form = o.tile ? o.tile : dw3_ok ? 3 : dw2_ok ? 2 : 1;
+        if (form < 1 || form > 3) return fail(msg, U, "depthwise kernel form %d is not 1, 2 or 3", form);
+        if (form == 3 && !dw3_ok) return fail(msg, U, "strip depthwise kernel needs a 3x3 filter with unit stride and dilation");
+        if (form == 2 && !dw2_ok) return fail(msg, U, "windowed depthwise kernel needs filter width 3, w-stride 1, w-dilation 1 and height 1, 3 or 5");
+        if (form == 1 && !((g.Y == 3 && g.X == 3) || (g.Y == 1 && (g.X == 3 || g.X == 5))))
+            return fail(msg, U, "generic depthwise kernel needs a 3x3, 1x3 or 1x5 filter");
+        // channel lanes of the windowed and strip kernels: a wave covers up to
+        // 64 x 8 = 512 channels of one pixel, so each load reads one contiguous run
+        int cl2 = 64;
+        while ((p.C / 8) % cl2) cl2 >>= 1;
+        if (form == 3) {
+            Dw3Args& b = out.dw3;
+            b = Dw3Args{};
+            b.C = (int32_t)p.C; b.Hi = (int32_t)g.Hi; b.Wi = (int32_t)g.Wi; b.Ho = (int32_t)g.Ho; b.Wo = (int32_t)g.Wo;
+            b.ph = (int32_t)g.ph; b.pw = (int32_t)g.pw;
+            b.nseg = (int32_t)ceil_div(g.Wo, 4);
+            const int64_t steps = p.N * b.nseg * g.Ho;
+            if (steps > kMax31) return fail(msg, U, "too many row steps");
+            b.steps = (int32_t)steps;
+            // lanes of 4 channels; two workgroups (8 waves) per CU, a split is
+            // one workgroup's share of a channel block
+            int cl3 = 64;
+            while ((p.C / 4) % cl3) cl3 >>= 1;
+            b.cl = cl3;
+            b.cblocks = (int32_t)(p.C / 4 / cl3);
+            const int64_t nsub = 64 / cl3;
+            int64_t S3 = o.split_k ? o.split_k : std::max<int64_t>(1, 2 * (int64_t)dev.num_cus / b.cblocks);
+            S3 = std::max<int64_t>(1, std::min<int64_t>(S3, ceil_div(std::max<int64_t>(steps, 1), 4 * nsub)));
+            if (steps == 0) S3 = 1;
+            if (S3 > 65535 || S3 * b.cblocks > kMax31) return fail(msg, U, "split_k too large");
+            b.S = (int32_t)S3;
+            b.waves = (int32_t)(4 * S3);
+            b.total_wg = (int32_t)(S3 * b.cblocks);
+            b.out_mode = S3 == 1 ? out_final : OUT_WORKSPACE;
+            b.slice_elems = (int32_t)ndw;
+            b.x_bytes = (uint32_t)(2 * nx);
+            b.dy_bytes = (uint32_t)(2 * ndy);
+            out.dw3_ty = 3;
+            S = S3;
+            cl = cl3 / 2;   // reported in 8-channel units like the other forms
+        } else if (form == 2) {
+            // windowed kernel: units of 4 output positions; splits hold whole units
+            Dw2Args& b = out.dw2;
+            b = Dw2Args{};
+            b.C = (int32_t)p.C; b.Hi = (int32_t)g.Hi; b.Wi = (int32_t)g.Wi; b.Ho = (int32_t)g.Ho; b.Wo = (int32_t)g.Wo;
+            b.Y = (int32_t)g.Y; b.sh = (int32_t)g.sh; b.dh = (int32_t)g.dh; b.ph = (int32_t)g.ph; b.pw = (int32_t)g.pw;
+            b.NHo = (int32_t)(p.N * g.Ho);
+            b.nseg = (int32_t)ceil_div(g.Wo, 4);
+            const int64_t units = (int64_t)b.NHo * b.nseg;
+            b.units = (int32_t)units;
+            b.cl = cl2;
+            b.cblocks = (int32_t)(p.C / 8 / cl2);
+            const int64_t ul = 256 / cl2;
+            // one workgroup per CU (the kernel double-buffers a lane's loads in
+            // registers and runs one wave per SIMD); a split's units are spread
+            // over the workgroup's lanes, a lane takes every ul-th unit
+            int64_t S2 = o.split_k ? o.split_k : std::max<int64_t>(1, (int64_t)dev.num_cus / b.cblocks);
+            S2 = std::max<int64_t>(1, std::min<int64_t>(S2, std::max<int64_t>(1, ceil_div(units, ul))));
+            const int64_t upw = std::max<int64_t>(1, ceil_div(units, S2));
+            const int64_t upt = ceil_div(upw, ul);
+            S2 = units > 0 ? ceil_div(units, upw) : 1;
+            if (S2 > 65535 || S2 * b.cblocks > kMax31) return fail(msg, U, "split_k too large");
+            b.upt = (int32_t)upt;
+            b.upw = (int32_t)upw;
+            b.S = (int32_t)S2;
+            b.total_wg = (int32_t)(S2 * b.cblocks);
+            b.out_mode = S2 == 1 ? out_final : OUT_WORKSPACE;
+            b.slice_elems = (int32_t)ndw;
+            b.x_bytes = (uint32_t)(2 * nx);
+            b.dy_bytes = (uint32_t)(2 * ndy);
+            b.mHo = make_magic((uint32_t)g.Ho);
+            b.mSeg = make_magic((uint32_t)b.nseg);
+            out.dw2_ty = (int)g.Y;
+            S = S2;
+            cl = cl2;
+        }
         if (S > 65535) return fail(msg, U, "split_k too large");
         a.S = (int32_t)S;
         a.kslice = (int32_t)kslice;
@@ -294,10 +374,12 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
         info.split_k = (int32_t)S;
         info.group_merge = 8 * cl;   // channels (groups) one workgroup covers
         info.vector_width = 8;
-        info.grid_main = a.total_wg;
+        info.grid_main = out.dw3_ty ? out.dw3.total_wg : out.dw2_ty ? out.dw2.total_wg : a.total_wg;
+        info.tile = out.dw3_ty ? 3 : out.dw2_ty ? 2 : 1;
         info.workspace_bytes = S > 1 ? S * ndw * 4 : 0;
-        snprintf(name, sizeof name, "wgrad_dw_%s_%lldx%lld_cl%d_spk%lld_gm%d", dname, (long long)g.Y,
-                 (long long)g.X, cl, (long long)S, 8 * cl);
+        snprintf(name, sizeof name, "wgrad_dw%s_%s_%lldx%lld_cl%d_spk%lld_gm%d",
+                 out.dw3_ty ? "strip" : out.dw2_ty ? "win" : "", dname,
+                 (long long)g.Y, (long long)g.X, cl, (long long)S, 8 * cl);
     } else {
         // ---- group merge degree
         int64_t Gm = o.group_merge;

@@ -129,6 +129,42 @@ struct DwArgs {
     MagicU32 mWo, mHo;
 };
 
+// Depthwise windowed kernel (C/G = K/G = 1, filter width 3, w-stride and
+// w-dilation 1): one lane owns 8 channels of one 4-wide output segment
+// ("unit") at a time and keeps the 6-column X window of each filter row.
+struct Dw2Args {
+    const uint16_t* x;
+    const uint16_t* dy;
+    void* out;
+    int32_t C, Hi, Wi, Ho, Wo, Y, sh, dh, ph, pw;
+    int32_t NHo;           // N*Ho output rows
+    int32_t nseg;          // 4-wide segments per output row
+    int32_t units;         // NHo*nseg
+    int32_t cl;            // channel lanes per workgroup (8 channels each)
+    int32_t cblocks;       // C / (8*cl)
+    int32_t upt;           // units per thread
+    int32_t upw;           // units per workgroup = upt * (256/cl)
+    int32_t S, total_wg, out_mode, slice_elems;
+    uint32_t x_bytes, dy_bytes;
+    MagicU32 mHo, mSeg;
+};
+
+// Depthwise strip kernel (filter width 3, stride and dilation 1 on both axes):
+// a wave walks down a 4-wide column strip keeping the filter's input rows in
+// registers, so each step loads one new input row and one dY row.
+struct Dw3Args {
+    const uint16_t* x;
+    const uint16_t* dy;
+    void* out;
+    int32_t C, Hi, Wi, Ho, Wo, ph, pw;
+    int32_t nseg;          // 4-wide strips per image
+    int32_t steps;         // N * nseg * Ho row steps (strip-major, then row)
+    int32_t cl, cblocks;   // channel lanes (8 channels each) and channel blocks
+    int32_t waves;         // waves per channel block (4 per workgroup)
+    int32_t S, total_wg, out_mode, slice_elems;
+    uint32_t x_bytes, dy_bytes;
+};
+
 struct ReduceArgs {
     const float* ws;
     void* dw;
@@ -165,6 +201,10 @@ struct Plan {
     int in_f16;          // 1 if inputs are fp16
     MfmaArgs mfma;       // pointers filled at run time
     DwArgs dwk;
+    Dw2Args dw2;
+    int dw2_ty;                  // filter height of the windowed depthwise instance (0 = not used)
+    Dw3Args dw3;
+    int dw3_ty;                  // filter height of the strip depthwise instance (0 = not used)
     RowSlabArgs rs;
     int rs_inst;                 // index into kRsInstances
     int lds_bytes;               // dynamic LDS of the main kernel
@@ -181,6 +221,8 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
 int launch_mfma(const Plan& plan, const MfmaArgs& a, void* stream);
 int launch_depthwise(const Plan& plan, const DwArgs& a, void* stream);
 int launch_rowslab(const Plan& plan, const RowSlabArgs& a, void* stream);
+int launch_depthwise2(const Plan& plan, const Dw2Args& a, void* stream);
+int launch_depthwise3(const Plan& plan, const Dw3Args& a, void* stream);
 int launch_reduce(const ReduceArgs& a, int64_t grid, void* stream);
 
 }  // namespace wgrad

@@ -86,7 +86,10 @@ typedef struct {
     int32_t split_k;      /* reduction slices S >= 1 */
     int32_t group_merge;  /* Gm: power of two dividing G (MFMA variant) */
     int32_t variant;      /* wgrad_variant */
-    int32_t tile;         /* MFMA tile id (see wgrad_plan_info.tile), 0 = auto */
+    int32_t tile;         /* MFMA variant: tile id (see wgrad_plan_info.tile). DEPTHWISE variant:
+                             kernel form, 1 = generic filter, 2 = windowed (filter width 3,
+                             w-stride 1, w-dilation 1), 3 = strip (3x3, stride 1, dilation 1).
+                             0 = auto */
 } wgrad_overrides;
 
 /* What a plan decided, for logging and tests. */
@@ -96,7 +99,7 @@ typedef struct {
     int64_t gemm_n;          /* (C/G)*Y*X */
     int64_t gemm_k;          /* N*Ho*Wo */
     int32_t variant;         /* wgrad_variant actually used */
-    int32_t tile;            /* MFMA tile id or 0 */
+    int32_t tile;            /* MFMA tile id, depthwise kernel form (1 generic, 2 windowed, 3 strip), or 0 */
     int32_t tile_m, tile_n, tile_k;
     int32_t split_k;         /* S */
     int32_t group_merge;     /* Gm */

@@ -303,3 +303,90 @@ def test_rowslab_split_sweep(split_k):
     _, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_ROWSLAB, split_k=split_k)
     dw64, _ = oracle_ref(cfg, xb, dyb)
     check_exact(cfg, bits.reshape(-1), dw64)
+
+
+DEPTHWISE_CASES = [
+    # windowed depthwise kernel: tails, padding, strides along h, filter heights, fp16
+    dict(ndim=2, G=64, N=2, C=64, K=64, in_len=(9, 13), filt_len=(3, 3), stride=(1, 1), dilation=(1, 1),
+         pad_lo=(1, 1), pad_hi=(1, 1), in_dtype="bf16", out_dtype="bf16"),
+    dict(ndim=2, G=40, N=1, C=40, K=40, in_len=(11, 7), filt_len=(3, 3), stride=(2, 1), dilation=(2, 1),
+         pad_lo=(2, 0), pad_hi=(0, 2), in_dtype="fp16", out_dtype="fp16"),
+    dict(ndim=2, G=128, N=2, C=128, K=128, in_len=(12, 10), filt_len=(5, 3), stride=(1, 1), dilation=(1, 1),
+         pad_lo=(2, 1), pad_hi=(2, 1), in_dtype="bf16", out_dtype="fp32"),
+    dict(ndim=2, G=16, N=3, C=16, K=16, in_len=(6, 30), filt_len=(1, 3), stride=(1, 1), dilation=(1, 1),
+         pad_lo=(0, 1), pad_hi=(0, 0), in_dtype="bf16", out_dtype="bf16"),
+    dict(ndim=1, G=256, N=2, C=256, K=256, in_len=(37,), filt_len=(3,), stride=(1,), dilation=(1,),
+         pad_lo=(1,), pad_hi=(1,), in_dtype="fp16", out_dtype="fp16"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DEPTHWISE_CASES)))
+def test_depthwise_windowed(i):
+    cfg = dict(DEPTHWISE_CASES[i], name=f"dw{i}")
+    cfg["out_len"] = oracle.out_len(cfg)
+    for dist, seed in (("int", 600 + i), ("uniform", 650 + i)):
+        xb = workloads.draw(workloads.x_shape(cfg), cfg["in_dtype"], dist, seed)
+        dyb = workloads.draw(workloads.dy_shape(cfg), cfg["in_dtype"], dist, seed + 1)
+        vals, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_DEPTHWISE)
+        assert "dwwin" in p.name or "dwstrip" in p.name
+        dw64, ab64 = oracle_ref(cfg, xb, dyb)
+        if dist == "int":
+            check_exact(cfg, bits.reshape(-1), dw64)
+        else:
+            check_tol(cfg, vals.reshape(-1), dw64, ab64)
+
+
+# strip depthwise kernel (3x3, unit stride and dilation): narrow channel
+# blocks (several workers per wave), outputs 1 or 2 rows high (every step
+# starts a strip), width tails, one-sided pads, fp16 and fp32 outputs
+STRIP_CASES = [
+    dict(ndim=2, G=24, N=3, C=24, K=24, in_len=(5, 7), pad_lo=(2, 0), pad_hi=(0, 2),
+         in_dtype="bf16", out_dtype="bf16"),
+    dict(ndim=2, G=512, N=1, C=512, K=512, in_len=(1, 10), pad_lo=(1, 1), pad_hi=(1, 1),
+         in_dtype="bf16", out_dtype="bf16"),
+    dict(ndim=2, G=256, N=5, C=256, K=256, in_len=(2, 5), pad_lo=(1, 1), pad_hi=(1, 1),
+         in_dtype="fp16", out_dtype="fp16"),
+    dict(ndim=2, G=96, N=2, C=96, K=96, in_len=(17, 6), pad_lo=(0, 0), pad_hi=(0, 0),
+         in_dtype="fp16", out_dtype="fp32"),
+    dict(ndim=2, G=1024, N=2, C=1024, K=1024, in_len=(9, 9), pad_lo=(1, 2), pad_hi=(1, 0),
+         in_dtype="bf16", out_dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(STRIP_CASES)))
+def test_depthwise_strip(i):
+    cfg = dict(STRIP_CASES[i], name=f"strip{i}", filt_len=(3, 3), stride=(1, 1), dilation=(1, 1))
+    cfg["out_len"] = oracle.out_len(cfg)
+    for dist, seed in (("int", 700 + i), ("uniform", 750 + i)):
+        xb = workloads.draw(workloads.x_shape(cfg), cfg["in_dtype"], dist, seed)
+        dyb = workloads.draw(workloads.dy_shape(cfg), cfg["in_dtype"], dist, seed + 1)
+        vals, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_DEPTHWISE)
+        assert "dwstrip" in p.name
+        dw64, ab64 = oracle_ref(cfg, xb, dyb)
+        if dist == "int":
+            check_exact(cfg, bits.reshape(-1), dw64)
+        else:
+            check_tol(cfg, vals.reshape(-1), dw64, ab64)
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 7, 64, 1000])
+def test_depthwise_strip_split_sweep(split_k):
+    # 1000 splits leave most workers without a step
+    cfg = workloads.problem("c5", N=1, in_len=(13, 10), out_len=(13, 10))
+    xb, dyb = workloads.inputs(cfg, "int")
+    _, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_DEPTHWISE, tile=3, split_k=split_k)
+    assert "dwstrip" in p.name
+    dw64, _ = oracle_ref(cfg, xb, dyb)
+    check_exact(cfg, bits.reshape(-1), dw64)
+
+
+@pytest.mark.parametrize("form", [1, 2, 3])
+def test_depthwise_forms_agree_bitwise(form):
+    # the three depthwise kernel forms on one shape, integer inputs: each is
+    # exact, so they agree bit for bit
+    cfg = workloads.problem("c5", N=2, in_len=(11, 14), out_len=(11, 14))
+    xb, dyb = workloads.inputs(cfg, "int")
+    _, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_DEPTHWISE, tile=form)
+    assert p.info["tile"] == form
+    dw64, _ = oracle_ref(cfg, xb, dyb)
+    check_exact(cfg, bits.reshape(-1), dw64)

@@ -64,9 +64,13 @@ def test_plan_sizes_for_configs(name):
 
 
 def test_depthwise_config_uses_depthwise_kernel_and_dense_uses_mfma():
-    assert plan(workloads.CONFIGS["c5"]).info["variant"] == gcb.VARIANT_DEPTHWISE
-    for n in ("c1", "c2", "c3", "c4a", "c4b"):
-        assert plan(workloads.CONFIGS[n]).info["variant"] == gcb.VARIANT_MFMA
+    p5 = plan(workloads.CONFIGS["c5"])
+    assert p5.info["variant"] == gcb.VARIANT_DEPTHWISE
+    assert p5.info["tile"] == 3 and "dwstrip" in p5.name     # 3x3, unit stride: strip form
+    # the tiny golden shape has too few output rows for row slabs
+    assert plan(workloads.CONFIGS["c1"]).info["variant"] == gcb.VARIANT_MFMA
+    for n in ("c2", "c3", "c4a", "c4b"):
+        assert plan(workloads.CONFIGS[n]).info["variant"] == gcb.VARIANT_ROWSLAB
 
 
 def test_grid_and_xcd_snap():
@@ -115,7 +119,9 @@ def test_group_merge_choices_are_admissible():
         assert Gm & (Gm - 1) == 0 and cfg["G"] % Gm == 0 and Gm <= 8, name
         if info["gemm_m"] >= 16:
             assert Gm == 1
-    assert plan(workloads.CONFIGS["c4a"]).info["group_merge"] == 2
+    assert plan(workloads.CONFIGS["c4a"], variant=gcb.VARIANT_MFMA).info["group_merge"] == 2
+    # the row-slab kernel fills its 32-row M block with groups instead
+    assert plan(workloads.CONFIGS["c4a"]).info["group_merge"] == 4
     assert plan(workloads.CONFIGS["c5"], variant=gcb.VARIANT_MFMA).info["group_merge"] == 8
     for gm in (1, 2, 4, 8):
         info = plan(workloads.CONFIGS["c5"], variant=gcb.VARIANT_MFMA, group_merge=gm).info
@@ -160,7 +166,23 @@ def test_empty_batch_plans_one_slice():
 
 def test_fp32_output_mode_plans():
     p = plan(workloads.problem("c3", out_dtype="fp32"))
-    assert p.info["variant"] == gcb.VARIANT_MFMA
+    assert p.info["variant"] in (gcb.VARIANT_MFMA, gcb.VARIANT_ROWSLAB)
+
+
+def test_depthwise_kernel_forms():
+    # tile selects the depthwise kernel form: 1 generic, 2 windowed, 3 strip
+    c5 = workloads.CONFIGS["c5"]
+    for form, tag in ((1, "wgrad_dw_"), (2, "wgrad_dwwin_"), (3, "wgrad_dwstrip_")):
+        p = plan(c5, variant=gcb.VARIANT_DEPTHWISE, tile=form)
+        assert p.info["tile"] == form and p.name.startswith(tag), (form, p.name)
+    # the strip form needs unit stride and dilation in both axes
+    strided = workloads.problem("c5", stride=(2, 1))
+    assert plan(strided).info["tile"] == 2
+    _expect(gcb.ERR_UNSUPPORTED, strided, variant=gcb.VARIANT_DEPTHWISE, tile=3)
+    _expect(gcb.ERR_UNSUPPORTED, c5, variant=gcb.VARIANT_DEPTHWISE, tile=4)
+    # strip-form splits: one per workgroup, two workgroups per CU
+    p = plan(c5)
+    assert p.info["grid_main"] == 2 * 256
 
 
 def test_magic_division_exhaustive(tmp_path):
