@@ -14,10 +14,14 @@ Honest memory: each configuration cycles through enough copies of its inputs
 behind by the previous steps. Steps are replayed from HIP graphs (captured
 through torch) so that the host's launch rate does not set the time.
 
-Dominant-kernel roofline: per-launch durations of the main kernel come from
-HIP events recorded on the launch stream around wgrad_run_stage(1) while the
-stream is kept busy ahead of the host (so events and kernels run back to
-back); achieved = algorithmic FLOPs or bytes per launch / that duration.
+Dominant-kernel roofline: the per-launch duration of the main kernel comes
+from HIP events recorded on the launch stream around replays of a graph that
+holds only wgrad_run_stage(1) launches (one per input set), divided by the
+launch count; achieved = algorithmic FLOPs or bytes per launch / that
+duration. traffic = HBM bytes per launch from committed rocprofv3 FETCH_SIZE
+and WRITE_SIZE runs, each scaled by what the counter reads for a plain
+device copy of known size (--copy-calibration), when they were taken on the
+current kernel sources.
 
 cpu_baseline: the CPU oracle (fp64 direct loop, OpenMP) over the full
 headline dW, timed on this host.
@@ -146,23 +150,33 @@ class Case:
             t1 = time.perf_counter()
         return (t1 - t0) / steps
 
-    def kernel_times(self, launches=100):
-        """Average per-launch durations (s) of stage 1 and stage 2 from HIP
-        events on the launch stream, with the stream kept busy ahead."""
+    def kernel_times(self, reps=8):
+        """Average per-launch durations (s) of stage 1 (main kernel) and stage 2
+        (reduce), each from HIP events on the launch stream around replays of a
+        graph that holds nsets launches of that stage alone."""
         torch = self.torch
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(2.4e9 * 0.002 * launches / 10 + 1e6))   # queue ahead of the GPU
-        for i in range(launches):
-            ev[i][0].record()
-            self.step(i, stage=1)
-            ev[i][1].record()
-            self.step(i, stage=2)
-            ev[i][2].record()
-        torch.cuda.synchronize()
-        main = sum(e[0].elapsed_time(e[1]) for e in ev) / launches * 1e-3
-        red = sum(e[1].elapsed_time(e[2]) for e in ev) / launches * 1e-3
-        return main, red
+        out = []
+        for stage in (1, 2):
+            if stage == 2 and self.plan.info["split_k"] <= 1:
+                out.append(0.0)
+                continue
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    for i in range(self.nsets):
+                        self.step(i, stage=stage)
+                g.replay()                       # untimed: graph upload
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                for _ in range(reps):
+                    g.replay()
+                e1.record(s)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e-3 / (reps * self.nsets))
+        return out[0], out[1]
 
     def row(self, sec_per_step, t_main, t_red):
         flops, nbytes = self.flops, self.bytes
@@ -209,6 +223,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (for profilers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-merge", action="store_true", help="also time the depthwise shape over Gm and S")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy (torch neg), the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
@@ -218,6 +234,14 @@ def main():
     import workloads
 
     torch.cuda.init()
+    if args.copy_calibration:
+        src = torch.ones(128 * 2 ** 20, dtype=torch.bfloat16, device="cuda")   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: neg over {src.numel() * 2} bytes read and written", file=sys.stderr)
+        del src, dst
     names = [n for n in args.configs.split(",") if n]
     if HEADLINE not in names:
         names.insert(0, HEADLINE)
@@ -227,7 +251,7 @@ def main():
         cfg = workloads.CONFIGS[name]
         case = Case(torch, gcb, workloads, name, cfg)
         sec = case.time_steps(args.steps, args.warmup, use_graphs=not args.eager)
-        t_main, t_red = case.kernel_times(min(args.steps, 100))
+        t_main, t_red = case.kernel_times()
         per[name] = case.row(sec, t_main, t_red)
         print(f"[bench] {name}: {per[name]}", file=sys.stderr, flush=True)
         if name == HEADLINE:

@@ -11,6 +11,7 @@ constructors and the per-group offsets in operator()).
 """
 
 import itertools
+import os
 
 import numpy as np
 import pytest
@@ -541,3 +542,23 @@ def test_bound_formula():
     assert np.allclose(oracle.bound(ab, "bf16"), [1e-6, 2 ** -7 + 1e-6, 1.0 + 1e-6])
     assert np.allclose(oracle.bound(ab, "fp16"), [1e-6, 2 ** -10 + 1e-6, 0.125 + 1e-6])
     assert np.allclose(oracle.bound(ab, "fp32"), [1e-6, 1e-5 + 1e-6, 1.28e-3 + 1e-6])
+
+
+def test_golden_shape_fixture_matches_c1_and_its_all_ones_values():
+    """The pages name one golden wgrad shape; c1 is that shape, and with
+    all-ones inputs every tap counts its valid positions (corner 49, edge 56,
+    centre 64)."""
+    import json
+    import re
+    with open(os.path.join(os.path.dirname(__file__), "golden", "golden_shape.json")) as f:
+        gold = json.load(f)
+    m = re.fullmatch(r"n(\d+)h(\d+)c(\d+)k(\d+)r(\d+)", gold["name"])
+    n, h, c, k, r = map(int, m.groups())
+    cfg = workloads.CONFIGS["c1"]
+    assert (cfg["N"], cfg["in_len"][0], cfg["in_len"][1], cfg["C"], cfg["K"]) == (n, h, h, c, k)
+    assert tuple(cfg["filt_len"]) == (r, r) and cfg["G"] == 1
+    xb, dyb = workloads.inputs(cfg, "ones")
+    dw, _ = oracle.wgrad(cfg, xb, dyb)
+    per_tap = dw.reshape(k, r, r, c)
+    expect = np.array([[49, 56, 49], [56, 64, 56], [49, 56, 49]], dtype=np.float64)
+    assert np.array_equal(per_tap, np.broadcast_to(expect[None, :, :, None], per_tap.shape))
