@@ -170,29 +170,38 @@ int launch_t(int ty, const Dw2Args& a, hipStream_t s) {
 }
 
 
-// Strip variant (3x3 filter, stride 1 and dilation 1 on both axes). A lane
-// owns 4 adjacent channels (one 8-byte load per pixel), so that two waves fit
-// on a SIMD. A worker (a wave, or a 64/cl-th of one when a channel block is
-// narrower than the wave) owns a contiguous range of row steps; a step is one
-// output row of a 4-wide column strip, and consecutive steps walk down the
-// strip. The three input rows a step needs are kept in a register ring,
-// already packed into the (column j, column j+1) pairs the dot products read,
-// so a step loads and packs one new input row (6 pixels) and its dY row (4
-// pixels). Compared with independent 4-position units this cuts the L1-to-L2
-// request volume per output position by about 2.2x and the packing work by
-// 3x. Steps are loaded kAhead ahead into three rotating buffers; the loop is
-// unrolled by three so that the ring and buffer rotation is static. Only the
-// first step of a worker and the first step of each new strip reload the two
-// older ring rows.
+// Strip variant (3x3 filter, stride 1 and dilation 1 on both axes).
+//
+// Work items: a 4-wide column strip of one image, cut into nch chunks of
+// consecutive output rows; a worker (a wave, or a 64/cl-th of one when a
+// channel block is narrower than the wave) takes items grid-stride. Within an
+// item it walks the chunk's rows one output row ("step") at a time and keeps
+// the three input rows of the step in a register ring, already packed into
+// the (column j, column j+1) pairs the dot products read, so a step loads and
+// packs one new input row (6 pixels) and its dY row (4 pixels). Steps are
+// loaded kAhead ahead into three rotating buffers; the loop is unrolled by
+// three so that the ring and buffer rotation is static.
+//
+// HBM reuse: items are numbered strip-major, chunk-minor, and chunk c walks
+// down when c is even and up when c is odd. All chunk rows are aligned across
+// strips, so neighbouring strips read their two shared input columns at the
+// same moment, and the two chunks on either side of a chunk boundary reach
+// the boundary's halo rows at the same moment (both at their start, or both
+// at their end). Each shared line then comes from HBM once and from L2 for
+// the second reader, instead of twice.
+//
+// A lane owns 4 adjacent channels (one 8-byte load per pixel); eight waves
+// per workgroup, one workgroup per CU, two waves per SIMD.
 #ifndef DW3_AHEAD
 #define DW3_AHEAD 2
 #endif
 constexpr int kAhead = DW3_AHEAD;   // steps loaded ahead of the one computed (1 or 2)
 constexpr int kW3 = 2;              // 32-bit words (channel pairs) per lane
+constexpr int kDw3Waves = 8;        // waves per workgroup
 
 struct StepBuf {
     u32x2 d[kUnit];      // dY of the step's 4 positions
-    u32x2 xn[kWin];      // newest input row of the step
+    u32x2 xn[kWin];      // the input row that enters the ring at this step
 };
 struct RowPairs {
     uint32_t lo[kW3][kWin - 1], hi[kW3][kWin - 1];   // [word][column j]: (col j, col j+1)
@@ -208,9 +217,15 @@ __device__ __forceinline__ void pack_row(const u32x2* raw, RowPairs& r) {
         }
 }
 
+// ring slot of window row y (0 = top) at step i of an item: walking down the
+// new row is y = 2 and takes the slot row 0 left; walking up it is y = 0 and
+// takes the slot row 2 left
+template <bool UP>
+constexpr int ring_slot(int y, int i) { return UP ? (y + 2 * i) % 3 : (y + i) % 3; }
+
 template <bool F16>
-__global__ __launch_bounds__(256, 2) void dw3_kernel(const Dw3Args a) {
-    constexpr int TY = 3, T = 9, CH = 2 * kW3;
+__global__ __launch_bounds__(64 * kDw3Waves, 1) void dw3_kernel(const Dw3Args a) {
+    constexpr int T = 9, CH = 2 * kW3;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cl = a.cl;
     const int cv = lane % cl;
@@ -220,10 +235,10 @@ __global__ __launch_bounds__(256, 2) void dw3_kernel(const Dw3Args a) {
     const __amdgpu_buffer_rsrc_t x_rs = buf_rsrc(a.x, a.x_bytes);
     const __amdgpu_buffer_rsrc_t dy_rs = buf_rsrc(a.dy, a.dy_bytes);
     const int sub = lane / cl, nsub = 64 / cl;
-    const int wid = (z * 4 + wave) * nsub + sub;
-    const int nworkers = a.waves * nsub;
-    const int st0 = (int)((int64_t)wid * a.steps / nworkers);
-    const int st1 = (int)((int64_t)(wid + 1) * a.steps / nworkers);
+    // worker w = (wave, sub) * S + z: consecutive items go to the same wave
+    // slot of consecutive workgroups (one XCD), and idle workers spread evenly
+    const int wid = (wave * nsub + sub) * a.S + z;
+    const int nworkers = kDw3Waves * nsub * a.S;
 
     float acc[T][CH];
 #pragma unroll
@@ -241,89 +256,79 @@ __global__ __launch_bounds__(256, 2) void dw3_kernel(const Dw3Args a) {
             r[j] = buf_load8(x_rs, ok ? (uint32_t)(((pix + j) * a.C + c0) * 2) : kBufOob);
         }
     };
-    // a step cursor: image, strip start column, output row
-    struct Cur {
-        int n, wo0, ho;
-    };
-    auto decode = [&](int st) {
-        const int strip = st / a.Ho;
-        Cur c;
-        c.ho = st - strip * a.Ho;
-        c.n = strip / a.nseg;
-        c.wo0 = (strip - c.n * a.nseg) * kUnit;
-        return c;
-    };
-    auto advance = [&](Cur& c) {
-        if (++c.ho == a.Ho) {
-            c.ho = 0;
-            c.wo0 += kUnit;
-            if (c.wo0 == a.nseg * kUnit) {
-                c.wo0 = 0;
-                ++c.n;
+
+    auto run_item = [&](int n, int wo0, int r0, int r1, auto up_tag) {
+        constexpr bool UP = decltype(up_tag)::value;
+        const int nsteps = r1 - r0;
+        // output row of step i, and the input row that enters the ring there
+        auto ho_of = [&](int i) { return UP ? r1 - 1 - i : r0 + i; };
+        auto load_step = [&](int i, StepBuf& b) {
+            const bool valid = i < nsteps;
+            const int ho = ho_of(i);
+#pragma unroll
+            for (int p = 0; p < kUnit; ++p) {
+                const bool ok = valid && wo0 + p < a.Wo;
+                b.d[p] = buf_load8(dy_rs, ok ? (uint32_t)((((n * a.Ho + ho) * a.Wo + wo0 + p) * a.C + c0) * 2)
+                                             : kBufOob);
             }
-        }
-    };
-    // loads of one step (all zeros when the step is outside the worker's range)
-    auto load_step = [&](const Cur& c, bool valid, StepBuf& b) {
+            x_row(n, valid ? ho - a.ph + (UP ? 0 : 2) : -1, wo0, b.xn);
+        };
+        RowPairs ring[3];
+        StepBuf buf[3];
 #pragma unroll
-        for (int p = 0; p < kUnit; ++p) {
-            const bool ok = valid && c.wo0 + p < a.Wo;
-            b.d[p] = buf_load8(dy_rs, ok ? (uint32_t)((((c.n * a.Ho + c.ho) * a.Wo + c.wo0 + p) * a.C + c0) * 2)
-                                         : kBufOob);
-        }
-        x_row(c.n, valid ? c.ho - a.ph + TY - 1 : -1, c.wo0, b.xn);
-    };
-
-    RowPairs ring[3];
-    StepBuf buf[3];
-    Cur cc = decode(st0 < st1 ? st0 : 0);   // compute cursor
-    Cur pc = cc;                            // prefetch cursor
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) {
-        load_step(pc, st0 + i < st1, buf[i]);
-        advance(pc);
-    }
-
-    // step st with rotation R: ring slot (R + y) % 3 holds input row y of the step
-    auto sub_step = [&](int st, auto rot) {
-        constexpr int R = decltype(rot)::value;
-        if (st >= st1) return;
-        if (st == st0 || cc.ho == 0) {
+        for (int i = 0; i < kAhead; ++i) load_step(i, buf[i]);
+        {
+            // the two rows of the first window that do not enter at step 0
+            const int ho = ho_of(0);
             u32x2 raw[kWin];
-            x_row(cc.n, cc.ho - a.ph, cc.wo0, raw);
-            pack_row(raw, ring[R % 3]);
-            x_row(cc.n, cc.ho - a.ph + 1, cc.wo0, raw);
-            pack_row(raw, ring[(R + 1) % 3]);
+            x_row(n, ho - a.ph + 1, wo0, raw);
+            pack_row(raw, ring[ring_slot<UP>(1, 0)]);
+            x_row(n, ho - a.ph + (UP ? 2 : 0), wo0, raw);
+            pack_row(raw, ring[ring_slot<UP>(UP ? 2 : 0, 0)]);
         }
-        load_step(pc, st + kAhead < st1, buf[(R + kAhead) % 3]);
-        advance(pc);
-        const StepBuf& b = buf[R % 3];
-        pack_row(b.xn, ring[(R + 2) % 3]);
+        auto sub_step = [&](int i, auto rot) {
+            constexpr int R = decltype(rot)::value;     // i % 3
+            if (i >= nsteps) return;
+            load_step(i + kAhead, buf[(R + kAhead) % 3]);
+            const StepBuf& b = buf[R];
+            pack_row(b.xn, ring[ring_slot<UP>(UP ? 0 : 2, R)]);
 #pragma unroll
-        for (int q = 0; q < kUnit / 2; ++q)
+            for (int q = 0; q < kUnit / 2; ++q)
 #pragma unroll
-            for (int w = 0; w < kW3; ++w) {
-                const uint32_t dlo = pair_lo(b.d[2 * q][w], b.d[2 * q + 1][w]);
-                const uint32_t dhi = pair_hi(b.d[2 * q][w], b.d[2 * q + 1][w]);
+                for (int w = 0; w < kW3; ++w) {
+                    const uint32_t dlo = pair_lo(b.d[2 * q][w], b.d[2 * q + 1][w]);
+                    const uint32_t dhi = pair_hi(b.d[2 * q][w], b.d[2 * q + 1][w]);
 #pragma unroll
-                for (int y = 0; y < TY; ++y)
+                    for (int y = 0; y < 3; ++y)
 #pragma unroll
-                    for (int x = 0; x < 3; ++x) {
-                        const RowPairs& rp = ring[(R + y) % 3];
-                        acc[y * 3 + x][2 * w] = dot2<F16>(dlo, rp.lo[w][2 * q + x], acc[y * 3 + x][2 * w]);
-                        acc[y * 3 + x][2 * w + 1] = dot2<F16>(dhi, rp.hi[w][2 * q + x], acc[y * 3 + x][2 * w + 1]);
-                    }
-            }
-        advance(cc);
+                        for (int x = 0; x < 3; ++x) {
+                            const RowPairs& rp = ring[ring_slot<UP>(y, R)];
+                            acc[y * 3 + x][2 * w] = dot2<F16>(dlo, rp.lo[w][2 * q + x], acc[y * 3 + x][2 * w]);
+                            acc[y * 3 + x][2 * w + 1] =
+                                dot2<F16>(dhi, rp.hi[w][2 * q + x], acc[y * 3 + x][2 * w + 1]);
+                        }
+                }
+        };
+        for (int i = 0; i < nsteps; i += 3) {
+            sub_step(i, std::integral_constant<int, 0>{});
+            sub_step(i + 1, std::integral_constant<int, 1>{});
+            sub_step(i + 2, std::integral_constant<int, 2>{});
+        }
     };
-    for (int st = st0; st < st1; st += 3) {
-        sub_step(st, std::integral_constant<int, 0>{});
-        sub_step(st + 1, std::integral_constant<int, 1>{});
-        sub_step(st + 2, std::integral_constant<int, 2>{});
+
+    for (int it = wid; it < a.items; it += nworkers) {
+        const int strip = it / a.nch, c = it - strip * a.nch;
+        const int n = strip / a.nseg;
+        const int wo0 = (strip - n * a.nseg) * kUnit;
+        const int r0 = (int)((int64_t)c * a.Ho / a.nch), r1 = (int)((int64_t)(c + 1) * a.Ho / a.nch);
+        if (c & 1)
+            run_item(n, wo0, r0, r1, std::true_type{});
+        else
+            run_item(n, wo0, r0, r1, std::false_type{});
     }
 
-    // lanes of one channel lane are cl apart within the wave; then the 4
-    // waves are summed through LDS, both in a fixed order
+    // lanes of one channel lane are cl apart within the wave; then the waves
+    // are summed through LDS, both in a fixed order
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -332,7 +337,7 @@ __global__ __launch_bounds__(256, 2) void dw3_kernel(const Dw3Args a) {
             for (int off = cl; off < 64; off <<= 1) v += __shfl_xor(v, off);
             acc[t][k] = v;
         }
-    __shared__ float part[4][64][T * CH];
+    __shared__ float part[kDw3Waves][64][T * CH];
     if (lane < cl) {
 #pragma unroll
         for (int t = 0; t < T; ++t)
@@ -341,10 +346,12 @@ __global__ __launch_bounds__(256, 2) void dw3_kernel(const Dw3Args a) {
     }
     __syncthreads();
     const int64_t zoff = a.out_mode == OUT_WORKSPACE ? (int64_t)z * a.slice_elems : 0;
-    for (int o = tid; o < cl * T * CH; o += 256) {
+    for (int o = tid; o < cl * T * CH; o += 64 * kDw3Waves) {
         const int v = o / (T * CH), w = o - v * (T * CH);
         const int t = w / CH, k = w - t * CH;
-        const float sum = ((part[0][v][w] + part[1][v][w]) + part[2][v][w]) + part[3][v][w];
+        float sum = part[0][v][w];
+#pragma unroll
+        for (int q = 1; q < kDw3Waves; ++q) sum += part[q][v][w];
         const int c = (cb * cl + v) * CH + k;
         store_out(a.out, a.out_mode, zoff + (int64_t)c * T + t, sum);
     }
@@ -352,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void dw3_kernel(const Dw3Args a) {
 
 template <bool F16>
 int launch_t3(int ty, const Dw3Args& a, hipStream_t s) {
-    dim3 grid(a.total_wg), block(256);
+    dim3 grid(a.total_wg), block(64 * kDw3Waves);
     if (ty != 3) return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL((dw3_kernel<F16>), grid, block, 0, s, a);
     return (int)hipGetLastError();

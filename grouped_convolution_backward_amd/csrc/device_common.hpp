@@ -99,6 +99,37 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t by
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
 }
 
+// Direct buffer-to-LDS load of 16 bytes per lane (gfx950): lane t's bytes land
+// at LDS byte address lds + 16*t; an out-of-range offset writes zeros. Issued
+// from inline assembly so that the compiler does not place its own
+// "wait for every LDS-bound load" before later LDS reads: the callers wait
+// with explicit vmcnt counts for exactly the loads they consume. desc is the
+// buffer descriptor as four scalar words (see buf_desc).
+__device__ __forceinline__ u32x4 buf_desc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4 d;
+    d[0] = (uint32_t)a;
+    d[1] = (uint32_t)(a >> 32) & 0xffffu;   // stride 0
+    d[2] = bytes;
+    d[3] = 0x00020000u;
+    return d;
+}
+__device__ __forceinline__ void dma_load16(const u32x4& desc, uint32_t lds_byte, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_byte), "v"(voff), "s"(desc)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
+}
+
+// s_waitcnt immediate that waits until at most N vector-memory operations of
+// this wave are outstanding and does not wait on LDS/scalar or export counters
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+constexpr int kWaitVm = (N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8);
+
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
 // operations, not for its global stores (__syncthreads also fences global
 // memory, which would stall on outstanding stores for a microsecond or more).

@@ -236,10 +236,16 @@ __global__ __launch_bounds__(256) void reduce_kernel(const ReduceArgs a) {
     }
     const f32x4 acc = (p0 + p1) + (p2 + p3);
     part[t] = acc;
+    // the zl slice lanes of an element are combined by a binary tree in LDS
+    // (lane z takes lane z + h, h = zl/2, zl/4, ..., 1): a fixed order, and
+    // log2(zl) steps instead of a zl-long chain in one thread
+    for (int h = zl >> 1; h >= 1; h >>= 1) {
+        __syncthreads();
+        if (lane_z < h) part[t] += part[t + h * eg];
+    }
     __syncthreads();
     if (lane_z == 0 && v < nvec) {
-        f32x4 s = part[lane_e];
-        for (int l = 1; l < zl; ++l) s += part[l * eg + lane_e];
+        const f32x4 s = part[lane_e];
         if (a.vec4) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) store_out(a.dw, a.out_mode, 4 * v + k, s[k]);

@@ -99,12 +99,17 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
     for (int i = 0; i < kNumRsInstances; ++i) {
         const RsInstance& r = kRsInstances[i];
         if (r.mb != mb || r.cb != cb || r.xf != g.X) continue;
-        if (r.stride != (g.sw == 2 ? 2 : 1)) continue;   // pitch tuned for the pixel step
-        if (4 * 2 * (int64_t)rs_wave_lds(r) > kRsLdsMax) continue;
-        const int64_t ks = 16 * r.nks, xwp = (int64_t)r.nxc * rs_pixels_per_chunk(r);
+        if (r.stride != (g.sw == 2 ? 2 : 1)) continue;   // stride 2 splits the tile into even / odd columns
+        if (rs_lds_bytes(r) > kRsLdsMax) continue;
+        const int64_t ks = 16 * r.nks;
+        // input columns the tile holds: xwp (stride 1), xwp/2 of each parity (stride 2)
+        auto fits = [&](int64_t sw) {
+            const int64_t xw = xw_of(sw);
+            return r.stride == 1 ? xw <= r.xwp : (xw + 1) / 2 <= r.xwp / 2;
+        };
         int64_t sw = std::min<int64_t>(g.Wo, ks);
-        while (sw > 1 && xw_of(sw) > xwp) --sw;
-        if (xw_of(sw) > xwp) continue;
+        while (sw > 1 && !fits(sw)) --sw;
+        if (!fits(sw)) continue;
         int64_t pr = sw == g.Wo ? std::min<int64_t>({ks / sw, (int64_t)r.nxr, std::max<int64_t>(1, NHo)}) : 1;
         const double eff = double(pr * sw) / double(ks);
         if (eff > best + 1e-9) { best = eff; inst = i; PR = pr; SW = sw; }
@@ -123,11 +128,12 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
         spw = ceil_div(nslabs, std::min<int64_t>(o.split_k, nslabs));
         S = ceil_div(nslabs, spw);
     } else {
-        // every wave gets the same number of slabs (the smallest that covers
-        // all slab-tile units with one workgroup per CU), then as few splits as
-        // that allows, which keeps the workspace small
-        const int64_t per_wave = ceil_div(tiles * nslabs, 4 * (int64_t)dev.num_cus);
-        spw = 4 * per_wave;
+        // one workgroup per CU (the kernel's LDS allows no more): as many
+        // splits as fit beside the tiles, each a multiple of four slabs so the
+        // four slab streams of a workgroup get equal counts, then as few
+        // splits as those slab counts need, which keeps the workspace small
+        const int64_t smax = std::max<int64_t>(1, (int64_t)dev.num_cus / tiles);
+        spw = 4 * ceil_div(ceil_div(nslabs, smax), 4);
         S = ceil_div(nslabs, spw);
     }
     if (tiles * S > kMax31 || S > 65535) return no("row-slab grid too large");
@@ -150,7 +156,7 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
     a.dy_bytes = (uint32_t)(2 * NHo * g.Wo * p.K);
     a.mSW = make_magic((uint32_t)SW); a.mXW = make_magic((uint32_t)XW); a.mHo = make_magic((uint32_t)g.Ho);
     out.rs_inst = inst;
-    out.lds_bytes = (int)std::max<int64_t>(4 * 2 * (int64_t)rs_wave_lds(ri), 4 * (int64_t)mb * (cb + 4) * 4);
+    out.lds_bytes = rs_lds_bytes(ri);
     wgrad_plan_info& info = out.info;
     info.tile = 0;
     info.tile_m = mb; info.tile_n = (int32_t)(g.X * cb); info.tile_k = 16 * ri.nks;
@@ -301,22 +307,31 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
             b.C = (int32_t)p.C; b.Hi = (int32_t)g.Hi; b.Wi = (int32_t)g.Wi; b.Ho = (int32_t)g.Ho; b.Wo = (int32_t)g.Wo;
             b.ph = (int32_t)g.ph; b.pw = (int32_t)g.pw;
             b.nseg = (int32_t)ceil_div(g.Wo, 4);
-            const int64_t steps = p.N * b.nseg * g.Ho;
-            if (steps > kMax31) return fail(msg, U, "too many row steps");
-            b.steps = (int32_t)steps;
-            // lanes of 4 channels; two workgroups (8 waves) per CU, a split is
-            // one workgroup's share of a channel block
+            // lanes of 4 channels; one 8-wave workgroup per CU, a split is one
+            // workgroup's share of a channel block
             int cl3 = 64;
             while ((p.C / 4) % cl3) cl3 >>= 1;
             b.cl = cl3;
             b.cblocks = (int32_t)(p.C / 4 / cl3);
             const int64_t nsub = 64 / cl3;
-            int64_t S3 = o.split_k ? o.split_k : std::max<int64_t>(1, 2 * (int64_t)dev.num_cus / b.cblocks);
-            S3 = std::max<int64_t>(1, std::min<int64_t>(S3, ceil_div(std::max<int64_t>(steps, 1), 4 * nsub)));
-            if (steps == 0) S3 = 1;
+            const int64_t strips = p.N * b.nseg;
+            int64_t S3 = o.split_k ? o.split_k : std::max<int64_t>(1, (int64_t)dev.num_cus / b.cblocks);
+            // never more workgroups than strips need at one chunk per strip
+            S3 = std::max<int64_t>(1, std::min<int64_t>(S3, ceil_div(std::max<int64_t>(strips * g.Ho, 1), 8 * nsub)));
             if (S3 > 65535 || S3 * b.cblocks > kMax31) return fail(msg, U, "split_k too large");
+            // chunks per strip: fewest passes x rows per chunk, counting the
+            // two ring rows loaded at each item's start as one more row
+            const int64_t workers = 8 * nsub * S3;
+            int64_t best_nch = 1, best_cost = INT64_MAX;
+            for (int64_t nch = 1; nch <= std::max<int64_t>(1, g.Ho); ++nch) {
+                const int64_t passes = ceil_div(std::max<int64_t>(strips * nch, 1), workers);
+                const int64_t cost = passes * (ceil_div(g.Ho, nch) + 1);
+                if (cost < best_cost) { best_cost = cost; best_nch = nch; }
+            }
+            if (strips * best_nch > kMax31) return fail(msg, U, "too many strip chunks");
+            b.nch = (int32_t)best_nch;
+            b.items = (int32_t)(strips * best_nch);
             b.S = (int32_t)S3;
-            b.waves = (int32_t)(4 * S3);
             b.total_wg = (int32_t)(S3 * b.cblocks);
             b.out_mode = S3 == 1 ? out_final : OUT_WORKSPACE;
             b.slice_elems = (int32_t)ndw;

@@ -9,18 +9,31 @@
 //   MB x (X*CB), and for one output row it needs exactly one input row.
 // * The reduction runs over slabs of PR output rows x SW output columns. A
 //   slab's dY rows are staged K-outer ([position][channel]) and its input
-//   rows as a pixel tile ([row][column][channel]); tap x of position k is
-//   pixel (k / SW, (k % SW)*stride + x*dilation) of that tile, so the three
-//   (or five) taps of the row are shifted reads of one tile.
+//   rows as a pixel tile ([row][pixel][channel]); tap x of position k is a
+//   fixed pixel shift of k's own pixel, so the three (or five) taps of the
+//   row are shifted reads of one tile. For stride 2 the tile holds the even
+//   input columns, then the odd ones, so every tap still reads consecutive
+//   pixels.
 // * MFMA operands come from the CDNA4 transposed LDS read
 //   ds_read_b64_tr_b16 (rocm-libraries PR 11602): each lane supplies the
 //   address of its own reduction row, which here is a per-lane pixel offset,
-//   so the halo tile needs no per-tap copy and nothing is transposed on store.
-// * Each of the four waves holds the whole workgroup tile in registers and
-//   takes every fourth slab of the workgroup's split; a wave only touches its
-//   own LDS region, so the slab loop has no workgroup barrier. The next
-//   slab's global loads are issued before the current slab's MFMAs and wait
-//   in registers (the single-buffer "basic" schedule of PR 11602).
+//   so the tile needs no per-tap copy and nothing is transposed on store.
+// * Tiles go from HBM to LDS with buffer loads that write LDS directly (16
+//   bytes per lane, lane-major), so no registers stage them and no LDS store
+//   instructions compete with the fragment reads. Each slab stream owns nb
+//   slab buffers and loads slabs nb - 1 ahead of the one it computes;
+//   a slab's loads are spread over the k-steps of the current slab, so the
+//   load path (64 B per clock per CU) never backs up into the MFMA issue.
+//   16-byte chunks are XOR-swizzled by bit 1 of the row (64-channel rows), so
+//   the four rows a 16-lane group reads land on all banks; the loads apply
+//   the swizzle by choosing which source chunk each lane fetches.
+// * The workgroup runs four slab streams; stream p takes every fourth slab of
+//   the workgroup's split into its own nb LDS buffers and holds the whole
+//   workgroup tile in registers. With 64-channel blocks a stream is two waves
+//   on one SIMD, each holding half of the channels and issuing half of the
+//   loads, with one workgroup barrier per slab; two waves per SIMD let one
+//   issue MFMAs while the other waits to issue loads. With 32-channel blocks a
+//   stream is one wave and the slab loop has no barrier.
 // * At the end the four wave tiles are added in LDS in a fixed order and the
 //   workgroup writes one partial (S > 1: fp32 workspace slice) or dW itself.
 //   With merged groups only diagonal group pairs are stored (PR 12359).
@@ -52,26 +65,43 @@ __device__ __forceinline__ void store4(void* out, int mode, int64_t e, const f32
     }
 }
 
-template <int MB, int CB, int XF, int NKS, int NXR, int NXC, int PA, int PX, bool ASWZ, bool F16>
-__global__ __launch_bounds__(256, 1) void rowslab_kernel(const RowSlabArgs a) {
+// s_waitcnt that leaves at most later * PER of this wave's vector-memory
+// loads outstanding, for later in 0..MAXL (immediate operands need a branch)
+template <int MAXL, int PER>
+__device__ __forceinline__ void vm_wait_slabs(int later) {
+    if (MAXL >= 2 && later >= 2) __builtin_amdgcn_s_waitcnt(kWaitVm<(MAXL >= 2 ? 2 * PER : 0)>);
+    else if (MAXL >= 1 && later >= 1) __builtin_amdgcn_s_waitcnt(kWaitVm<PER>);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+}
+
+template <int MB, int CB, int XF, int NKS, int NXR, int XWP, int STRIDE, int NB, int WPS, bool F16>
+__global__ __launch_bounds__(256 * WPS, 1) void rowslab_kernel(const RowSlabArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-    static_assert(PA >= MB && PX >= CB && PA % 8 == 0 && PX % 8 == 0, "LDS pitches");
-    static_assert(!ASWZ || MB == 64, "the dY swizzle is defined for 64-wide rows");
-    constexpr int FM = MB / 32, FC = CB / 32, FN = XF * FC;
-    constexpr int AV = MB / 8, XV = CB / 8;        // 16-byte vectors per position / pixel
+    constexpr int NT = 256 * WPS;                  // threads per workgroup
+    constexpr int FM = MB / 32, FC = CB / 32;
+    constexpr int FCW = FC / WPS, FNW = XF * FCW;  // 32-channel blocks and B fragments per wave
     constexpr int KS = 16 * NKS;                   // positions per slab (padded)
-    constexpr int APL = 64 / AV;                   // positions per dY load instruction
-    constexpr int NA = KS / APL;
-    constexpr int PPL = 64 / XV;                   // pixels per X load instruction
-    constexpr int XWP = NXC * PPL;                 // pixels per X tile row in LDS
-    constexpr int WAVE_LDS = KS * PA + NXR * XWP * PX;
+    constexpr int ACH = MB / 8, XCH = CB / 8;      // 16-byte chunks per position / pixel
+    constexpr int RA = 64 / ACH, RX = 64 / XCH;    // rows one 1 KB load fills
+    constexpr int NA = KS / RA, NXI = NXR * XWP / RX;
+    constexpr int NL = NA + NXI;                   // loads per slab
+    constexpr int ABUF = KS * MB;                  // elements of the dY tile
+    constexpr int BUF = ABUF + NXR * XWP * CB;     // elements of one slab buffer
+    constexpr int HALF = XWP / 2;                  // stride 2: odd input columns start here
     constexpr int RP = CB + 4;                     // row pitch of the reduction tile (floats)
     constexpr int TILE = MB * RP;
-    static_assert(KS % APL == 0, "slab positions");
+    static_assert(KS % RA == 0 && XWP % RX == 0 && (STRIDE == 1 || HALF % RX == 0), "slab geometry");
+    static_assert((NB - 1) * NL <= 63, "vmcnt range");
+    static_assert(NB >= 2 && NB <= 4, "slab buffers");
+    static_assert(MB == 64 || MB == 32, "M block");
+    static_assert(FC % WPS == 0 && (WPS == 1 || CB == 64), "channel split between the waves of a slab");
+    static_assert(NKS % 2 == 0, "fragment double buffer restarts at 0 each slab");
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint16_t* sA = smem + wave * WAVE_LDS;
-    uint16_t* sX = sA + KS * PA;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = wave & 3;                     // slab stream of this wave
+    const int half = wave >> 2;                    // its part of the channel block (WPS = 2)
+    uint16_t* wbuf = smem + pair * NB * BUF;
 
     const int L = xcd_logical_id(blockIdx.x, a.total_wg);
     int t = L % a.tiles;
@@ -87,37 +117,36 @@ __global__ __launch_bounds__(256, 1) void rowslab_kernel(const RowSlabArgs a) {
     const int s_end = min(a.nslabs, s_begin + a.spw);
     const int hoff = y * a.dh - a.ph;
     const int kreal = a.PR * a.SW;
+    const u32x4 dy_desc = buf_desc(a.dy, a.dy_bytes);
+    const u32x4 x_desc = buf_desc(a.x, a.x_bytes);
 
-    // dY: the slab's positions are one contiguous run of r (whole rows, or a
-    // segment of one row), so load i of a lane reads position lane/AV + i*APL
-    const int a_cv = lane % AV;
-    const bool a_ok = m0 + a_cv * 8 < a.Mm;
-    const __amdgpu_buffer_rsrc_t dy_rs = buf_rsrc(a.dy, a.dy_bytes);
-    const __amdgpu_buffer_rsrc_t x_rs = buf_rsrc(a.x, a.x_bytes);
-    const uint32_t a_lane = (uint32_t)(((lane / AV) * a.Ktot + gb * a.gkpg + m0 + a_cv * 8) * 2);
-    const uint32_t a_step = (uint32_t)(APL * a.Ktot * 2);
-    // X: load (q, cc) of a lane reads pixel column cc*PPL + lane/XV of tile row q
-    const int x_cv = lane % XV;
-    const int x_col = lane / XV;
-    const int x_chan = gb * a.gcpg + c0 + x_cv * 8;
+    // lane roles in the loads: lane -> (row ja of the 1 KB block, LDS slot);
+    // the slot holds source chunk slot ^ swizzle(row), and bit 1 of the row is
+    // bit 1 of ja for every block (a block starts on a multiple of 8 rows)
+    const int ja = lane / ACH;
+    const int a_chunk = (lane % ACH) ^ (MB == 64 ? 4 * ((ja >> 1) & 1) : 0);
+    const bool a_ok = m0 + a_chunk * 8 < a.Mm;
+    const uint32_t a_lane = (uint32_t)((ja * a.Ktot + gb * a.gkpg + m0 + a_chunk * 8) * 2);
+    const uint32_t a_step = (uint32_t)(RA * a.Ktot * 2);
+    const int jx = lane / XCH;
+    const int x_chunk = (lane % XCH) ^ (CB == 64 ? 4 * ((jx >> 1) & 1) : 0);
+    const int x_chan = gb * a.gcpg + c0 + x_chunk * 8;
 
-    u32x4 ra[NA], rx[NXR][NXC];
-    // per-slab load geometry, computed once; the loads themselves are issued
-    // in NKS parts, one part per k-step of the previous slab's MFMA stream
+    // per-slab load geometry; issue_part then issues this wave's share
+    // (loads l with l % WPS == half) of loads [l0, l1) of the slab into buffer
+    // bsel. Out-of-range lanes write zeros, so padding needs no branch.
     struct SlabGeo {
         uint32_t abase;
         int kvalid, wbase;
-        int pix0[NXR];
-        bool row_ok[NXR];
+        int pixrow[NXR];
+        bool rowok[NXR];
     };
-    // valid == false gives a geometry whose loads are all out of range (they
-    // return zeros without touching memory), so the load stream needs no branch
-    auto slab_geo = [&](int slab, bool valid) {
+    auto slab_geo = [&](int slab) {
         SlabGeo gq;
         const int sr = slab / a.nseg;
         const int row0 = sr * a.PR, wo0 = (slab - sr * a.nseg) * a.SW;
         const int r0 = row0 * a.Wo + wo0;
-        gq.kvalid = valid ? min(kreal, a.SW == a.Wo ? a.NHo * a.Wo - r0 : a.Wo - wo0) : 0;
+        gq.kvalid = min(kreal, a.SW == a.Wo ? a.NHo * a.Wo - r0 : a.Wo - wo0);
         gq.abase = a_lane + (uint32_t)(r0 * a.Ktot * 2);
         gq.wbase = wo0 * a.sw - a.pw;
 #pragma unroll
@@ -125,127 +154,146 @@ __global__ __launch_bounds__(256, 1) void rowslab_kernel(const RowSlabArgs a) {
             const int row = row0 + q;
             const int n = (int)magic_div((uint32_t)row, a.mHo);
             const int hi = (row - n * a.Ho) * a.sh + hoff;
-            gq.row_ok[q] = valid && q < a.PR && row < a.NHo && (unsigned)hi < (unsigned)a.Hi;
-            gq.pix0[q] = (n * a.Hi + hi) * a.Wi + gq.wbase + x_col;
+            gq.rowok[q] = q < a.PR && row < a.NHo && (unsigned)hi < (unsigned)a.Hi;
+            gq.pixrow[q] = (n * a.Hi + hi) * a.Wi;
         }
         return gq;
     };
-    constexpr int NL = NA + NXR * NXC;                 // loads per slab
-    auto gload_part = [&](const SlabGeo& gq, int part, int nparts) {
+    auto issue_part = [&](const SlabGeo& gq, int bsel, int l0, int l1) {
+        uint16_t* sA = wbuf + bsel * BUF;
+        uint16_t* sX = sA + ABUF;
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
-            if (l * nparts / NL != part) continue;
+            if (l < l0 || l >= l1) continue;           // l0, l1 are compile-time at every call
+            if (WPS > 1 && l % WPS != half) continue;
             if (l < NA) {
-                const int k = lane / AV + l * APL;
-                ra[l] = buf_load16(dy_rs, (a_ok && k < gq.kvalid) ? gq.abase + l * a_step : kBufOob);
+                const bool ok = a_ok && l * RA + ja < gq.kvalid;
+                dma_load16(dy_desc, lds_addr(sA + l * RA * MB), ok ? gq.abase + l * a_step : kBufOob);
             } else {
-                const int q = (l - NA) / NXC, cc = (l - NA) % NXC;
-                const int col = cc * PPL + x_col;
-                const bool ok = gq.row_ok[q] && col < a.XW && (unsigned)(gq.wbase + col) < (unsigned)a.Wi;
-                rx[q][cc] = buf_load16(x_rs, ok ? (uint32_t)(((gq.pix0[q] + cc * PPL) * a.Ctot + x_chan) * 2) : kBufOob);
+                const int i = l - NA;
+                const int q = (i * RX) / XWP;
+                const int pj = (i * RX) % XWP + jx;
+                const int off = STRIDE == 1 ? pj : (pj < HALF ? 2 * pj : 2 * (pj - HALF) + 1);
+                const int col = gq.wbase + off;
+                const bool ok = gq.rowok[q] && off < a.XW && (unsigned)col < (unsigned)a.Wi;
+                dma_load16(x_desc, lds_addr(sX + i * RX * CB),
+                           ok ? (uint32_t)(((gq.pixrow[q] + col) * a.Ctot + x_chan) * 2) : kBufOob);
             }
         }
     };
-    // every slot of the wave's tiles is written (out-of-range slots hold zeros);
-    // dY chunk a_cv of position k goes to slot a_cv ^ 4*((k >> 1) & 1), and bit 1
-    // of k = lane/AV + i*APL is bit 1 of lane/AV for every i
-    const int a_slot = ASWZ ? (a_cv ^ (4 * (((lane / AV) >> 1) & 1))) : a_cv;
-    uint16_t* sA_lane = sA + (lane / AV) * PA + a_slot * 8;
-    uint16_t* sX_lane = sX + x_col * PX + x_cv * 8;
-    auto sstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < NA; ++i) *reinterpret_cast<u32x4*>(sA_lane + i * APL * PA) = ra[i];
-#pragma unroll
-        for (int q = 0; q < NXR; ++q)
-#pragma unroll
-            for (int cc = 0; cc < NXC; ++cc)
-                *reinterpret_cast<u32x4*>(sX_lane + (q * XWP + cc * PPL) * PX) = rx[q][cc];
-    };
+    // loads of one slab this wave issues (compile-time per half)
+    constexpr int NLW0 = (NL + WPS - 1) / WPS, NLW1 = NL / WPS;
 
-    // issue the first slab's loads before the lane tables are built, so that
-    // their latency covers the setup arithmetic
-    int s = s_begin + wave;
-    if (s < s_end) {
-        const SlabGeo g0 = slab_geo(s, true);
+    // this stream's slabs: s_begin + pair + 4*i, i < cnt; the first NB - 1 are
+    // issued now, slab i + NB - 1 during the k-steps of slab i. Every wave of
+    // the workgroup runs cnt_max iterations (the barrier count must agree).
+    const int cnt = s_begin + pair < s_end ? (s_end - s_begin - pair + 3) / 4 : 0;
+    const int cnt_max = s_end > s_begin ? (s_end - s_begin + 3) / 4 : 0;
 #pragma unroll
-        for (int p = 0; p < NKS; ++p) gload_part(g0, p, NKS);
-    }
+    for (int i = 0; i < NB - 1; ++i)
+        if (i < cnt) issue_part(slab_geo(s_begin + pair + 4 * i), i, 0, NL);
 
     // lane geometry of the transposed reads: rows frow (+4), columns fcol..fcol+3
     const int g16 = lane >> 4;
     const int frow = (g16 >> 1) * 8 + ((lane & 15) >> 2);
     const int fcol = (g16 & 1) * 16 + (lane & 3) * 4;
-    // pixel (as an LDS element offset) of each reduction row this lane
-    // addresses; rows past the slab's positions point at pixel 0 (their dY is 0)
-    int xoff[NKS][2];
+    // LDS element offset (inside a buffer's X tile) of the pixel each
+    // reduction row of this lane reads for tap x, swizzle included, for the
+    // wave's first 32-channel block (for 64-channel rows the other block is
+    // the same address with bit 5 flipped); rows past the slab's positions
+    // read pixel 0, whose products are zero because their dY rows are zero
+    constexpr int XOFF_N = CB == 64 ? XF : 1;
+    int xaddr[NKS][2][XOFF_N];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int k = ks * 16 + frow + 4 * h;
             const int q = (int)magic_div((uint32_t)k, a.mSW);
-            xoff[ks][h] = k < kreal ? (q * XWP + (k - q * a.SW) * a.sw) * PX : 0;
+            const int col = k - q * a.SW;
+            const int base = k < kreal ? q * XWP + col : 0;
+#pragma unroll
+            for (int x = 0; x < XOFF_N; ++x) {
+                const int j = base + (STRIDE == 1 ? x : (x & 1) * HALF + (x >> 1));
+                xaddr[ks][h][x] = CB == 64 ? (j * CB + (((j >> 1) & 1) << 5) + fcol) ^ ((half * FCW) << 5)
+                                           : j * CB + fcol;
+            }
         }
 
-    // the lane's reduction rows share bit 1 (bit 3 of the lane id), so its swizzle
-    // swaps the two 32-column fragments of a 64-wide row
-    const int a_sw = ASWZ ? ((lane >> 3) & 1) : 0;
-    const uint16_t* aread = sA + frow * PA + fcol;
-    const uint16_t* bread = sX + fcol;
+    // the lane's reduction rows share bit 1 (bit 3 of the lane id), so the dY
+    // swizzle swaps the two 32-column fragments of a 64-wide row
+    const int a_sw = MB == 64 ? ((lane >> 3) & 1) : 0;
 
-    f32x16 acc[FM][FN];
+    f32x16 acc[FM][FNW];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{0};
+        for (int j = 0; j < FNW; ++j) acc[i][j] = f32x16{0};
 
-    i16x8 af[2][FM], bf[2][FN];
-    auto read_frags = [&](int ks, i16x8* fa, i16x8* fb) {
+    i16x8 af[2][FM], bf[2][FNW];
+    auto read_frags = [&](const uint16_t* sA, int ks, i16x8* fa, i16x8* fb) {
+        const uint16_t* sX = sA + ABUF;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[i] = tr_frag(aread + ks * 16 * PA + (i ^ a_sw) * 32, PA);
+        for (int i = 0; i < FM; ++i) fa[i] = tr_frag(sA + (ks * 16 + frow) * MB + (i ^ a_sw) * 32 + fcol, MB);
 #pragma unroll
         for (int x = 0; x < XF; ++x)
 #pragma unroll
-            for (int fc = 0; fc < FC; ++fc) {
-                const uint16_t* b = bread + x * PX + fc * 32;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + xoff[ks][0]));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + xoff[ks][1]));
-                fb[x * FC + fc] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            for (int fc = 0; fc < FCW; ++fc) {
+                int o0, o1;
+                if constexpr (CB == 64) {
+                    o0 = xaddr[ks][0][x] ^ (fc << 5);
+                    o1 = xaddr[ks][1][x] ^ (fc << 5);
+                } else {
+                    const int dx = (STRIDE == 1 ? x : (x & 1) * HALF + (x >> 1)) * CB + fc * 32;
+                    o0 = xaddr[ks][0][0] + dx;
+                    o1 = xaddr[ks][1][0] + dx;
+                }
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sX + o0));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sX + o1));
+                fb[x * FCW + fc] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
     };
-    for (; s < s_end; s += 4) {
-        sstore();
-        const bool more = s + 4 < s_end;
-        const SlabGeo gn = slab_geo(more ? s + 4 : s, more);
-        read_frags(0, af[0], bf[0]);
-        // each k-step: the MFMAs of this step interleaved with the fragment
-        // reads of the next step and one part of the next slab's global loads,
-        // so that LDS latency, VMEM issue and address arithmetic overlap the
-        // matrix pipe
+    // wait until slab i's loads from this wave have landed: at most the loads
+    // of the slabs issued after it (up to NB - 2 of them) stay outstanding
+    auto wait_slab = [&](int i) {
+        const int later = i < cnt ? min(cnt - 1 - i, NB - 2) : 0;
+        if (WPS == 1 || half == 0) vm_wait_slabs<NB - 2, NLW0>(later);
+        else vm_wait_slabs<NB - 2, NLW1>(later);
+    };
+    for (int i = 0; i < cnt_max; ++i) {
+        wait_slab(i);
+        // the other half of the slab is the partner wave's; the barrier also
+        // tells every wave that the buffer refilled below is no longer read
+        if (WPS > 1) __builtin_amdgcn_s_barrier();
+        if (i >= cnt) continue;
+        const bool pre = i + NB - 1 < cnt;
+        const SlabGeo gn = slab_geo(s_begin + pair + 4 * (pre ? i + NB - 1 : i));
+        const int bn = (i + NB - 1) % NB;
+        const uint16_t* sA = wbuf + (i % NB) * BUF;
+        read_frags(sA, 0, af[0], bf[0]);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int cur = ks & 1;
             __builtin_amdgcn_sched_barrier(0);
-            if (ks + 1 < NKS) read_frags(ks + 1, af[cur ^ 1], bf[cur ^ 1]);
-            gload_part(gn, ks, NKS);
+            if (pre) issue_part(gn, bn, ks * NL / NKS, (ks + 1) * NL / NKS);
+            if (ks + 1 < NKS) read_frags(sA, ks + 1, af[cur ^ 1], bf[cur ^ 1]);
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+            for (int j = 0; j < FNW; ++j)
 #pragma unroll
-                for (int i = 0; i < FM; ++i) mfma_step32<F16>(af[cur][i], bf[cur][j], acc[i][j]);
+                for (int i2 = 0; i2 < FM; ++i2) mfma_step32<F16>(af[cur][i2], bf[cur][j], acc[i2][j]);
 #pragma unroll
-            for (int m = 0; m < FM * FN; ++m) {
+            for (int m = 0; m < FM * FNW; ++m) {
                 __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // the next iteration's stores must follow this slab's reads
+        // the loads that later refill this buffer must follow these reads
         asm volatile("" ::: "memory");
     }
 
-    // ---- sum the four wave tiles in LDS (fixed order) and store, one tap at a time
+    // ---- sum the four stream tiles in LDS (fixed order) and store, one tap at a time
     lds_barrier();
     float* red = reinterpret_cast<float*>(smem);
     const int mbase = gb * a.gkpg;
@@ -255,18 +303,19 @@ __global__ __launch_bounds__(256, 1) void rowslab_kernel(const RowSlabArgs a) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int fc = 0; fc < FC; ++fc)
+            for (int fc = 0; fc < FCW; ++fc)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int row = i * 32 + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
-                    const int col = fc * 32 + (lane & 31);
-                    red[wave * TILE + row * RP + col] = acc[i][x * FC + fc][v];
+                    const int col = (half * FCW + fc) * 32 + (lane & 31);
+                    red[pair * TILE + row * RP + col] = acc[i][x * FCW + fc][v];
                 }
         lds_barrier();
-        // thread t sums the float4 at row t/(CB/4) + u*(256/(CB/4)), columns
+        // thread t sums the float4 at row t/(CB/4) + u*(NT/(CB/4)), columns
         // (t % (CB/4))*4 .. +3 of this tap's tile, for u = 0, 1, ...
         constexpr int TPR = CB / 4;                 // threads per tile row
-        constexpr int RPI = 256 / TPR;              // rows per pass
+        constexpr int RPI = NT / TPR;               // rows per pass
+        static_assert(MB % RPI == 0, "reduction passes");
         const int col = (threadIdx.x % TPR) * 4;
         const int cg = c0 + col;                    // channel inside the merged run
         const int gj = cg / a.cpg;                  // group of this column
@@ -290,10 +339,11 @@ __global__ __launch_bounds__(256, 1) void rowslab_kernel(const RowSlabArgs a) {
 template <int I, bool F16>
 int launch_rs(const Plan& plan, const RowSlabArgs& a, hipStream_t s) {
     constexpr RsInstance r = kRsInstances[I];
-    auto k = rowslab_kernel<r.mb, r.cb, r.xf, r.nks, r.nxr, r.nxc, r.pa, r.px, (bool)r.aswz, F16>;
+    constexpr int wps = rs_waves_per_slab(r);
+    auto k = rowslab_kernel<r.mb, r.cb, r.xf, r.nks, r.nxr, r.xwp, r.stride, r.nb, wps, F16>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes);
     if (e != hipSuccess) return (int)e;
-    hipLaunchKernelGGL(k, dim3(a.total_wg), dim3(256), plan.lds_bytes, s, a);
+    hipLaunchKernelGGL(k, dim3(a.total_wg), dim3(256 * wps), plan.lds_bytes, s, a);
     return (int)hipGetLastError();
 }
 

@@ -60,32 +60,31 @@ struct MfmaArgs {
 
 // Row-slab kernel instances, shared by the planner and the kernels. Each
 // fixes the tile (M block mb, C block cb, filter width xf) and the slab
-// geometry at compile time: nks 16-position MFMA steps per slab, an X tile of
-// nxr rows x nxc load chunks (a chunk is 64 / (cb / 8) pixels). Fixed shapes
-// keep the slab loop free of runtime guards, so accumulators never need
-// merging copies and LDS stores are unconditional.
-// LDS layout: a 16-lane group of a transposed read fetches 4 rows x 16
-// columns (two 16-byte chunks per row). 64-wide dY rows (128 bytes) use an
-// XOR swizzle instead of padding: chunk c of row r is stored in slot
-// c ^ 4*((r >> 1) & 1), which puts the 4 rows of two groups on all 64 banks
-// once. X pixels use a padded pitch px: 48 words (96 elements) for stride 1,
-// 40 words (80 elements) for stride 2, where a read steps two pixels. 32-wide
-// rows need neither (four consecutive 64-byte rows already cover the banks).
+// geometry at compile time: nks 16-position MFMA steps per slab and an X tile
+// of nxr rows x xwp pixels, for one w-stride. Fixed shapes keep the slab loop
+// free of runtime guards, so accumulators never need merging copies.
+// LDS: each slab stream owns nb slab buffers of 16*nks*mb + nxr*xwp*cb
+// elements, filled by 1 KB direct-to-LDS loads (8 rows of 64 channels or 16
+// rows of 32); slabs are loaded nb - 1 ahead of the one computed.
 constexpr int kRsLdsMax = 160 * 1024;
 struct RsInstance {
-    int mb, cb, xf, nks, nxr, nxc, pa, px, aswz, stride;
+    int mb, cb, xf, nks, nxr, xwp, stride, nb;
 };
 constexpr RsInstance kRsInstances[] = {
-    {64, 64, 3, 7, 2, 8, 64, 96, 1, 1},   // two 56-wide output rows
-    {64, 64, 3, 4, 2, 8, 64, 80, 1, 2},   // two rows up to 32 wide, stride 2
-    {32, 32, 3, 7, 4, 2, 32, 32, 0, 1},   // four 28-wide rows
-    {32, 32, 3, 8, 2, 4, 32, 32, 0, 1},   // two rows up to 64 wide
-    {32, 32, 5, 8, 1, 9, 32, 32, 0, 1},   // one 128-wide row segment (1D)
+    {64, 64, 3, 2, 1, 40, 1, 4},    // 32-position row segments
+    {64, 64, 3, 2, 1, 64, 2, 3},    // one row up to 31 wide, stride 2
+    {32, 32, 3, 4, 2, 32, 1, 4},    // two rows up to 30 wide
+    {32, 32, 3, 4, 1, 80, 1, 4},    // one row (or segment) up to 64 wide
+    {32, 32, 5, 8, 1, 144, 1, 2},   // 128-position row segments, width-5 filter
 };
 constexpr int kNumRsInstances = sizeof(kRsInstances) / sizeof(kRsInstances[0]);
-inline int rs_pixels_per_chunk(const RsInstance& r) { return 64 / (r.cb / 8); }
-inline int rs_wave_lds(const RsInstance& r) {
-    return 16 * r.nks * r.pa + r.nxr * r.nxc * rs_pixels_per_chunk(r) * r.px;
+// waves per slab stream: two for 64-channel blocks (each holds 32 channels)
+constexpr int rs_waves_per_slab(const RsInstance& r) { return r.cb == 64 ? 2 : 1; }
+inline int rs_buffer_elems(const RsInstance& r) { return 16 * r.nks * r.mb + r.nxr * r.xwp * r.cb; }
+inline int rs_lds_bytes(const RsInstance& r) {
+    const int slabs = 4 * r.nb * rs_buffer_elems(r) * 2;         // 4 streams, 16-bit elements
+    const int reduce = 4 * r.mb * (r.cb + 4) * 4;                // fp32 stream tiles of the epilogue
+    return slabs > reduce ? slabs : reduce;
 }
 
 // Row-slab MFMA kernel: a workgroup owns one filter row y of one
@@ -149,19 +148,20 @@ struct Dw2Args {
     MagicU32 mHo, mSeg;
 };
 
-// Depthwise strip kernel (filter width 3, stride and dilation 1 on both axes):
-// a wave walks down a 4-wide column strip keeping the filter's input rows in
-// registers, so each step loads one new input row and one dY row.
+// Depthwise strip kernel (3x3 filter, stride and dilation 1 on both axes):
+// work items are row chunks of 4-wide column strips; a worker walks a chunk
+// keeping the filter's input rows in registers, so each output row loads one
+// new input row and one dY row.
 struct Dw3Args {
     const uint16_t* x;
     const uint16_t* dy;
     void* out;
     int32_t C, Hi, Wi, Ho, Wo, ph, pw;
-    int32_t nseg;          // 4-wide strips per image
-    int32_t steps;         // N * nseg * Ho row steps (strip-major, then row)
-    int32_t cl, cblocks;   // channel lanes (8 channels each) and channel blocks
-    int32_t waves;         // waves per channel block (4 per workgroup)
-    int32_t S, total_wg, out_mode, slice_elems;
+    int32_t nseg;          // 4-wide strips per image row
+    int32_t nch;           // row chunks per strip
+    int32_t items;         // N * nseg * nch items per channel block (strip-major)
+    int32_t cl, cblocks;   // channel lanes (4 channels each) and channel blocks
+    int32_t S, total_wg, out_mode, slice_elems;   // S: workgroups (slices) per channel block
     uint32_t x_bytes, dy_bytes;
 };
 

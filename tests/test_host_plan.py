@@ -180,9 +180,10 @@ def test_depthwise_kernel_forms():
     assert plan(strided).info["tile"] == 2
     _expect(gcb.ERR_UNSUPPORTED, strided, variant=gcb.VARIANT_DEPTHWISE, tile=3)
     _expect(gcb.ERR_UNSUPPORTED, c5, variant=gcb.VARIANT_DEPTHWISE, tile=4)
-    # strip-form splits: one per workgroup, two workgroups per CU
+    # strip form: one 8-wave workgroup per CU, a split per workgroup of a
+    # 256-channel block (two blocks for C = 512)
     p = plan(c5)
-    assert p.info["grid_main"] == 2 * 256
+    assert p.info["grid_main"] == 256 and p.info["split_k"] == 128
 
 
 def test_magic_division_exhaustive(tmp_path):
