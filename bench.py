@@ -12,12 +12,13 @@ the same way and reported under "per_config".
 Honest memory: each configuration cycles through enough copies of its inputs
 (> 512 MB in total) that no step finds its inputs in the 256 MB MALL left
 behind by the previous steps. Steps are replayed from HIP graphs (captured
-through torch) so that the host's launch rate does not set the time.
+through torch, at least 64 steps per graph) so that neither the host's
+launch rate nor a graph replay's own start-up sets the time.
 
 Dominant-kernel roofline: the per-launch duration of the main kernel comes
 from HIP events recorded on the launch stream around replays of a graph that
-holds only wgrad_run_stage(1) launches (one per input set), divided by the
-launch count; achieved = algorithmic FLOPs or bytes per launch / that
+holds only wgrad_run_stage(1) launches (at least 64, cycling through the
+input sets), divided by the launch count; achieved = algorithmic FLOPs or bytes per launch / that
 duration. traffic = HBM bytes per launch from committed rocprofv3 FETCH_SIZE
 and WRITE_SIZE runs, each scaled by what the counter reads for a plain
 device copy of known size (--copy-calibration), when they were taken on the
@@ -45,6 +46,7 @@ PEAK_HBM = 8.0e12         # HBM3E, B/s
 METRIC = "wgrad TFLOP/s (GB/s for depthwise) and % of roofline, 1 MI355X"
 HEADLINE = "c2"
 ROTATE_BYTES = 600 * 2 ** 20
+GRAPH_MIN_LAUNCHES = 64
 
 
 def algorithmic(cfg, info):
@@ -110,7 +112,8 @@ class Case:
         j = i % self.nsets
         self.plan.run(self.xs[j], self.dys[j], self.dw, self.ws, stage=stage)
 
-    def capture(self, nsteps):
+    def capture(self, nsteps, stage=0):
+        """A HIP graph of nsteps launches (cycling through the input sets)."""
         torch = self.torch
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -118,9 +121,13 @@ class Case:
         with torch.cuda.stream(s):
             with torch.cuda.graph(g, stream=s):
                 for i in range(nsteps):
-                    self.step(i)
+                    self.step(i, stage=stage)
         torch.cuda.current_stream().wait_stream(s)
         return g
+
+    def graph_len(self):
+        # enough launches per graph that the replay's own cost is spread thin
+        return self.nsets * max(1, math.ceil(GRAPH_MIN_LAUNCHES / self.nsets))
 
     def time_steps(self, steps, warmup, use_graphs=True):
         torch = self.torch
@@ -128,15 +135,16 @@ class Case:
             self.step(i)
         torch.cuda.synchronize()
         if use_graphs:
-            full = self.capture(self.nsets)
-            rem = steps % self.nsets
+            glen = self.graph_len()
+            full = self.capture(glen)
+            rem = steps % glen
             tail = self.capture(rem) if rem else None
             full.replay()                      # untimed: graph upload
             if tail is not None:
                 tail.replay()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            for _ in range(steps // self.nsets):
+            for _ in range(steps // glen):
                 full.replay()
             if tail is not None:
                 tail.replay()
@@ -150,23 +158,21 @@ class Case:
             t1 = time.perf_counter()
         return (t1 - t0) / steps
 
-    def kernel_times(self, reps=8):
+    def kernel_times(self, reps=4):
         """Average per-launch durations (s) of stage 1 (main kernel) and stage 2
         (reduce), each from HIP events on the launch stream around replays of a
-        graph that holds nsets launches of that stage alone."""
+        graph that holds graph_len() launches of that stage alone."""
         torch = self.torch
         out = []
+        glen = self.graph_len()
         for stage in (1, 2):
             if stage == 2 and self.plan.info["split_k"] <= 1:
                 out.append(0.0)
                 continue
-            g = torch.cuda.CUDAGraph()
+            g = self.capture(glen, stage=stage)
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(s):
-                with torch.cuda.graph(g, stream=s):
-                    for i in range(self.nsets):
-                        self.step(i, stage=stage)
                 g.replay()                       # untimed: graph upload
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -175,7 +181,7 @@ class Case:
                     g.replay()
                 e1.record(s)
             torch.cuda.synchronize()
-            out.append(e0.elapsed_time(e1) * 1e-3 / (reps * self.nsets))
+            out.append(e0.elapsed_time(e1) * 1e-3 / (reps * glen))
         return out[0], out[1]
 
     def row(self, sec_per_step, t_main, t_red):

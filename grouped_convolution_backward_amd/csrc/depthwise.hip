@@ -190,24 +190,26 @@ int launch_t(int ty, const Dw2Args& a, hipStream_t s) {
 // at their end). Each shared line then comes from HBM once and from L2 for
 // the second reader, instead of twice.
 //
-// A lane owns 4 adjacent channels (one 8-byte load per pixel); eight waves
-// per workgroup, one workgroup per CU, two waves per SIMD.
-#ifndef DW3_AHEAD
-#define DW3_AHEAD 2
-#endif
-constexpr int kAhead = DW3_AHEAD;   // steps loaded ahead of the one computed (1 or 2)
-constexpr int kW3 = 2;              // 32-bit words (channel pairs) per lane
-constexpr int kDw3Waves = 8;        // waves per workgroup
+// A lane owns kDw3Channels adjacent channels (one 8- or 16-byte load per
+// pixel); kDw3Waves waves per workgroup, one workgroup per CU.
+constexpr int kAhead = 2;           // steps loaded ahead of the one computed (1 or 2)
+constexpr int kW3 = kDw3Words;      // 32-bit words (channel pairs) per lane
 
+typedef typename VecT<2 * kW3>::T PxVec;   // one lane's channels of one pixel
+template <int W = kW3>
+__device__ __forceinline__ typename VecT<2 * W>::T load_px(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (W == 4) return buf_load16(r, off);
+    else return buf_load8(r, off);
+}
 struct StepBuf {
-    u32x2 d[kUnit];      // dY of the step's 4 positions
-    u32x2 xn[kWin];      // the input row that enters the ring at this step
+    PxVec d[kUnit];      // dY of the step's 4 positions
+    PxVec xn[kWin];      // the input row that enters the ring at this step
 };
 struct RowPairs {
     uint32_t lo[kW3][kWin - 1], hi[kW3][kWin - 1];   // [word][column j]: (col j, col j+1)
 };
 
-__device__ __forceinline__ void pack_row(const u32x2* raw, RowPairs& r) {
+__device__ __forceinline__ void pack_row(const PxVec* raw, RowPairs& r) {
 #pragma unroll
     for (int w = 0; w < kW3; ++w)
 #pragma unroll
@@ -230,7 +232,10 @@ __global__ __launch_bounds__(64 * kDw3Waves, 1) void dw3_kernel(const Dw3Args a)
     const int cl = a.cl;
     const int cv = lane % cl;
     const int L = xcd_logical_id(blockIdx.x, a.total_wg);
-    const int cb = L / a.S, z = L - (L / a.S) * a.S;
+    // channel blocks are the fastest index: the blocks of one split read the
+    // two (or more) halves of the same pixels at the same time on one XCD, so
+    // each pixel's full channel run is fetched from HBM together
+    const int cb = L % a.cblocks, z = L / a.cblocks;
     const int c0 = (cb * cl + cv) * CH;
     const __amdgpu_buffer_rsrc_t x_rs = buf_rsrc(a.x, a.x_bytes);
     const __amdgpu_buffer_rsrc_t dy_rs = buf_rsrc(a.dy, a.dy_bytes);
@@ -247,13 +252,13 @@ __global__ __launch_bounds__(64 * kDw3Waves, 1) void dw3_kernel(const Dw3Args a)
         for (int k = 0; k < CH; ++k) acc[t][k] = 0.f;
 
     // input row hi of image n, columns wo0 - pw .. wo0 - pw + 5 (zeros outside)
-    auto x_row = [&](int n, int hi, int wo0, u32x2* r) {
+    auto x_row = [&](int n, int hi, int wo0, PxVec* r) {
         const bool rok = (unsigned)hi < (unsigned)a.Hi;
         const int pix = (n * a.Hi + hi) * a.Wi + wo0 - a.pw;
 #pragma unroll
         for (int j = 0; j < kWin; ++j) {
             const bool ok = rok && (unsigned)(wo0 - a.pw + j) < (unsigned)a.Wi;
-            r[j] = buf_load8(x_rs, ok ? (uint32_t)(((pix + j) * a.C + c0) * 2) : kBufOob);
+            r[j] = load_px(x_rs, ok ? (uint32_t)(((pix + j) * a.C + c0) * 2) : kBufOob);
         }
     };
 
@@ -268,8 +273,8 @@ __global__ __launch_bounds__(64 * kDw3Waves, 1) void dw3_kernel(const Dw3Args a)
 #pragma unroll
             for (int p = 0; p < kUnit; ++p) {
                 const bool ok = valid && wo0 + p < a.Wo;
-                b.d[p] = buf_load8(dy_rs, ok ? (uint32_t)((((n * a.Ho + ho) * a.Wo + wo0 + p) * a.C + c0) * 2)
-                                             : kBufOob);
+                b.d[p] = load_px(dy_rs, ok ? (uint32_t)((((n * a.Ho + ho) * a.Wo + wo0 + p) * a.C + c0) * 2)
+                                           : kBufOob);
             }
             x_row(n, valid ? ho - a.ph + (UP ? 0 : 2) : -1, wo0, b.xn);
         };
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(64 * kDw3Waves, 1) void dw3_kernel(const Dw3Args a)
         {
             // the two rows of the first window that do not enter at step 0
             const int ho = ho_of(0);
-            u32x2 raw[kWin];
+            PxVec raw[kWin];
             x_row(n, ho - a.ph + 1, wo0, raw);
             pack_row(raw, ring[ring_slot<UP>(1, 0)]);
             x_row(n, ho - a.ph + (UP ? 2 : 0), wo0, raw);
@@ -345,15 +350,18 @@ __global__ __launch_bounds__(64 * kDw3Waves, 1) void dw3_kernel(const Dw3Args a)
             for (int k = 0; k < CH; ++k) part[wave][lane][t * CH + k] = acc[t][k];
     }
     __syncthreads();
+    // thread o writes element o of the block's contiguous dW run (channel
+    // c = o / 9, tap t = o % 9), so the stores are coalesced
     const int64_t zoff = a.out_mode == OUT_WORKSPACE ? (int64_t)z * a.slice_elems : 0;
+    const int64_t base = zoff + (int64_t)cb * cl * CH * T;
     for (int o = tid; o < cl * T * CH; o += 64 * kDw3Waves) {
-        const int v = o / (T * CH), w = o - v * (T * CH);
-        const int t = w / CH, k = w - t * CH;
+        const int cloc = o / T, t = o - cloc * T;
+        const int v = cloc / CH, k = cloc - v * CH;
+        const int w = t * CH + k;
         float sum = part[0][v][w];
 #pragma unroll
         for (int q = 1; q < kDw3Waves; ++q) sum += part[q][v][w];
-        const int c = (cb * cl + v) * CH + k;
-        store_out(a.out, a.out_mode, zoff + (int64_t)c * T + t, sum);
+        store_out(a.out, a.out_mode, base + o, sum);
     }
 }
 

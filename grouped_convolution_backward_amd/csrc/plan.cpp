@@ -307,21 +307,22 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
             b.C = (int32_t)p.C; b.Hi = (int32_t)g.Hi; b.Wi = (int32_t)g.Wi; b.Ho = (int32_t)g.Ho; b.Wo = (int32_t)g.Wo;
             b.ph = (int32_t)g.ph; b.pw = (int32_t)g.pw;
             b.nseg = (int32_t)ceil_div(g.Wo, 4);
-            // lanes of 4 channels; one 8-wave workgroup per CU, a split is one
-            // workgroup's share of a channel block
-            int cl3 = 64;
-            while ((p.C / 4) % cl3) cl3 >>= 1;
+            // lanes of kDw3Channels channels; one workgroup per CU, a split is
+            // one workgroup's share of a channel block
+            if (p.C % kDw3Channels) return fail(msg, U, "strip depthwise kernel needs C to be a multiple of %d", kDw3Channels);
+            int cl3 = kDw3MaxLanes;
+            while ((p.C / kDw3Channels) % cl3) cl3 >>= 1;
             b.cl = cl3;
-            b.cblocks = (int32_t)(p.C / 4 / cl3);
+            b.cblocks = (int32_t)(p.C / kDw3Channels / cl3);
             const int64_t nsub = 64 / cl3;
             const int64_t strips = p.N * b.nseg;
             int64_t S3 = o.split_k ? o.split_k : std::max<int64_t>(1, (int64_t)dev.num_cus / b.cblocks);
             // never more workgroups than strips need at one chunk per strip
-            S3 = std::max<int64_t>(1, std::min<int64_t>(S3, ceil_div(std::max<int64_t>(strips * g.Ho, 1), 8 * nsub)));
+            S3 = std::max<int64_t>(1, std::min<int64_t>(S3, ceil_div(std::max<int64_t>(strips * g.Ho, 1), kDw3Waves * nsub)));
             if (S3 > 65535 || S3 * b.cblocks > kMax31) return fail(msg, U, "split_k too large");
             // chunks per strip: fewest passes x rows per chunk, counting the
             // two ring rows loaded at each item's start as one more row
-            const int64_t workers = 8 * nsub * S3;
+            const int64_t workers = kDw3Waves * nsub * S3;
             int64_t best_nch = 1, best_cost = INT64_MAX;
             for (int64_t nch = 1; nch <= std::max<int64_t>(1, g.Ho); ++nch) {
                 const int64_t passes = ceil_div(std::max<int64_t>(strips * nch, 1), workers);
@@ -339,7 +340,7 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
             b.dy_bytes = (uint32_t)(2 * ndy);
             out.dw3_ty = 3;
             S = S3;
-            cl = cl3 / 2;   // reported in 8-channel units like the other forms
+            cl = cl3 * kDw3Channels / 8;   // reported in 8-channel units like the other forms
         } else if (form == 2) {
             // windowed kernel: units of 4 output positions; splits hold whole units
             Dw2Args& b = out.dw2;

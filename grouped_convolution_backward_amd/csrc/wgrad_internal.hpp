@@ -152,6 +152,15 @@ struct Dw2Args {
 // work items are row chunks of 4-wide column strips; a worker walks a chunk
 // keeping the filter's input rows in registers, so each output row loads one
 // new input row and one dY row.
+// strip kernel shape: 32-bit words (channel pairs) each lane loads per pixel,
+// waves per workgroup, and the most lanes that share one pixel's channels
+// (fewer lanes per pixel let one wave cover several strips)
+// (measured on the 512-channel 56x56 depthwise shape: 8-byte lanes with two
+// waves per SIMD beat 16-byte lanes with one, and three waves per SIMD with a
+// shallower prefetch)
+constexpr int kDw3Words = 2, kDw3Waves = 8, kDw3MaxLanes = 64;
+constexpr int kDw3Channels = 2 * kDw3Words;   // channels per lane
+
 struct Dw3Args {
     const uint16_t* x;
     const uint16_t* dy;
@@ -160,7 +169,7 @@ struct Dw3Args {
     int32_t nseg;          // 4-wide strips per image row
     int32_t nch;           // row chunks per strip
     int32_t items;         // N * nseg * nch items per channel block (strip-major)
-    int32_t cl, cblocks;   // channel lanes (4 channels each) and channel blocks
+    int32_t cl, cblocks;   // lanes per pixel (kDw3Channels channels each) and channel blocks
     int32_t S, total_wg, out_mode, slice_elems;   // S: workgroups (slices) per channel block
     uint32_t x_bytes, dy_bytes;
 };
