@@ -20,20 +20,18 @@
 //   so the tile needs no per-tap copy and nothing is transposed on store.
 // * Tiles go from HBM to LDS with buffer loads that write LDS directly (16
 //   bytes per lane, lane-major), so no registers stage them and no LDS store
-//   instructions compete with the fragment reads. Each slab stream owns nb
-//   slab buffers and loads slabs nb - 1 ahead of the one it computes;
-//   a slab's loads are spread over the k-steps of the current slab, so the
-//   load path (64 B per clock per CU) never backs up into the MFMA issue.
+//   instructions compete with the fragment reads.
 //   16-byte chunks are XOR-swizzled by bit 1 of the row (64-channel rows), so
 //   the four rows a 16-lane group reads land on all banks; the loads apply
 //   the swizzle by choosing which source chunk each lane fetches.
 // * The workgroup runs four slab streams; stream p takes every fourth slab of
-//   the workgroup's split into its own nb LDS buffers and holds the whole
-//   workgroup tile in registers. With 64-channel blocks a stream is two waves
-//   on one SIMD, each holding half of the channels and issuing half of the
-//   loads, with one workgroup barrier per slab; two waves per SIMD let one
-//   issue MFMAs while the other waits to issue loads. With 32-channel blocks a
-//   stream is one wave and the slab loop has no barrier.
+//   the workgroup's split into its own nb LDS buffers. A stream's MFMA waves
+//   (two, each holding 32 of 64 channels, or one for 32-channel blocks) hold
+//   the workgroup tile in registers and never touch vector memory: one
+//   producer wave per stream issues all of its loads and waits for them, so
+//   a stalled load issue never holds up an MFMA. One workgroup barrier per
+//   slab hands slab i + 1 to the MFMA waves and slab i's buffer back to the
+//   producer, which refills it nb - 1 slabs ahead.
 // * At the end the four wave tiles are added in LDS in a fixed order and the
 //   workgroup writes one partial (S > 1: fp32 workspace slice) or dW itself.
 //   With merged groups only diagonal group pairs are stored (PR 12359).
@@ -75,9 +73,9 @@ __device__ __forceinline__ void vm_wait_slabs(int later) {
 }
 
 template <int MB, int CB, int XF, int NKS, int NXR, int XWP, int STRIDE, int NB, int WPS, bool F16>
-__global__ __launch_bounds__(256 * WPS, 1) void rowslab_kernel(const RowSlabArgs a) {
+__global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSlabArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-    constexpr int NT = 256 * WPS;                  // threads per workgroup
+    constexpr int NT = 256 * WPS;                  // consumer threads (the MFMA waves)
     constexpr int FM = MB / 32, FC = CB / 32;
     constexpr int FCW = FC / WPS, FNW = XF * FCW;  // 32-channel blocks and B fragments per wave
     constexpr int KS = 16 * NKS;                   // positions per slab (padded)
@@ -99,8 +97,9 @@ __global__ __launch_bounds__(256 * WPS, 1) void rowslab_kernel(const RowSlabArgs
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool producer = wave >= 4 * WPS;         // one load-issuing wave per stream
     const int pair = wave & 3;                     // slab stream of this wave
-    const int half = wave >> 2;                    // its part of the channel block (WPS = 2)
+    const int half = producer ? 0 : wave >> 2;     // its part of the channel block (WPS = 2)
     uint16_t* wbuf = smem + pair * NB * BUF;
 
     const int L = xcd_logical_id(blockIdx.x, a.total_wg);
@@ -165,7 +164,6 @@ __global__ __launch_bounds__(256 * WPS, 1) void rowslab_kernel(const RowSlabArgs
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             if (l < l0 || l >= l1) continue;           // l0, l1 are compile-time at every call
-            if (WPS > 1 && l % WPS != half) continue;
             if (l < NA) {
                 const bool ok = a_ok && l * RA + ja < gq.kvalid;
                 dma_load16(dy_desc, lds_addr(sA + l * RA * MB), ok ? gq.abase + l * a_step : kBufOob);
@@ -184,14 +182,32 @@ __global__ __launch_bounds__(256 * WPS, 1) void rowslab_kernel(const RowSlabArgs
     // loads of one slab this wave issues (compile-time per half)
     constexpr int NLW0 = (NL + WPS - 1) / WPS, NLW1 = NL / WPS;
 
-    // this stream's slabs: s_begin + pair + 4*i, i < cnt; the first NB - 1 are
-    // issued now, slab i + NB - 1 during the k-steps of slab i. Every wave of
-    // the workgroup runs cnt_max iterations (the barrier count must agree).
+    // this stream's slabs: s_begin + pair + 4*i, i < cnt. Every wave of the
+    // workgroup passes the same cnt_max + 1 barriers.
     const int cnt = s_begin + pair < s_end ? (s_end - s_begin - pair + 3) / 4 : 0;
     const int cnt_max = s_end > s_begin ? (s_end - s_begin + 3) / 4 : 0;
+    if (producer) {
+        // issue slabs 0 .. NB-2, then before barrier i+1 issue slab i+NB-1
+        // (into the buffer slab i-1 left) and wait for slab i+1
 #pragma unroll
-    for (int i = 0; i < NB - 1; ++i)
-        if (i < cnt) issue_part(slab_geo(s_begin + pair + 4 * i), i, 0, NL);
+        for (int i = 0; i < NB - 1; ++i)
+            if (i < cnt) issue_part(slab_geo(s_begin + pair + 4 * i), i, 0, NL);
+        if (cnt > 0) vm_wait_slabs<NB - 2, NL>(min(cnt - 1, NB - 2));
+        __builtin_amdgcn_s_barrier();
+        for (int i = 0; i < cnt_max; ++i) {
+            if (i + NB - 1 < cnt) issue_part(slab_geo(s_begin + pair + 4 * (i + NB - 1)), (i + NB - 1) % NB, 0, NL);
+            if (i + 1 < cnt) vm_wait_slabs<NB - 2, NL>(min(cnt - 2 - i, NB - 2));
+            __builtin_amdgcn_s_barrier();
+        }
+        // the epilogue's barriers
+        lds_barrier();
+#pragma unroll
+        for (int x = 0; x < XF; ++x) {
+            lds_barrier();
+            lds_barrier();
+        }
+        return;
+    }
 
     // lane geometry of the transposed reads: rows frow (+4), columns fcol..fcol+3
     const int g16 = lane >> 4;
@@ -253,44 +269,31 @@ __global__ __launch_bounds__(256 * WPS, 1) void rowslab_kernel(const RowSlabArgs
                 fb[x * FCW + fc] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
     };
-    // wait until slab i's loads from this wave have landed: at most the loads
-    // of the slabs issued after it (up to NB - 2 of them) stay outstanding
-    auto wait_slab = [&](int i) {
-        const int later = i < cnt ? min(cnt - 1 - i, NB - 2) : 0;
-        if (WPS == 1 || half == 0) vm_wait_slabs<NB - 2, NLW0>(later);
-        else vm_wait_slabs<NB - 2, NLW1>(later);
-    };
+    __builtin_amdgcn_s_barrier();
     for (int i = 0; i < cnt_max; ++i) {
-        wait_slab(i);
-        // the other half of the slab is the partner wave's; the barrier also
-        // tells every wave that the buffer refilled below is no longer read
-        if (WPS > 1) __builtin_amdgcn_s_barrier();
-        if (i >= cnt) continue;
-        const bool pre = i + NB - 1 < cnt;
-        const SlabGeo gn = slab_geo(s_begin + pair + 4 * (pre ? i + NB - 1 : i));
-        const int bn = (i + NB - 1) % NB;
-        const uint16_t* sA = wbuf + (i % NB) * BUF;
-        read_frags(sA, 0, af[0], bf[0]);
+        if (i < cnt) {
+            const uint16_t* sA = wbuf + (i % NB) * BUF;
+            read_frags(sA, 0, af[0], bf[0]);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int cur = ks & 1;
-            __builtin_amdgcn_sched_barrier(0);
-            if (pre) issue_part(gn, bn, ks * NL / NKS, (ks + 1) * NL / NKS);
-            if (ks + 1 < NKS) read_frags(sA, ks + 1, af[cur ^ 1], bf[cur ^ 1]);
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int cur = ks & 1;
+                __builtin_amdgcn_sched_barrier(0);
+                if (ks + 1 < NKS) read_frags(sA, ks + 1, af[cur ^ 1], bf[cur ^ 1]);
 #pragma unroll
-            for (int j = 0; j < FNW; ++j)
+                for (int j = 0; j < FNW; ++j)
 #pragma unroll
-                for (int i2 = 0; i2 < FM; ++i2) mfma_step32<F16>(af[cur][i2], bf[cur][j], acc[i2][j]);
+                    for (int i2 = 0; i2 < FM; ++i2) mfma_step32<F16>(af[cur][i2], bf[cur][j], acc[i2][j]);
 #pragma unroll
-            for (int m = 0; m < FM * FNW; ++m) {
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+                for (int m = 0; m < FM * FNW; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
-        // the loads that later refill this buffer must follow these reads
-        asm volatile("" ::: "memory");
+        // slab i is consumed (its buffer may be refilled) and slab i + 1 has landed
+        lds_barrier();
     }
 
     // ---- sum the four stream tiles in LDS (fixed order) and store, one tap at a time
@@ -317,7 +320,8 @@ __global__ __launch_bounds__(256 * WPS, 1) void rowslab_kernel(const RowSlabArgs
         constexpr int RPI = NT / TPR;               // rows per pass
         static_assert(MB % RPI == 0, "reduction passes");
         const int col = (threadIdx.x % TPR) * 4;
-        const int cg = c0 + col;                    // channel inside the merged run
+        const int cg = c0 + col;
+        static_assert(NT % TPR == 0, "consumer threads cover whole rows");
         const int gj = cg / a.cpg;                  // group of this column
         const int glo = gj * a.kpg, ghi = glo + a.kpg;   // its rows (the diagonal block)
         const int64_t e0 = (int64_t)mbase * a.row_len + (y * XF + x) * a.cpg + (cg - gj * a.cpg);
@@ -343,7 +347,7 @@ int launch_rs(const Plan& plan, const RowSlabArgs& a, hipStream_t s) {
     auto k = rowslab_kernel<r.mb, r.cb, r.xf, r.nks, r.nxr, r.xwp, r.stride, r.nb, wps, F16>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes);
     if (e != hipSuccess) return (int)e;
-    hipLaunchKernelGGL(k, dim3(a.total_wg), dim3(256 * wps), plan.lds_bytes, s, a);
+    hipLaunchKernelGGL(k, dim3(a.total_wg), dim3(256 * (wps + 1)), plan.lds_bytes, s, a);
     return (int)hipGetLastError();
 }
 

@@ -78,7 +78,8 @@ constexpr RsInstance kRsInstances[] = {
     {32, 32, 5, 8, 1, 144, 1, 2},   // 128-position row segments, width-5 filter
 };
 constexpr int kNumRsInstances = sizeof(kRsInstances) / sizeof(kRsInstances[0]);
-// waves per slab stream: two for 64-channel blocks (each holds 32 channels)
+// MFMA waves per slab stream: two for 64-channel blocks (each holds 32
+// channels); every stream also has one load-issuing producer wave
 constexpr int rs_waves_per_slab(const RsInstance& r) { return r.cb == 64 ? 2 : 1; }
 inline int rs_buffer_elems(const RsInstance& r) { return 16 * r.nks * r.mb + r.nxr * r.xwp * r.cb; }
 inline int rs_lds_bytes(const RsInstance& r) {
