@@ -42,9 +42,9 @@ class _Problem(ctypes.Structure):
         ("ndim", ctypes.c_int64),
         ("G", ctypes.c_int64), ("N", ctypes.c_int64),
         ("C", ctypes.c_int64), ("K", ctypes.c_int64),
-        ("in_len", ctypes.c_int64 * 2), ("filt_len", ctypes.c_int64 * 2),
-        ("stride", ctypes.c_int64 * 2), ("dilation", ctypes.c_int64 * 2),
-        ("pad_lo", ctypes.c_int64 * 2), ("pad_hi", ctypes.c_int64 * 2),
+        ("in_len", ctypes.c_int64 * 3), ("filt_len", ctypes.c_int64 * 3),
+        ("stride", ctypes.c_int64 * 3), ("dilation", ctypes.c_int64 * 3),
+        ("pad_lo", ctypes.c_int64 * 3), ("pad_hi", ctypes.c_int64 * 3),
         ("in_dtype", ctypes.c_int64),
     ]
 
@@ -78,7 +78,7 @@ def _load():
                                              f64p, f64p, ctypes.c_int]
         lib.oracle_wgrad_sampled.restype = ctypes.c_int
         lib.oracle_out_len.argtypes = [P, ctypes.POINTER(ctypes.c_int64),
-                                       ctypes.POINTER(ctypes.c_int64)]
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
         lib.oracle_out_len.restype = ctypes.c_int
         lib.oracle_widen.argtypes = [u16p, ctypes.c_int64, ctypes.c_int64, f64p]
         lib.oracle_widen.restype = ctypes.c_int
@@ -87,36 +87,32 @@ def _load():
     return _lib
 
 
-def _pair(v, ndim):
-    v = tuple(v)
-    if ndim == 1:
-        return (v[0], 0)
-    return (v[0], v[1])
-
-
 def _to_struct(prob: dict) -> _Problem:
     nd = int(prob["ndim"])
     p = _Problem()
     p.ndim = nd
     p.G, p.N, p.C, p.K = (int(prob[k]) for k in ("G", "N", "C", "K"))
     for name in ("in_len", "filt_len", "stride", "dilation", "pad_lo", "pad_hi"):
-        a, b = _pair(prob[name], nd)
+        v = tuple(prob[name])[:nd]
         arr = getattr(p, name)
-        arr[0], arr[1] = a, b
+        for i in range(3):
+            arr[i] = int(v[i]) if i < len(v) else 0
     p.in_dtype = DTYPE_CODE[prob["in_dtype"]]
     return p
 
 
 def out_len(prob: dict) -> tuple:
-    """Output spatial lengths, (Ho, Wo) for 2D or (Wo,) for 1D."""
-    ho, wo = ctypes.c_int64(), ctypes.c_int64()
-    if _load().oracle_out_len(ctypes.byref(_to_struct(prob)), ctypes.byref(ho), ctypes.byref(wo)):
+    """Output spatial lengths, outermost first: (Do, Ho, Wo) for 3D, (Ho, Wo)
+    for 2D, (Wo,) for 1D."""
+    od, oh, ow = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    if _load().oracle_out_len(ctypes.byref(_to_struct(prob)), ctypes.byref(od), ctypes.byref(oh),
+                              ctypes.byref(ow)):
         raise ValueError("invalid problem")
-    return (ho.value, wo.value) if int(prob["ndim"]) == 2 else (wo.value,)
+    return (od.value, oh.value, ow.value)[3 - int(prob["ndim"]):]
 
 
 def dw_shape(prob: dict) -> tuple:
-    """GKYXC shape as (K_total, *filter, C/G)."""
+    """GK[Z]YXC shape as (K_total, *filter, C/G)."""
     return (int(prob["K"]), *tuple(prob["filt_len"])[: int(prob["ndim"])],
             int(prob["C"]) // int(prob["G"]))
 
@@ -132,7 +128,7 @@ def _check_sizes(prob, x_bits, dy_bits):
 
 
 def wgrad(prob: dict, x_bits: np.ndarray, dy_bits: np.ndarray, nthreads: int = 0):
-    """Full dW and sum|dY*X| in fp64, each shaped (K, [Y,] X, C/G)."""
+    """Full dW and sum|dY*X| in fp64, each shaped (K, [Z,] [Y,] X, C/G)."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16).reshape(-1)
     dy_bits = np.ascontiguousarray(dy_bits, dtype=np.uint16).reshape(-1)
     _check_sizes(prob, x_bits, dy_bits)
@@ -146,7 +142,7 @@ def wgrad(prob: dict, x_bits: np.ndarray, dy_bits: np.ndarray, nthreads: int = 0
 
 def wgrad_sampled(prob: dict, x_bits: np.ndarray, dy_bits: np.ndarray,
                   flat_idx: np.ndarray, nthreads: int = 0):
-    """dW and sum|dY*X| at the given flat GKYXC indices only."""
+    """dW and sum|dY*X| at the given flat GK[Z]YXC indices only."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16).reshape(-1)
     dy_bits = np.ascontiguousarray(dy_bits, dtype=np.uint16).reshape(-1)
     _check_sizes(prob, x_bits, dy_bits)

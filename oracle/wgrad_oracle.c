@@ -6,21 +6,24 @@
  * helper with the HIP path in grouped_convolution_backward_amd/.
  *
  * What it computes (Composable Kernel doxygen page, "grouped_convolution_
- * backward_weight_kernel.hpp": the NWGC/GKXC/NWGK and NHWGC/GKYXC/NHWGK
- * argument constructors fix the three layouts and the per-group base offsets
- * group_stride_a = K, group_stride_b = C, group_stride_c = K*C*prod(filter);
- * the operator() comment "conv_bwd_weight = Out * In = Weight" fixes the
- * operands). With per-group channel counts cpg = C/G and kpg = K/G:
+ * backward_weight_kernel.hpp": the NWGC/GKXC/NWGK, NHWGC/GKYXC/NHWGK and
+ * NDHWGC/GKZYXC/NDHWGK argument constructors fix the layouts and the
+ * per-group base offsets group_stride_a = K, group_stride_b = C,
+ * group_stride_c = K*C*prod(filter); the operator() comment
+ * "conv_bwd_weight = Out * In = Weight" fixes the operands). With per-group
+ * channel counts cpg = C/G and kpg = K/G:
  *
- *   dW[g,k,y,x,c] = sum_{n<N} sum_{ho<Ho} sum_{wo<Wo}
- *                     [0 <= hi < Hi and 0 <= wi < Wi]
- *                     * dY[n,ho,wo,g,k] * X[n,hi,wi,g,c],
- *   hi = ho*s_h - pl_h + y*d_h,   wi = wo*s_w - pl_w + x*d_w.
+ *   dW[g,k,z,y,x,c] = sum_{n<N} sum_{do<Do} sum_{ho<Ho} sum_{wo<Wo}
+ *                       [0 <= di < Di and 0 <= hi < Hi and 0 <= wi < Wi]
+ *                       * dY[n,do,ho,wo,g,k] * X[n,di,hi,wi,g,c],
+ *   di = do*s_d - pl_d + z*d_d,  hi = ho*s_h - pl_h + y*d_h,
+ *   wi = wo*s_w - pl_w + x*d_w.
  *
- * 1D drops the h axis (Hi = Ho = Y = 1). Every bf16/fp16 input is widened to
- * fp64 (exact) and each output element is one fp64 sum in ascending
- * (n, ho, wo) order, so the result is deterministic. Alongside dW it returns
- * sum |dY*X| per element, which scales the acceptance bound.
+ * 2D drops the d axis (Di = Do = Z = 1) and 1D the h axis as well. Every
+ * bf16/fp16 input is widened to fp64 (exact) and each output element is one
+ * fp64 sum in ascending (n, do, ho, wo) order, so the result is
+ * deterministic. Alongside dW it returns sum |dY*X| per element, which
+ * scales the acceptance bound.
  *
  * Readings where the pages are silent (each listed in the design doc):
  *   - C and K are totals; cpg = C/G and kpg = K/G must be whole.
@@ -38,14 +41,15 @@
 /* Mirrors the fields of the problem; every field is int64 so that the
  * Python side can fill it with a flat array. */
 typedef struct {
-    int64_t ndim;          /* 1 or 2 */
+    int64_t ndim;          /* 1, 2 or 3 */
     int64_t G, N, C, K;    /* C, K are totals over all groups */
-    int64_t in_len[2];     /* (Hi, Wi); 1D uses in_len[0] only */
-    int64_t filt_len[2];   /* (Y, X) */
-    int64_t stride[2];
-    int64_t dilation[2];
-    int64_t pad_lo[2];
-    int64_t pad_hi[2];
+    int64_t in_len[3];     /* the first ndim of (Di, Hi, Wi), outermost first:
+                              3D (Di, Hi, Wi), 2D (Hi, Wi), 1D (Wi) */
+    int64_t filt_len[3];   /* likewise (Z, Y, X) */
+    int64_t stride[3];
+    int64_t dilation[3];
+    int64_t pad_lo[3];
+    int64_t pad_hi[3];
     int64_t in_dtype;      /* 0 = bf16, 1 = fp16 */
 } oracle_problem;
 
@@ -76,49 +80,42 @@ static double widen_fp16(uint16_t h)
     return sign ? -v : v;
 }
 
-/* Spatial extents in (h, w) order; a 1D problem is a 2D one with h of size 1. */
+/* Spatial extents along (d, h, w); missing leading axes have size 1. */
 typedef struct {
-    int64_t Hi, Wi, Y, X, sh, sw, dh, dw, ph, pw, Ho, Wo;
+    int64_t in[3], f[3], s[3], dl[3], pl[3], out[3];
 } geom;
 
 static int make_geom(const oracle_problem* p, geom* g)
 {
-    int64_t hi_pad = 0, wi_pad = 0;
-    if (p->ndim == 2) {
-        g->Hi = p->in_len[0];   g->Wi = p->in_len[1];
-        g->Y = p->filt_len[0];  g->X = p->filt_len[1];
-        g->sh = p->stride[0];   g->sw = p->stride[1];
-        g->dh = p->dilation[0]; g->dw = p->dilation[1];
-        g->ph = p->pad_lo[0];   g->pw = p->pad_lo[1];
-        hi_pad = p->pad_lo[0] + p->pad_hi[0];
-        wi_pad = p->pad_lo[1] + p->pad_hi[1];
-    } else if (p->ndim == 1) {
-        g->Hi = 1; g->Y = 1; g->sh = 1; g->dh = 1; g->ph = 0;
-        g->Wi = p->in_len[0];  g->X = p->filt_len[0];
-        g->sw = p->stride[0];  g->dw = p->dilation[0];
-        g->pw = p->pad_lo[0];
-        wi_pad = p->pad_lo[0] + p->pad_hi[0];
-    } else {
-        return -1;
-    }
-    if (g->sh < 1 || g->sw < 1 || g->dh < 1 || g->dw < 1) return -1;
-    {
-        int64_t nh = g->Hi + hi_pad - g->dh * (g->Y - 1) - 1;
-        int64_t nw = g->Wi + wi_pad - g->dw * (g->X - 1) - 1;
-        if (nh < 0 || nw < 0) return -1;
-        g->Ho = nh / g->sh + 1;
-        g->Wo = nw / g->sw + 1;
+    if (p->ndim < 1 || p->ndim > 3) return -1;
+    const int64_t lead = 3 - p->ndim;   /* axes the problem does not have */
+    for (int a = 0; a < 3; ++a) {
+        if (a < lead) {
+            g->in[a] = 1; g->f[a] = 1; g->s[a] = 1; g->dl[a] = 1; g->pl[a] = 0;
+            g->out[a] = 1;
+            continue;
+        }
+        const int i = a - (int)lead;
+        g->in[a] = p->in_len[i];  g->f[a] = p->filt_len[i];
+        g->s[a] = p->stride[i];   g->dl[a] = p->dilation[i];
+        g->pl[a] = p->pad_lo[i];
+        if (g->s[a] < 1 || g->dl[a] < 1) return -1;
+        int64_t span = g->in[a] + p->pad_lo[i] + p->pad_hi[i] - g->dl[a] * (g->f[a] - 1) - 1;
+        if (span < 0) return -1;
+        g->out[a] = span / g->s[a] + 1;
     }
     return 0;
 }
 
-/* Output spatial size; returns -1 for an invalid problem. */
-int oracle_out_len(const oracle_problem* p, int64_t* ho, int64_t* wo)
+/* Output spatial sizes along (d, h, w) (1 for axes the problem does not
+ * have); returns -1 for an invalid problem. */
+int oracle_out_len(const oracle_problem* p, int64_t* od, int64_t* oh, int64_t* ow)
 {
     geom g;
     if (make_geom(p, &g)) return -1;
-    *ho = g.Ho;
-    *wo = g.Wo;
+    *od = g.out[0];
+    *oh = g.out[1];
+    *ow = g.out[2];
     return 0;
 }
 
@@ -131,26 +128,33 @@ static double* widen_all(const uint16_t* src, int64_t n, int64_t dtype)
     return d;
 }
 
-/* One output element: the sum over (n, ho, wo) in ascending order. */
+/* One output element: the sum over (n, do, ho, wo) in ascending order;
+ * (z, y, x) is the filter tap. */
 static void one_element(const geom* g, int64_t N, int64_t C, int64_t K,
                         const double* xs, const double* dys,
                         int64_t gi, int64_t cpg, int64_t kt,
-                        int64_t y, int64_t x, int64_t c,
+                        int64_t z, int64_t y, int64_t x, int64_t c,
                         double* acc_out, double* abs_out)
 {
+    const int64_t Di = g->in[0], Hi = g->in[1], Wi = g->in[2];
+    const int64_t Do = g->out[0], Ho = g->out[1], Wo = g->out[2];
     double acc = 0.0, ab = 0.0;
     for (int64_t n = 0; n < N; ++n)
-        for (int64_t ho = 0; ho < g->Ho; ++ho) {
-            int64_t hi = ho * g->sh - g->ph + y * g->dh;
-            if (hi < 0 || hi >= g->Hi) continue;
-            for (int64_t wo = 0; wo < g->Wo; ++wo) {
-                int64_t wi = wo * g->sw - g->pw + x * g->dw;
-                if (wi < 0 || wi >= g->Wi) continue;
-                double dy = dys[((n * g->Ho + ho) * g->Wo + wo) * K + kt];
-                double xv = xs[((n * g->Hi + hi) * g->Wi + wi) * C + gi * cpg + c];
-                double prod = dy * xv;
-                acc += prod;
-                ab += fabs(prod);
+        for (int64_t od = 0; od < Do; ++od) {
+            int64_t di = od * g->s[0] - g->pl[0] + z * g->dl[0];
+            if (di < 0 || di >= Di) continue;
+            for (int64_t ho = 0; ho < Ho; ++ho) {
+                int64_t hi = ho * g->s[1] - g->pl[1] + y * g->dl[1];
+                if (hi < 0 || hi >= Hi) continue;
+                for (int64_t wo = 0; wo < Wo; ++wo) {
+                    int64_t wi = wo * g->s[2] - g->pl[2] + x * g->dl[2];
+                    if (wi < 0 || wi >= Wi) continue;
+                    double dy = dys[(((n * Do + od) * Ho + ho) * Wo + wo) * K + kt];
+                    double xv = xs[(((n * Di + di) * Hi + hi) * Wi + wi) * C + gi * cpg + c];
+                    double prod = dy * xv;
+                    acc += prod;
+                    ab += fabs(prod);
+                }
             }
         }
     *acc_out = acc;
@@ -158,8 +162,8 @@ static void one_element(const geom* g, int64_t N, int64_t C, int64_t K,
 }
 
 /*
- * Full dW in GKYXC order (k_tot = g*kpg + k outer, then y, x, c), fp64.
- * x: N*Hi*Wi*C 16-bit patterns; dy: N*Ho*Wo*K 16-bit patterns.
+ * Full dW in GK[Z]YXC order (k_tot = g*kpg + k outer, then z, y, x, c), fp64.
+ * x: N*Di*Hi*Wi*C 16-bit patterns; dy: N*Do*Ho*Wo*K 16-bit patterns.
  * nthreads <= 0 uses the OpenMP default. Returns 0, or -1 on a bad problem
  * or allocation failure.
  */
@@ -170,25 +174,27 @@ int oracle_wgrad(const oracle_problem* p, const uint16_t* x, const uint16_t* dy,
     if (make_geom(p, &g)) return -1;
     if (p->G < 1 || p->C % p->G || p->K % p->G || p->N < 0) return -1;
     const int64_t cpg = p->C / p->G, kpg = p->K / p->G;
-    const int64_t nx = p->N * g.Hi * g.Wi * p->C;
-    const int64_t ndy = p->N * g.Ho * g.Wo * p->K;
+    const int64_t nx = p->N * g.in[0] * g.in[1] * g.in[2] * p->C;
+    const int64_t ndy = p->N * g.out[0] * g.out[1] * g.out[2] * p->K;
     double* xs = widen_all(x, nx, p->in_dtype);
     double* dys = widen_all(dy, ndy, p->in_dtype);
     if (!xs || !dys) { free(xs); free(dys); return -1; }
-    const int64_t per_k = g.Y * g.X * cpg;
+    const int64_t Z = g.f[0], Y = g.f[1], X = g.f[2];
+    const int64_t per_k = Z * Y * X * cpg;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1)
 #endif
     for (int64_t kt = 0; kt < p->K; ++kt) {
         const int64_t gi = kt / kpg;
-        for (int64_t y = 0; y < g.Y; ++y)
-            for (int64_t xx = 0; xx < g.X; ++xx)
-                for (int64_t c = 0; c < cpg; ++c) {
-                    int64_t e = kt * per_k + (y * g.X + xx) * cpg + c;
-                    one_element(&g, p->N, p->C, p->K, xs, dys, gi, cpg, kt, y, xx, c,
-                                &dw[e], &absdw[e]);
-                }
+        for (int64_t z = 0; z < Z; ++z)
+            for (int64_t y = 0; y < Y; ++y)
+                for (int64_t xx = 0; xx < X; ++xx)
+                    for (int64_t c = 0; c < cpg; ++c) {
+                        int64_t e = kt * per_k + ((z * Y + y) * X + xx) * cpg + c;
+                        one_element(&g, p->N, p->C, p->K, xs, dys, gi, cpg, kt, z, y, xx, c,
+                                    &dw[e], &absdw[e]);
+                    }
     }
     free(xs);
     free(dys);
@@ -196,7 +202,7 @@ int oracle_wgrad(const oracle_problem* p, const uint16_t* x, const uint16_t* dy,
 }
 
 /*
- * The same sums for a list of flat GKYXC indices only (for full-size
+ * The same sums for a list of flat GK[Z]YXC indices only (for full-size
  * problems, where the whole dW would take too long on the CPU).
  */
 int oracle_wgrad_sampled(const oracle_problem* p, const uint16_t* x, const uint16_t* dy,
@@ -207,9 +213,10 @@ int oracle_wgrad_sampled(const oracle_problem* p, const uint16_t* x, const uint1
     if (make_geom(p, &g)) return -1;
     if (p->G < 1 || p->C % p->G || p->K % p->G || p->N < 0) return -1;
     const int64_t cpg = p->C / p->G, kpg = p->K / p->G;
-    const int64_t nx = p->N * g.Hi * g.Wi * p->C;
-    const int64_t ndy = p->N * g.Ho * g.Wo * p->K;
-    const int64_t total = p->K * g.Y * g.X * cpg;
+    const int64_t nx = p->N * g.in[0] * g.in[1] * g.in[2] * p->C;
+    const int64_t ndy = p->N * g.out[0] * g.out[1] * g.out[2] * p->K;
+    const int64_t Z = g.f[0], Y = g.f[1], X = g.f[2];
+    const int64_t total = p->K * Z * Y * X * cpg;
     for (int64_t i = 0; i < nidx; ++i)
         if (idx[i] < 0 || idx[i] >= total) return -1;
     double* xs = widen_all(x, nx, p->in_dtype);
@@ -223,10 +230,11 @@ int oracle_wgrad_sampled(const oracle_problem* p, const uint16_t* x, const uint1
         int64_t e = idx[i];
         int64_t c = e % cpg;
         int64_t t = e / cpg;
-        int64_t xx = t % g.X;  t /= g.X;
-        int64_t y = t % g.Y;
-        int64_t kt = t / g.Y;
-        one_element(&g, p->N, p->C, p->K, xs, dys, kt / kpg, cpg, kt, y, xx, c,
+        int64_t xx = t % X;  t /= X;
+        int64_t y = t % Y;   t /= Y;
+        int64_t z = t % Z;
+        int64_t kt = t / Z;
+        one_element(&g, p->N, p->C, p->K, xs, dys, kt / kpg, cpg, kt, z, y, xx, c,
                     &dw[i], &absdw[i]);
     }
     free(xs);
