@@ -37,9 +37,9 @@ class wgrad_problem(ctypes.Structure):
         ("ndim", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("G", ctypes.c_int64), ("N", ctypes.c_int64), ("C", ctypes.c_int64), ("K", ctypes.c_int64),
-        ("in_len", ctypes.c_int64 * 2), ("filt_len", ctypes.c_int64 * 2),
-        ("stride", ctypes.c_int64 * 2), ("dilation", ctypes.c_int64 * 2),
-        ("pad_lo", ctypes.c_int64 * 2), ("pad_hi", ctypes.c_int64 * 2),
+        ("in_len", ctypes.c_int64 * 3), ("filt_len", ctypes.c_int64 * 3),
+        ("stride", ctypes.c_int64 * 3), ("dilation", ctypes.c_int64 * 3),
+        ("pad_lo", ctypes.c_int64 * 3), ("pad_hi", ctypes.c_int64 * 3),
     ]
 
 
@@ -50,7 +50,7 @@ class wgrad_overrides(ctypes.Structure):
 
 class wgrad_plan_info(ctypes.Structure):
     _fields_ = [
-        ("out_len", ctypes.c_int64 * 2), ("gemm_m", ctypes.c_int64), ("gemm_n", ctypes.c_int64),
+        ("out_len", ctypes.c_int64 * 3), ("gemm_m", ctypes.c_int64), ("gemm_n", ctypes.c_int64),
         ("gemm_k", ctypes.c_int64), ("variant", ctypes.c_int32), ("tile", ctypes.c_int32),
         ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
         ("split_k", ctypes.c_int32), ("group_merge", ctypes.c_int32), ("vector_width", ctypes.c_int32),
@@ -122,8 +122,8 @@ def make_problem(p: dict) -> wgrad_problem:
     for name in ("in_len", "filt_len", "stride", "dilation", "pad_lo", "pad_hi"):
         v = tuple(p[name])[:nd]
         arr = getattr(s, name)
-        for i in range(2):
-            arr[i] = int(v[i]) if i < nd else 0
+        for i in range(3):
+            arr[i] = int(v[i]) if i < len(v) else 0
     return s
 
 

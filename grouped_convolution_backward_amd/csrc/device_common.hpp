@@ -114,12 +114,17 @@ __device__ __forceinline__ u32x4 buf_desc(const void* base, uint32_t bytes) {
     d[3] = 0x00020000u;
     return d;
 }
+// M0 is listed as clobbered; the compiler reserves it and uses it for nothing
+// else in these kernels (checked in their assembly), hence the pragma.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_load16(const u32x4& desc, uint32_t lds_byte, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(lds_byte), "v"(voff), "s"(desc)
                  : "memory", "m0");
 }
+#pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
 }

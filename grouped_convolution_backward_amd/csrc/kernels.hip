@@ -75,8 +75,9 @@ __global__ __launch_bounds__(256) void mfma_kernel(const MfmaArgs a) {
     const bool b_col_ok = jb < a.Nm;
     const int tap = jb / a.gcpg;
     const int cc = jb - tap * a.gcpg;
-    const int ty = tap / a.Xf, tx = tap - (tap / a.Xf) * a.Xf;
-    const int hoff = ty * a.dh - a.ph, woff = tx * a.dw - a.pw;
+    const int tzy = tap / a.Xf, tx = tap - tzy * a.Xf;   // tap = (z*Y + y)*X + x
+    const int tz = tzy / a.Yf, ty = tzy - tz * a.Yf;
+    const int doff = tz * a.dd - a.pd, hoff = ty * a.dh - a.ph, woff = tx * a.dw - a.pw;
     const uint16_t* b_src = xp + cc;
 
     VT ra[A_PASSES], rb[B_PASSES];
@@ -97,14 +98,18 @@ __global__ __launch_bounds__(256) void mfma_kernel(const MfmaArgs a) {
             const int r = r0 + row;
             VT v = 0;
             if ((B_PASSES * B_RPP <= BK || row < BK) && b_col_ok && r < r_end) {
+                // r = ((n*Do + do)*Ho + ho)*Wo + wo
                 const uint32_t q1 = magic_div((uint32_t)r, a.mWo);
                 const int wo = r - (int)q1 * a.Wo;
-                const uint32_t n = magic_div(q1, a.mHo);
-                const int ho = (int)q1 - (int)n * a.Ho;
+                const uint32_t q2 = magic_div(q1, a.mHo);
+                const int ho = (int)q1 - (int)q2 * a.Ho;
+                const uint32_t n = magic_div(q2, a.mDo);
+                const int od = (int)q2 - (int)n * a.Do;
+                const int di = od * a.sd + doff;
                 const int hi = ho * a.sh + hoff;
                 const int wi = wo * a.sw + woff;
-                if ((unsigned)hi < (unsigned)a.Hi && (unsigned)wi < (unsigned)a.Wi)
-                    v = *reinterpret_cast<const VT*>(b_src + (((int)n * a.Hi + hi) * a.Wi + wi) * a.Ctot);
+                if ((unsigned)di < (unsigned)a.Di && (unsigned)hi < (unsigned)a.Hi && (unsigned)wi < (unsigned)a.Wi)
+                    v = *reinterpret_cast<const VT*>(b_src + ((((int)n * a.Di + di) * a.Hi + hi) * a.Wi + wi) * a.Ctot);
             }
             rb[p] = v;
         }

@@ -37,8 +37,11 @@ bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 int64_t gcd64(int64_t a, int64_t b) { while (b) { int64_t t = a % b; a = b; b = t; } return a; }
 
 // Geometry with 1D folded into 2D (h axis of size 1).
+// Spatial geometry along (d, h, w); axes a problem does not have are 1 long
+// (stride and dilation 1, no pad).
 struct Geo {
     int64_t Hi, Wi, Y, X, sh, sw, dh, dw, ph, pw, Ho, Wo;
+    int64_t Di, Z, sd, dd, pd, Do;
 };
 
 // Split-K degree in the manner of a groups-aware occupancy target: enough
@@ -88,7 +91,7 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
     if (g.X == 3 && gcpg % 64 == 0 && gkpg > 32) { mb = 64; cb = 64; }
     else if (gcpg % 32 == 0) { mb = 32; cb = 32; }
     else return no("row-slab needs a merged channel run that is a multiple of 32");
-    const int64_t NHo = p.N * g.Ho;
+    const int64_t NHo = p.N * g.Do * g.Ho;       // output rows (n, do, ho)
     auto xw_of = [&](int64_t sw) { return (sw - 1) * g.sw + (g.X - 1) * g.dw + 1; };
     // slab: PR output rows x SW output columns whose positions are one
     // contiguous run of r (whole output rows, or a segment of one row). Pick
@@ -120,7 +123,7 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
     const int64_t nseg = ceil_div(g.Wo, SW);
     const int64_t nslabs = ceil_div(NHo, PR) * nseg;
     const int64_t mblocks = ceil_div(gkpg, mb), cblocks = gcpg / cb, gblocks = p.G / Gm;
-    const int64_t tiles = gblocks * mblocks * cblocks * g.Y;
+    const int64_t tiles = gblocks * mblocks * cblocks * g.Z * g.Y;   // one filter row (z, y) per tile
     int64_t spw, S;
     if (nslabs == 0) {
         spw = 0; S = 1;
@@ -137,24 +140,27 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
         S = ceil_div(nslabs, spw);
     }
     if (tiles * S > kMax31 || S > 65535) return no("row-slab grid too large");
-    const int64_t ndw = p.K * g.Y * g.X * cpg;
+    const int64_t ndw = p.K * g.Z * g.Y * g.X * cpg;
     RowSlabArgs& a = out.rs;
     a = RowSlabArgs{};
     a.Ktot = (int32_t)p.K; a.Ctot = (int32_t)p.C; a.kpg = (int32_t)kpg; a.cpg = (int32_t)cpg;
     a.gkpg = (int32_t)gkpg; a.gcpg = (int32_t)gcpg;
-    a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo; a.Y = (int32_t)g.Y;
+    a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo;
+    a.Y = (int32_t)(g.Z * g.Y); a.Yf = (int32_t)g.Y;
+    a.Di = (int32_t)g.Di; a.Do = (int32_t)g.Do; a.sd = (int32_t)g.sd; a.dd = (int32_t)g.dd; a.pd = (int32_t)g.pd;
     a.sh = (int32_t)g.sh; a.sw = (int32_t)g.sw; a.dh = (int32_t)g.dh; a.dw = (int32_t)g.dw;
     a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
-    a.NHo = (int32_t)NHo; a.Mm = (int32_t)gkpg; a.row_len = (int32_t)(g.Y * g.X * cpg);
+    a.NHo = (int32_t)NHo; a.Mm = (int32_t)gkpg; a.row_len = (int32_t)(g.Z * g.Y * g.X * cpg);
     a.mblocks = (int32_t)mblocks; a.cblocks = (int32_t)cblocks; a.tiles = (int32_t)tiles;
     a.PR = (int32_t)PR; a.SW = (int32_t)SW; a.XW = (int32_t)XW;
     a.nseg = (int32_t)nseg; a.nslabs = (int32_t)nslabs; a.spw = (int32_t)spw;
     a.S = (int32_t)S; a.total_wg = (int32_t)(tiles * S);
     a.out_mode = S == 1 ? out_final : OUT_WORKSPACE;
     a.slice_elems = (int32_t)ndw;
-    a.x_bytes = (uint32_t)(2 * p.N * g.Hi * g.Wi * p.C);
+    a.x_bytes = (uint32_t)(2 * p.N * g.Di * g.Hi * g.Wi * p.C);
     a.dy_bytes = (uint32_t)(2 * NHo * g.Wo * p.K);
     a.mSW = make_magic((uint32_t)SW); a.mXW = make_magic((uint32_t)XW); a.mHo = make_magic((uint32_t)g.Ho);
+    a.mDo = make_magic((uint32_t)g.Do);
     out.rs_inst = inst;
     out.lds_bytes = rs_lds_bytes(ri);
     wgrad_plan_info& info = out.info;
@@ -173,7 +179,7 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
 int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceModel& dev, Plan& out,
                std::string* msg) {
     const int E = WGRAD_ERR_INVALID_ARG, U = WGRAD_ERR_UNSUPPORTED;
-    if (p.ndim != 1 && p.ndim != 2) return fail(msg, E, "ndim must be 1 or 2 (got %d)", p.ndim);
+    if (p.ndim < 1 || p.ndim > 3) return fail(msg, E, "ndim must be 1, 2 or 3 (got %d)", p.ndim);
     if (p.reserved != 0) return fail(msg, E, "reserved field must be 0");
     if (p.in_dtype != WGRAD_BF16 && p.in_dtype != WGRAD_FP16)
         return fail(msg, E, "in_dtype must be BF16 or FP16");
@@ -189,30 +195,40 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
             return fail(msg, E, "lengths, strides and dilations must be >= 1 (axis %d)", i);
         if (p.pad_lo[i] < 0 || p.pad_hi[i] < 0) return fail(msg, E, "pads must be >= 0 (axis %d)", i);
     }
-    Geo g{};
-    if (p.ndim == 2) {
-        g = Geo{p.in_len[0], p.in_len[1], p.filt_len[0], p.filt_len[1], p.stride[0], p.stride[1],
-                p.dilation[0], p.dilation[1], p.pad_lo[0], p.pad_lo[1], 0, 0};
-        int64_t nh = p.in_len[0] + p.pad_lo[0] + p.pad_hi[0] - p.dilation[0] * (p.filt_len[0] - 1) - 1;
-        int64_t nw = p.in_len[1] + p.pad_lo[1] + p.pad_hi[1] - p.dilation[1] * (p.filt_len[1] - 1) - 1;
-        if (nh < 0 || nw < 0) return fail(msg, E, "empty output: the dilated filter exceeds the padded input");
-        g.Ho = nh / p.stride[0] + 1;
-        g.Wo = nw / p.stride[1] + 1;
-    } else {
-        g = Geo{1, p.in_len[0], 1, p.filt_len[0], 1, p.stride[0], 1, p.dilation[0], 0, p.pad_lo[0], 1, 0};
-        int64_t nw = p.in_len[0] + p.pad_lo[0] + p.pad_hi[0] - p.dilation[0] * (p.filt_len[0] - 1) - 1;
-        if (nw < 0) return fail(msg, E, "empty output: the dilated filter exceeds the padded input");
-        g.Wo = nw / p.stride[0] + 1;
+    // axes outermost first; the problem's ndim axes are the last ones of (d, h, w)
+    int64_t len[3], fl[3], st[3], dl[3], pl[3], ol[3];
+    const int lead = 3 - p.ndim;
+    for (int ax = 0; ax < 3; ++ax) {
+        if (ax < lead) {
+            len[ax] = fl[ax] = st[ax] = dl[ax] = 1;
+            pl[ax] = 0;
+            ol[ax] = 1;
+            continue;
+        }
+        const int i = ax - lead;
+        len[ax] = p.in_len[i]; fl[ax] = p.filt_len[i]; st[ax] = p.stride[i];
+        dl[ax] = p.dilation[i]; pl[ax] = p.pad_lo[i];
+        const int64_t span = p.in_len[i] + p.pad_lo[i] + p.pad_hi[i] - p.dilation[i] * (p.filt_len[i] - 1) - 1;
+        if (span < 0) return fail(msg, E, "empty output: the dilated filter exceeds the padded input");
+        ol[ax] = span / p.stride[i] + 1;
     }
+    Geo g{};
+    g.Di = len[0]; g.Hi = len[1]; g.Wi = len[2];
+    g.Z = fl[0];   g.Y = fl[1];   g.X = fl[2];
+    g.sd = st[0];  g.sh = st[1];  g.sw = st[2];
+    g.dd = dl[0];  g.dh = dl[1];  g.dw = dl[2];
+    g.pd = pl[0];  g.ph = pl[1];  g.pw = pl[2];
+    g.Do = ol[0];  g.Ho = ol[1];  g.Wo = ol[2];
     const int64_t cpg = p.C / p.G, kpg = p.K / p.G;
-    const int64_t R = p.N * g.Ho * g.Wo;
-    const int64_t nx = p.N * g.Hi * g.Wi * p.C;
+    const int64_t R = p.N * g.Do * g.Ho * g.Wo;
+    const int64_t nx = p.N * g.Di * g.Hi * g.Wi * p.C;
     const int64_t ndy = R * p.K;
-    const int64_t ndw = p.K * g.Y * g.X * cpg;
+    const int64_t ndw = p.K * g.Z * g.Y * g.X * cpg;
     if (nx > kMax31 || ndy > kMax31 || ndw > kMax31 || R > kMax31 || g.Hi > kMax31 || g.Wi > kMax31)
         return fail(msg, E, "tensor element offsets must fit in 31 bits");
     // index arithmetic on the padded input also stays in 31 bits
-    if ((g.Ho * g.sh + g.Y * g.dh) > kMax31 || (g.Wo * g.sw + g.X * g.dw) > kMax31)
+    if ((g.Do * g.sd + g.Z * g.dd) > kMax31 || (g.Ho * g.sh + g.Y * g.dh) > kMax31 ||
+        (g.Wo * g.sw + g.X * g.dw) > kMax31)
         return fail(msg, E, "spatial index range must fit in 31 bits");
 
     wgrad_overrides o{};
@@ -224,10 +240,12 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
     out.prob = p;
     out.in_f16 = p.in_dtype == WGRAD_FP16;
     wgrad_plan_info& info = out.info;
-    info.out_len[0] = p.ndim == 2 ? g.Ho : g.Wo;
-    info.out_len[1] = p.ndim == 2 ? g.Wo : 0;
+    {
+        const int64_t all[3] = {g.Do, g.Ho, g.Wo};
+        for (int i = 0; i < 3; ++i) info.out_len[i] = i < p.ndim ? all[3 - p.ndim + i] : 0;
+    }
     info.gemm_m = kpg;
-    info.gemm_n = cpg * g.Y * g.X;
+    info.gemm_n = cpg * g.Z * g.Y * g.X;
     info.gemm_k = R;
     info.num_cus = dev.num_cus;
     const int out_final = p.out_dtype == WGRAD_BF16 ? OUT_BF16 : p.out_dtype == WGRAD_FP16 ? OUT_FP16 : OUT_FP32;
@@ -235,7 +253,7 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
     const char* dname = out.in_f16 ? "fp16" : "bf16";
 
     // ---- kernel family
-    const bool dw_shape = cpg == 1 && kpg == 1 && p.C % 8 == 0;
+    const bool dw_shape = cpg == 1 && kpg == 1 && p.C % 8 == 0 && p.ndim <= 2;
     // windowed depthwise kernel: width-3 filter, w-stride and w-dilation 1, height 1, 3 or 5
     const bool dw2_ok = g.X == 3 && g.sw == 1 && g.dw == 1 && (g.Y == 1 || g.Y == 3 || g.Y == 5) &&
                         2 * nx < (int64_t{1} << 31) && 2 * ndy < (int64_t{1} << 31);
@@ -250,7 +268,7 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
         else variant = WGRAD_VARIANT_MFMA;
     }
     if (variant == WGRAD_VARIANT_DEPTHWISE && !(dw_shape && dw_filter))
-        return fail(msg, U, "depthwise variant needs C/G = K/G = 1, C %% 8 == 0 and a 3x3, 1x3 or 1x5 filter");
+        return fail(msg, U, "depthwise variant needs a 1D or 2D problem with C/G = K/G = 1, C %% 8 == 0 and a 3x3, 1x3 or 1x5 filter");
     out.variant = variant;
     info.variant = variant;
 
@@ -408,7 +426,7 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
             Gm = 1;
             while (Gm * 2 <= 8 && Gm * kpg < 16 && p.G % (Gm * 2) == 0) Gm *= 2;
         }
-        const int64_t Mm = Gm * kpg, Nm = Gm * cpg * g.Y * g.X;
+        const int64_t Mm = Gm * kpg, Nm = Gm * cpg * g.Z * g.Y * g.X;
         if (Mm > kMax31 || Nm > kMax31) return fail(msg, E, "merged GEMM too large");
         // ---- load vector width: a vector stays inside one channel run and
         // every run starts on a multiple of it
@@ -447,12 +465,13 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
         a.kpg = (int32_t)kpg; a.cpg = (int32_t)cpg; a.Gm = (int32_t)Gm;
         a.gkpg = (int32_t)(Gm * kpg); a.gcpg = (int32_t)(Gm * cpg);
         a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo;
-        a.Xf = (int32_t)g.X;
+        a.Xf = (int32_t)g.X; a.Yf = (int32_t)g.Y;
+        a.Di = (int32_t)g.Di; a.Do = (int32_t)g.Do; a.sd = (int32_t)g.sd; a.dd = (int32_t)g.dd; a.pd = (int32_t)g.pd;
         a.sh = (int32_t)g.sh; a.sw = (int32_t)g.sw; a.dh = (int32_t)g.dh; a.dw = (int32_t)g.dw;
         a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
         a.R = (int32_t)R;
         a.Mm = (int32_t)Mm; a.Nm = (int32_t)Nm;
-        a.row_len = (int32_t)(g.Y * g.X * cpg);
+        a.row_len = (int32_t)(g.Z * g.Y * g.X * cpg);
         a.tiles_m = (int32_t)tiles_m; a.tiles_n = (int32_t)tiles_n; a.gblocks = (int32_t)gblocks;
         a.S = (int32_t)S;
         a.kslice = (int32_t)kslice;
@@ -461,6 +480,7 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
         a.slice_elems = (int32_t)ndw;
         a.mWo = make_magic((uint32_t)g.Wo);
         a.mHo = make_magic((uint32_t)g.Ho);
+        a.mDo = make_magic((uint32_t)g.Do);
         info.tile = tile_id;
         info.tile_m = t->bm; info.tile_n = t->bn; info.tile_k = t->bk;
         info.split_k = (int32_t)S;

@@ -4,9 +4,10 @@
 // gathered per filter tap, reduction over r = (n*Ho + ho)*Wo + wo), tiled so
 // that X is staged once per output row instead of once per tap:
 //
-// * A workgroup owns one filter row y of one (group block, M block, C block)
-//   tile and every filter column x of that row: its output tile is
-//   MB x (X*CB), and for one output row it needs exactly one input row.
+// * A workgroup owns one filter row (z, y) of one (group block, M block,
+//   C block) tile and every filter column x of that row: its output tile is
+//   MB x (X*CB), and for one output row (n, do, ho) it needs exactly one
+//   input row (n, di, hi). 2D is the depth-1 case, 1D also height 1.
 // * The reduction runs over slabs of PR output rows x SW output columns. A
 //   slab's dY rows are staged K-outer ([position][channel]) and its input
 //   rows as a pixel tile ([row][pixel][channel]); tap x of position k is a
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
     const int L = xcd_logical_id(blockIdx.x, a.total_wg);
     int t = L % a.tiles;
     const int z = L / a.tiles;
-    const int y = t % a.Y;
+    const int y = t % a.Y;                         // filter row (z, y) = z*Yf + y
     t /= a.Y;
     const int cbk = t % a.cblocks;
     t /= a.cblocks;
@@ -114,7 +115,8 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
     const int m0 = mbk * MB, c0 = cbk * CB;
     const int s_begin = z * a.spw;
     const int s_end = min(a.nslabs, s_begin + a.spw);
-    const int hoff = y * a.dh - a.ph;
+    const int fz = y / a.Yf, fy = y - fz * a.Yf;
+    const int doff = fz * a.dd - a.pd, hoff = fy * a.dh - a.ph;
     const int kreal = a.PR * a.SW;
     const u32x4 dy_desc = buf_desc(a.dy, a.dy_bytes);
     const u32x4 x_desc = buf_desc(a.x, a.x_bytes);
@@ -150,11 +152,14 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
         gq.wbase = wo0 * a.sw - a.pw;
 #pragma unroll
         for (int q = 0; q < NXR; ++q) {
+            // output row = (n*Do + do)*Ho + ho
             const int row = row0 + q;
-            const int n = (int)magic_div((uint32_t)row, a.mHo);
-            const int hi = (row - n * a.Ho) * a.sh + hoff;
-            gq.rowok[q] = q < a.PR && row < a.NHo && (unsigned)hi < (unsigned)a.Hi;
-            gq.pixrow[q] = (n * a.Hi + hi) * a.Wi;
+            const int b = (int)magic_div((uint32_t)row, a.mHo);
+            const int n = (int)magic_div((uint32_t)b, a.mDo);
+            const int di = (b - n * a.Do) * a.sd + doff;
+            const int hi = (row - b * a.Ho) * a.sh + hoff;
+            gq.rowok[q] = q < a.PR && row < a.NHo && (unsigned)di < (unsigned)a.Di && (unsigned)hi < (unsigned)a.Hi;
+            gq.pixrow[q] = ((n * a.Di + di) * a.Hi + hi) * a.Wi;
         }
         return gq;
     };

@@ -45,17 +45,19 @@ struct MfmaArgs {
     int32_t kpg, cpg, Gm;   // per-group K, C and merge degree
     int32_t gkpg, gcpg;     // Gm*kpg (merged M), Gm*cpg (merged channel run)
     int32_t Hi, Wi, Ho, Wo; // 1D: Hi = Ho = 1
-    int32_t Xf;             // filter width
+    int32_t Xf, Yf;         // filter width and height
+    int32_t Di, Do;         // input and output depth (2D, 1D: 1)
+    int32_t sd, dd, pd;     // depth stride, dilation, left pad
     int32_t sh, sw, dh, dw, ph, pw;
     int32_t R;              // N*Ho*Wo
-    int32_t Mm, Nm;         // merged GEMM sizes: Gm*kpg, Y*X*Gm*cpg
-    int32_t row_len;        // Y*X*cpg: length of one dW row
+    int32_t Mm, Nm;         // merged GEMM sizes: Gm*kpg, Z*Y*X*Gm*cpg
+    int32_t row_len;        // Z*Y*X*cpg: length of one dW row
     int32_t tiles_m, tiles_n, gblocks, S;
     int32_t kslice;         // reduction elements per split, a multiple of the tile K
     int32_t total_wg;
     int32_t out_mode;
-    int32_t slice_elems;    // K*Y*X*cpg: elements of one workspace slice
-    MagicU32 mWo, mHo;
+    int32_t slice_elems;    // K*Z*Y*X*cpg: elements of one workspace slice
+    MagicU32 mWo, mHo, mDo;
 };
 
 // Row-slab kernel instances, shared by the planner and the kernels. Each
@@ -96,11 +98,13 @@ struct RowSlabArgs {
     const uint16_t* dy;
     void* out;
     int32_t Ktot, Ctot, kpg, cpg, gkpg, gcpg;
-    int32_t Hi, Wi, Ho, Wo, Y;
+    int32_t Hi, Wi, Ho, Wo;
+    int32_t Y, Yf;          // filter rows (z, y) = Z*Y, and the filter height Y
+    int32_t Di, Do, sd, dd, pd;   // depth (2D, 1D: Di = Do = 1, pd = 0)
     int32_t sh, sw, dh, dw, ph, pw;
-    int32_t NHo;            // N*Ho output rows
+    int32_t NHo;            // N*Do*Ho output rows
     int32_t Mm;             // merged M = Gm*kpg
-    int32_t row_len;        // Y*X*cpg
+    int32_t row_len;        // Z*Y*X*cpg
     int32_t mblocks, cblocks, tiles;
     int32_t PR, SW;         // slab rows and columns (PR*SW <= the instance's positions)
     int32_t XW;             // X tile columns: (SW-1)*sw + (X-1)*dw + 1
@@ -108,7 +112,7 @@ struct RowSlabArgs {
     int32_t spw;            // slabs per workgroup (one split)
     int32_t S, total_wg, out_mode, slice_elems;
     uint32_t x_bytes, dy_bytes;   // buffer sizes for the bounds-checked loads
-    MagicU32 mSW, mXW, mHo;
+    MagicU32 mSW, mXW, mHo, mDo;
 };
 
 // Depthwise (C/G = K/G = 1) channel-vector kernel.

@@ -3,24 +3,27 @@
  * backward-weight library (libwgrad.so).
  *
  * Operation (Composable Kernel page "grouped_convolution_backward_weight_
- * kernel.hpp": the 1D NWGC/GKXC/NWGK and 2D NHWGC/GKYXC/NHWGK argument
- * constructors, their group strides, and operator()'s "Out * In = Weight"):
+ * kernel.hpp": the 1D NWGC/GKXC/NWGK, 2D NHWGC/GKYXC/NHWGK and 3D
+ * NDHWGC/GKZYXC/NDHWGK argument constructors, their group strides, and
+ * operator()'s "Out * In = Weight"), written here for 3D:
  *
- *   dW[g,k,y,x,c] = sum_{n,ho,wo} [0<=hi<Hi, 0<=wi<Wi] dY[n,ho,wo,g,k] * X[n,hi,wi,g,c]
- *   hi = ho*stride_h - pad_lo_h + y*dilation_h
- *   wi = wo*stride_w - pad_lo_w + x*dilation_w
+ *   dW[g,k,z,y,x,c] = sum_{n,do,ho,wo} [0<=di<Di, 0<=hi<Hi, 0<=wi<Wi]
+ *                       dY[n,do,ho,wo,g,k] * X[n,di,hi,wi,g,c]
+ *   di = do*stride_d - pad_lo_d + z*dilation_d   (likewise hi with y, wi with x)
  *
- * computed as a batched-over-groups implicit GEMM with M = K/G,
- * N = (C/G)*Y*X and a reduction of length N*Ho*Wo. The pad_hi values only
- * size the output: Ho = floor((Hi + pad_lo + pad_hi - dilation*(Y-1) - 1)/stride) + 1.
+ * 2D drops the d axis (Di = Do = Z = 1), 1D the h axis as well. Computed as
+ * a batched-over-groups implicit GEMM with M = K/G, N = (C/G)*Z*Y*X and a
+ * reduction of length N*Do*Ho*Wo. The pad_hi values only size the output:
+ * Ho = floor((Hi + pad_lo + pad_hi - dilation*(Y-1) - 1)/stride) + 1, and so on.
  *
  * Layouts (all dense, row-major, innermost index last):
- *   X  : [N][Hi][Wi][C]        (1D: [N][Wi][C])      C = G * (C/G), group-major
- *   dY : [N][Ho][Wo][K]        (1D: [N][Wo][K])      K = G * (K/G), group-major
- *   dW : [K][Y][X][C/G]        (1D: [K][X][C/G])     i.e. GKYXC
+ *   X  : [N][Di][Hi][Wi][C]    (2D: [N][Hi][Wi][C], 1D: [N][Wi][C])   C = G*(C/G), group-major
+ *   dY : [N][Do][Ho][Wo][K]    (2D: [N][Ho][Wo][K], 1D: [N][Wo][K])   K = G*(K/G), group-major
+ *   dW : [K][Z][Y][X][C/G]     (2D: [K][Y][X][C/G], 1D: [K][X][C/G])  i.e. GKZYXC
  * X and dY share one 16-bit element type (bf16 or fp16); dW is that type or
- * fp32. A torch tensor [N,C,H,W] in channels_last memory order is exactly X;
- * a grouped conv weight [K, C/G, Y, X] in channels_last is exactly dW.
+ * fp32. A torch tensor [N,C,H,W] (or [N,C,D,H,W]) in channels_last memory
+ * order is exactly X; a grouped conv weight [K, C/G, (Z,) Y, X] in
+ * channels_last is exactly dW.
  *
  * Ownership: the caller owns every device buffer and the stream. The library
  * allocates no device memory; a plan owns only host memory.
@@ -53,21 +56,22 @@ typedef enum {
 } wgrad_status;
 
 /* The problem. C and K are totals over all G groups and must be multiples
- * of G. ndim 1 uses index [0] of each array (the w axis); ndim 2 uses
- * [0] = h and [1] = w. Lengths, strides and dilations are >= 1, pads >= 0.
- * N may be 0 (dW is then all zeros). */
+ * of G. Each array holds the problem's ndim axes outermost first: ndim 3
+ * uses [0] = d, [1] = h, [2] = w; ndim 2 uses [0] = h, [1] = w; ndim 1 uses
+ * [0] = w; unused entries are ignored. Lengths, strides and dilations are
+ * >= 1, pads >= 0. N may be 0 (dW is then all zeros). */
 typedef struct {
-    int32_t ndim;       /* 1 or 2 */
+    int32_t ndim;       /* 1, 2 or 3 */
     int32_t in_dtype;   /* wgrad_dtype of X and dY: BF16 or FP16 */
     int32_t out_dtype;  /* wgrad_dtype of dW: in_dtype or FP32 */
     int32_t reserved;   /* must be 0 */
     int64_t G, N, C, K;
-    int64_t in_len[2];
-    int64_t filt_len[2];
-    int64_t stride[2];
-    int64_t dilation[2];
-    int64_t pad_lo[2];
-    int64_t pad_hi[2];
+    int64_t in_len[3];
+    int64_t filt_len[3];
+    int64_t stride[3];
+    int64_t dilation[3];
+    int64_t pad_lo[3];
+    int64_t pad_hi[3];
 } wgrad_problem;
 
 /* Kernel families a plan can use. */
@@ -94,10 +98,10 @@ typedef struct {
 
 /* What a plan decided, for logging and tests. */
 typedef struct {
-    int64_t out_len[2];      /* Ho, Wo (1D: out_len[0] = Wo) */
+    int64_t out_len[3];      /* output lengths, ordered like in_len: (Do, Ho, Wo), (Ho, Wo) or (Wo) */
     int64_t gemm_m;          /* K/G */
-    int64_t gemm_n;          /* (C/G)*Y*X */
-    int64_t gemm_k;          /* N*Ho*Wo */
+    int64_t gemm_n;          /* (C/G)*Z*Y*X */
+    int64_t gemm_k;          /* N*Do*Ho*Wo */
     int32_t variant;         /* wgrad_variant actually used */
     int32_t tile;            /* MFMA tile id, depthwise kernel form (1 generic, 2 windowed, 3 strip), or 0 */
     int32_t tile_m, tile_n, tile_k;
@@ -120,7 +124,7 @@ typedef struct wgrad_plan_s wgrad_plan_t;
  * without touching the HIP runtime, for host-side tests.
  * Returns WGRAD_ERR_INVALID_ARG for: C or K not a multiple of G, a
  * non-positive length/stride/dilation, a negative pad, an empty output
- * (Ho or Wo < 1), ndim not 1 or 2, an unsupported dtype pair, or sizes whose
+ * (an output length < 1), ndim not 1, 2 or 3, an unsupported dtype pair, or sizes whose
  * element offsets do not fit in 31 bits. WGRAD_ERR_UNSUPPORTED for an
  * override the kernels cannot honour (e.g. Gm not a power of two dividing G).
  * On success *out owns host memory; free it with wgrad_plan_destroy.

@@ -390,3 +390,49 @@ def test_depthwise_forms_agree_bitwise(form):
     assert p.info["tile"] == form
     dw64, _ = oracle_ref(cfg, xb, dyb)
     check_exact(cfg, bits.reshape(-1), dw64)
+
+
+# 3D (NDHWGC / NDHWGK / GKZYXC): dense, strided fp16, merged groups,
+# depthwise (merged MFMA), depth dilation with one-sided pads and fp32
+# output, and a depth-1 filter with depth stride 3
+THREE_D_CASES = [
+    dict(G=1, N=2, C=64, K=64, in_len=(5, 9, 10), filt_len=(3, 3, 3), stride=(1, 1, 1), dilation=(1, 1, 1),
+         pad_lo=(1, 1, 1), pad_hi=(1, 1, 1), in_dtype="bf16", out_dtype="bf16"),
+    dict(G=1, N=1, C=64, K=96, in_len=(7, 11, 12), filt_len=(3, 3, 3), stride=(2, 2, 2), dilation=(1, 1, 1),
+         pad_lo=(1, 1, 1), pad_hi=(1, 1, 1), in_dtype="fp16", out_dtype="fp16"),
+    dict(G=4, N=2, C=32, K=32, in_len=(4, 8, 8), filt_len=(3, 3, 3), stride=(1, 1, 1), dilation=(1, 1, 1),
+         pad_lo=(1, 1, 1), pad_hi=(1, 1, 1), in_dtype="bf16", out_dtype="bf16"),
+    dict(G=64, N=2, C=64, K=64, in_len=(4, 7, 7), filt_len=(3, 3, 3), stride=(1, 1, 1), dilation=(1, 1, 1),
+         pad_lo=(1, 1, 1), pad_hi=(1, 1, 1), in_dtype="bf16", out_dtype="bf16"),
+    dict(G=2, N=1, C=64, K=64, in_len=(6, 6, 9), filt_len=(2, 3, 3), stride=(1, 1, 1), dilation=(2, 1, 1),
+         pad_lo=(1, 0, 1), pad_hi=(0, 1, 1), in_dtype="bf16", out_dtype="fp32"),
+    dict(G=1, N=1, C=64, K=64, in_len=(7, 8, 8), filt_len=(1, 3, 3), stride=(3, 1, 1), dilation=(1, 1, 1),
+         pad_lo=(0, 1, 1), pad_hi=(0, 1, 1), in_dtype="bf16", out_dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(THREE_D_CASES)))
+@pytest.mark.parametrize("variant", ["auto", "mfma", "rowslab"])
+def test_3d(i, variant):
+    cfg = dict(THREE_D_CASES[i], ndim=3, name=f"3d{i}")
+    cfg["out_len"] = oracle.out_len(cfg)
+    ov = {}
+    if variant == "mfma":
+        ov["variant"] = gcb.VARIANT_MFMA
+    elif variant == "rowslab":
+        ov["variant"] = gcb.VARIANT_ROWSLAB
+        try:
+            gcb.Plan(cfg, **ov)
+        except gcb.WgradError as e:
+            assert e.code == gcb.ERR_UNSUPPORTED
+            pytest.skip("row-slab kernel does not take this shape")
+    for dist, seed in (("int", 800 + i), ("uniform", 850 + i)):
+        xb = workloads.draw(workloads.x_shape(cfg), cfg["in_dtype"], dist, seed)
+        dyb = workloads.draw(workloads.dy_shape(cfg), cfg["in_dtype"], dist, seed + 1)
+        vals, bits, p = run_gpu(cfg, xb, dyb, **ov)
+        assert p.dw_shape() == oracle.dw_shape(cfg)
+        dw64, ab64 = oracle_ref(cfg, xb, dyb)
+        if dist == "int":
+            check_exact(cfg, bits.reshape(-1), dw64)
+        else:
+            check_tol(cfg, vals.reshape(-1), dw64, ab64)

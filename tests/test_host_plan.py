@@ -237,3 +237,73 @@ def test_run_rejects_null_plan_and_pointers_without_gpu():
     assert lib.wgrad_run(p2.handle, 16, 16, 16, None, 0, None) == gcb.ERR_INVALID_ARG
     assert lib.wgrad_run(p2.handle, 16, 16, 16, 16, p2.workspace_bytes - 1, None) == gcb.ERR_INVALID_ARG
     assert "smaller" in gcb.wgrad_last_error()
+
+
+def test_abi_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors of wgrad_problem, wgrad_overrides and
+    wgrad_plan_info have the sizes and field offsets a C compiler gives the
+    header's structs."""
+    import ctypes
+    fields = {
+        "wgrad_problem": gcb.wgrad_problem,
+        "wgrad_overrides": gcb.wgrad_overrides,
+        "wgrad_plan_info": gcb.wgrad_plan_info,
+    }
+    lines = ["#include <cstdio>", "#include <cstddef>", '#include "wgrad.h"', "int main() {"]
+    for sname, cls in fields.items():
+        lines.append(f'    printf("{sname} size %zu\\n", sizeof({sname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'    printf("{sname} {fname} %zu\\n", offsetof({sname}, {fname}));')
+    lines += ["    return 0;", "}"]
+    src = tmp_path / "layout.cpp"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["g++", "-std=c++17", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line:
+            parts = line.split()
+            got[tuple(parts[:-1])] = int(parts[-1])
+    for sname, cls in fields.items():
+        assert got[(sname, "size")] == ctypes.sizeof(cls), sname
+        for fname, _ in cls._fields_:
+            assert got[(sname, fname)] == getattr(cls, fname).offset, (sname, fname)
+
+
+def prob3(G, N, C, K, in_len, filt, stride=(1, 1, 1), pad=(0, 0, 0), dil=(1, 1, 1), dtype="bf16"):
+    return {"ndim": 3, "G": G, "N": N, "C": C, "K": K, "in_len": in_len, "filt_len": filt,
+            "stride": stride, "dilation": dil, "pad_lo": pad, "pad_hi": pad,
+            "in_dtype": dtype, "out_dtype": dtype}
+
+
+def test_3d_plans_sizes_and_kernels():
+    import oracle
+    cfg = prob3(1, 2, 64, 64, (6, 10, 12), (3, 3, 3), pad=(1, 1, 1))
+    p = plan(cfg)
+    ol = oracle.out_len(cfg)
+    assert p.info["out_len"] == ol
+    assert p.info["gemm_k"] == 2 * ol[0] * ol[1] * ol[2]
+    assert p.info["gemm_n"] == 64 * 27 and p.info["gemm_m"] == 64
+    assert p.info["variant"] == gcb.VARIANT_ROWSLAB
+    # one row-slab tile per filter row (z, y): the grid is a multiple of 9
+    assert p.info["grid_main"] % 9 == 0
+    S = p.info["split_k"]
+    assert p.workspace_bytes == (S * 64 * 27 * 64 * 4 if S > 1 else 0)
+    assert p.dw_shape() == (64, 3, 3, 3, 64)
+    # the flat MFMA kernel takes any 3D shape
+    p = plan(cfg, variant=gcb.VARIANT_MFMA)
+    assert p.info["variant"] == gcb.VARIANT_MFMA
+    # depthwise 3D has no channel-vector kernel: it plans the MFMA kernel
+    # with merged groups, and asking for the depthwise form is unsupported
+    dw = prob3(32, 1, 32, 32, (4, 6, 6), (3, 3, 3), pad=(1, 1, 1))
+    p = plan(dw)
+    assert p.info["variant"] in (gcb.VARIANT_MFMA, gcb.VARIANT_ROWSLAB) and p.info["group_merge"] > 1
+    _expect(gcb.ERR_UNSUPPORTED, dw, variant=gcb.VARIANT_DEPTHWISE)
+
+
+def test_3d_invalid_problems_rejected():
+    _expect(gcb.ERR_INVALID_ARG, prob3(1, 1, 8, 8, (2, 4, 4), (3, 1, 1)))          # empty depth output
+    _expect(gcb.ERR_INVALID_ARG, prob3(1, 1, 8, 8, (4, 4, 4), (1, 1, 1), stride=(0, 1, 1)))
+    _expect(gcb.ERR_INVALID_ARG, dict(prob3(1, 1, 8, 8, (4, 4, 4), (1, 1, 1)), ndim=4))
