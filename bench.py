@@ -225,7 +225,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="c1,c2,c3,c4a,c4b,c5")
+    ap.add_argument("--configs", default="c1,c2,c3,c4a,c4b,c5,pw,c3d")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (for profilers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-merge", action="store_true", help="also time the depthwise shape over Gm and S")
@@ -254,7 +254,7 @@ def main():
     per = {}
     head = None
     for name in names:
-        cfg = workloads.CONFIGS[name]
+        cfg = workloads.get(name)
         case = Case(torch, gcb, workloads, name, cfg)
         sec = case.time_steps(args.steps, args.warmup, use_graphs=not args.eager)
         t_main, t_red = case.kernel_times()

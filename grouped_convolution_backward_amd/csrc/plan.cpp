@@ -74,7 +74,7 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
                   int out_final, Plan& out, std::string* why) {
     const int64_t cpg = p.C / p.G, kpg = p.K / p.G;
     auto no = [&](const char* m) { if (why) *why = m; return false; };
-    if (g.X != 3 && g.X != 5) return no("row-slab needs a filter width of 3 or 5");
+    if (g.X != 1 && g.X != 3 && g.X != 5) return no("row-slab needs a filter width of 1, 3 or 5");
     if (g.dw != 1) return no("row-slab needs a filter dilation of 1 along w");
     if (2 * p.N * g.Hi * g.Wi * p.C >= (int64_t{1} << 31) || 2 * p.N * g.Ho * g.Wo * p.K >= (int64_t{1} << 31))
         return no("row-slab needs X and dY below 2 GiB");
@@ -88,7 +88,7 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
     if (cpg % 4 || gkpg % 8 || p.K % 8 || p.C % 8) return no("row-slab needs 16-byte channel vectors");
     // tile: 64 x 64 channel blocks when the merged runs allow it, else 32 x 32
     int mb, cb;
-    if (g.X == 3 && gcpg % 64 == 0 && gkpg > 32) { mb = 64; cb = 64; }
+    if ((g.X == 3 || g.X == 1) && gcpg % 64 == 0 && gkpg > 32) { mb = 64; cb = 64; }
     else if (gcpg % 32 == 0) { mb = 32; cb = 32; }
     else return no("row-slab needs a merged channel run that is a multiple of 32");
     const int64_t NHo = p.N * g.Do * g.Ho;       // output rows (n, do, ho)

@@ -358,13 +358,16 @@ int launch_rs(const Plan& plan, const RowSlabArgs& a, hipStream_t s) {
 
 template <bool F16>
 int launch_rs_t(const Plan& plan, const RowSlabArgs& a, hipStream_t s) {
-    static_assert(kNumRsInstances == 5, "dispatch table");
+    static_assert(kNumRsInstances == 8, "dispatch table");
     switch (plan.rs_inst) {
         case 0: return launch_rs<0, F16>(plan, a, s);
         case 1: return launch_rs<1, F16>(plan, a, s);
         case 2: return launch_rs<2, F16>(plan, a, s);
         case 3: return launch_rs<3, F16>(plan, a, s);
         case 4: return launch_rs<4, F16>(plan, a, s);
+        case 5: return launch_rs<5, F16>(plan, a, s);
+        case 6: return launch_rs<6, F16>(plan, a, s);
+        case 7: return launch_rs<7, F16>(plan, a, s);
         default: return (int)hipErrorInvalidValue;
     }
 }

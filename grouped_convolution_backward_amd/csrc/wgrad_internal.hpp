@@ -78,6 +78,9 @@ constexpr RsInstance kRsInstances[] = {
     {32, 32, 3, 4, 2, 32, 1, 4},    // two rows up to 30 wide
     {32, 32, 3, 4, 1, 80, 1, 4},    // one row (or segment) up to 64 wide
     {32, 32, 5, 8, 1, 144, 1, 2},   // 128-position row segments, width-5 filter
+    {64, 64, 1, 2, 1, 32, 1, 4},    // pointwise (width-1 filter): 32-position row segments
+    {64, 64, 1, 2, 1, 64, 2, 3},    // pointwise, stride 2: 32-position segments
+    {32, 32, 1, 4, 1, 64, 1, 4},    // pointwise, 32-channel blocks
 };
 constexpr int kNumRsInstances = sizeof(kRsInstances) / sizeof(kRsInstances[0]);
 // MFMA waves per slab stream: two for 64-channel blocks (each holds 32

@@ -436,3 +436,47 @@ def test_3d(i, variant):
             check_exact(cfg, bits.reshape(-1), dw64)
         else:
             check_tol(cfg, vals.reshape(-1), dw64, ab64)
+
+
+# the widened rows at full size (pointwise and 3D dense), on sampled elements
+@pytest.mark.parametrize("name", list(workloads.WIDER))
+@pytest.mark.parametrize("dist", ["int", "uniform", "ones"])
+def test_wider_full_size_sampled(name, dist):
+    cfg = workloads.WIDER[name]
+    assert tuple(oracle.out_len(cfg)) == tuple(cfg["out_len"])
+    xb, dyb = workloads.inputs(cfg, dist)
+    vals, bits, p = run_gpu(cfg, xb, dyb)
+    idx = sample_idx(cfg, bits.size)
+    dw64, ab64 = oracle_ref(cfg, xb, dyb, idx)
+    if dist == "uniform":
+        check_tol(cfg, vals.reshape(-1), dw64, ab64, idx)
+    else:
+        check_exact(cfg, bits.reshape(-1), dw64, idx)
+
+
+# pointwise (1x1) shapes on every element: both row-slab channel blocks,
+# stride 2, merged groups, fp16 with fp32 output, and the flat MFMA kernel
+POINTWISE_CASES = [
+    ("pw", dict(N=2), {}),
+    ("pw", dict(N=2, stride=(2, 2), out_len=(28, 28)), {}),
+    ("pw", dict(N=1, C=96, K=64, in_len=(20, 30), out_len=(20, 30)), {}),
+    ("pw", dict(N=2, G=8, C=256, K=128, in_len=(14, 14), out_len=(14, 14)), {}),
+    ("pw", dict(N=1, in_len=(17, 23), out_len=(17, 23), in_dtype="fp16", out_dtype="fp32"), {}),
+    ("pw", dict(N=1, in_len=(17, 23), out_len=(17, 23)), dict(variant=gcb.VARIANT_MFMA)),
+]
+
+
+@pytest.mark.parametrize("i", range(len(POINTWISE_CASES)))
+def test_pointwise(i):
+    base, changes, ov = POINTWISE_CASES[i]
+    cfg = workloads.problem(base, **changes)
+    cfg["name"] = f"pw{i}"
+    assert tuple(oracle.out_len(cfg)) == tuple(cfg["out_len"])
+    for dist in ("int", "uniform"):
+        xb, dyb = workloads.inputs(cfg, dist)
+        vals, bits, p = run_gpu(cfg, xb, dyb, **ov)
+        dw64, ab64 = oracle_ref(cfg, xb, dyb)
+        if dist == "int":
+            check_exact(cfg, bits.reshape(-1), dw64)
+        else:
+            check_tol(cfg, vals.reshape(-1), dw64, ab64)

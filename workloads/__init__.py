@@ -118,9 +118,26 @@ CONFIGS = {
 }
 
 
+# Shapes for the rows beyond the five configurations (pointwise and 3D),
+# measured and parity-tested the same way.
+WIDER = {
+    "pw": _cfg("pw", 2, 1, 32, 256, 64, (56, 56), (1, 1), (1, 1), (0, 0), (1, 1), (56, 56),
+               "bf16", "bf16", "uniform", (6001, 6002),
+               "pointwise: G=1 N=32 56x56 C=256 K=64 1x1 s1 p0"),
+    "c3d": _cfg("c3d", 3, 1, 4, 64, 64, (16, 28, 28), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1),
+                (16, 28, 28), "bf16", "bf16", "uniform", (7001, 7002),
+                "3D dense: G=1 N=4 16x28x28 C=64 K=64 3x3x3 s1 p1"),
+}
+
+
+def get(name: str) -> dict:
+    """A configuration by name, from CONFIGS or WIDER."""
+    return CONFIGS[name] if name in CONFIGS else WIDER[name]
+
+
 def problem(name_or_cfg, **changes) -> dict:
     """A copy of a configuration with some fields replaced."""
-    cfg = dict(CONFIGS[name_or_cfg]) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
+    cfg = dict(get(name_or_cfg)) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
     cfg.update(changes)
     return cfg
 
