@@ -8,7 +8,8 @@ The sums themselves run in ``wgrad_oracle.c`` (fp64, direct loop, one fixed
 summation order per element); this module builds and loads that library and
 adds the pieces of the acceptance test that sit on the oracle side:
 
-* ``wgrad`` / ``wgrad_sampled``: dW and sum|dY*X| in fp64 (GKYXC order).
+* ``wgrad`` / ``wgrad_sampled``: dW and sum|dY*X| in fp64 (GK[Z]YXC order).
+* ``dgrad``: the backward-data sums dX and sum|dY*W| in fp64 (N[D]HWGC order).
 * ``round_to``: fp64 -> bf16/fp16 round-to-nearest-even, done directly from
   fp64 (no intermediate fp32, so no double rounding).
 * ``bound``: the elementwise acceptance bound tau*sum|dY*X| + 1e-6 with
@@ -80,6 +81,8 @@ def _load():
         lib.oracle_out_len.argtypes = [P, ctypes.POINTER(ctypes.c_int64),
                                        ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
         lib.oracle_out_len.restype = ctypes.c_int
+        lib.oracle_dgrad.argtypes = [P, u16p, u16p, f64p, f64p, ctypes.c_int]
+        lib.oracle_dgrad.restype = ctypes.c_int
         lib.oracle_widen.argtypes = [u16p, ctypes.c_int64, ctypes.c_int64, f64p]
         lib.oracle_widen.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -221,3 +224,22 @@ def violations(gpu64: np.ndarray, dw64: np.ndarray, absdw: np.ndarray, out_dtype
     """Boolean mask of elements outside the bound (NaN counts as outside)."""
     err = np.abs(np.asarray(gpu64, np.float64) - dw64)
     return ~(err <= bound(absdw, out_dtype))
+
+
+def dgrad(prob: dict, dy_bits: np.ndarray, w_bits: np.ndarray, nthreads: int = 0):
+    """Backward data: dX and sum|dY*W| in fp64, each shaped (N, *in_len, C)
+    (NDHWGC order). w_bits is the GK[Z]YXC weight, dy_bits the NDHWGK output
+    gradient."""
+    nd = int(prob["ndim"])
+    dy_bits = np.ascontiguousarray(dy_bits, dtype=np.uint16).reshape(-1)
+    w_bits = np.ascontiguousarray(w_bits, dtype=np.uint16).reshape(-1)
+    if dy_bits.size != int(prob["N"]) * int(np.prod(out_len(prob))) * int(prob["K"]):
+        raise ValueError("dy has the wrong number of elements")
+    if w_bits.size != int(np.prod(dw_shape(prob))):
+        raise ValueError("w has the wrong number of elements")
+    shape = (int(prob["N"]), *tuple(prob["in_len"])[:nd], int(prob["C"]))
+    dx = np.zeros(int(np.prod(shape)), np.float64)
+    ab = np.zeros_like(dx)
+    if _load().oracle_dgrad(ctypes.byref(_to_struct(prob)), dy_bits, w_bits, dx, ab, nthreads):
+        raise ValueError("oracle rejected the problem")
+    return dx.reshape(shape), ab.reshape(shape)

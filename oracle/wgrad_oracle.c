@@ -242,6 +242,85 @@ int oracle_wgrad_sampled(const oracle_problem* p, const uint16_t* x, const uint1
     return 0;
 }
 
+/*
+ * Backward data (dgrad) of the same convolution, fp64: the input gradient
+ *
+ *   dX[n,di,hi,wi,g,c] = sum_{k<kpg} sum_{z,y,x} [do, ho, wo exist]
+ *                          dY[n,do,ho,wo,g,k] * W[g,k,z,y,x,c]
+ *
+ * where (do, ho, wo) is the output position whose tap (z, y, x) reads
+ * (di, hi, wi): do = (di + pl_d - z*d_d) / s_d when that division is exact
+ * and 0 <= do < Do, likewise for h and w. It is the adjoint of the forward
+ * convolution's map X -> Y for a fixed W (the Composable Kernel page's
+ * backward-weight kernel computes the other adjoint, W -> Y for a fixed X).
+ * w: K*Z*Y*X*(C/G) 16-bit patterns in GK[Z]YXC order; dy: N*Do*Ho*Wo*K.
+ * dx and absdx hold N*Di*Hi*Wi*C doubles (NDHWGC order). Each element is one
+ * fp64 sum in ascending (k, z, y, x) order. Returns 0, or -1 on a bad
+ * problem or allocation failure.
+ */
+int oracle_dgrad(const oracle_problem* p, const uint16_t* dy, const uint16_t* w,
+                 double* dx, double* absdx, int nthreads)
+{
+    geom g;
+    if (make_geom(p, &g)) return -1;
+    if (p->G < 1 || p->C % p->G || p->K % p->G || p->N < 0) return -1;
+    const int64_t cpg = p->C / p->G, kpg = p->K / p->G;
+    const int64_t Di = g.in[0], Hi = g.in[1], Wi = g.in[2];
+    const int64_t Do = g.out[0], Ho = g.out[1], Wo = g.out[2];
+    const int64_t Z = g.f[0], Y = g.f[1], X = g.f[2];
+    const int64_t ndy = p->N * Do * Ho * Wo * p->K;
+    const int64_t nw = p->K * Z * Y * X * cpg;
+    double* dys = widen_all(dy, ndy, p->in_dtype);
+    double* ws = widen_all(w, nw, p->in_dtype);
+    if (!dys || !ws) { free(dys); free(ws); return -1; }
+    const int64_t rows = p->N * Di * Hi * Wi;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+#endif
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t t = r;
+        const int64_t wi = t % Wi;  t /= Wi;
+        const int64_t hi = t % Hi;  t /= Hi;
+        const int64_t di = t % Di;
+        const int64_t n = t / Di;
+        for (int64_t gi = 0; gi < p->G; ++gi)
+            for (int64_t c = 0; c < cpg; ++c) {
+                double acc = 0.0, ab = 0.0;
+                for (int64_t k = 0; k < kpg; ++k) {
+                    const int64_t kt = gi * kpg + k;
+                    for (int64_t z = 0; z < Z; ++z) {
+                        const int64_t nd = di + g.pl[0] - z * g.dl[0];
+                        if (nd < 0 || nd % g.s[0]) continue;
+                        const int64_t od = nd / g.s[0];
+                        if (od >= Do) continue;
+                        for (int64_t y = 0; y < Y; ++y) {
+                            const int64_t nh = hi + g.pl[1] - y * g.dl[1];
+                            if (nh < 0 || nh % g.s[1]) continue;
+                            const int64_t ho = nh / g.s[1];
+                            if (ho >= Ho) continue;
+                            for (int64_t x = 0; x < X; ++x) {
+                                const int64_t nwv = wi + g.pl[2] - x * g.dl[2];
+                                if (nwv < 0 || nwv % g.s[2]) continue;
+                                const int64_t wo = nwv / g.s[2];
+                                if (wo >= Wo) continue;
+                                const double a = dys[(((n * Do + od) * Ho + ho) * Wo + wo) * p->K + kt];
+                                const double b = ws[(((kt * Z + z) * Y + y) * X + x) * cpg + c];
+                                acc += a * b;
+                                ab += fabs(a * b);
+                            }
+                        }
+                    }
+                }
+                dx[r * p->C + gi * cpg + c] = acc;
+                absdx[r * p->C + gi * cpg + c] = ab;
+            }
+    }
+    free(dys);
+    free(ws);
+    return 0;
+}
+
 /* Widening of a buffer of 16-bit patterns, exposed so that tests can pin it. */
 int oracle_widen(const uint16_t* src, int64_t n, int64_t dtype, double* out)
 {
