@@ -1,10 +1,11 @@
-"""Grouped 1D/2D convolution backward-weight (wgrad) for MI355X (gfx950).
+"""Grouped 1D/2D/3D convolution backward-weight (wgrad), and backward data
+(dgrad) of the same convolution, for MI355X (gfx950).
 
 A thin ctypes binding over libwgrad.so, whose C ABI is include/wgrad.h. The
 functions keep the ABI's names (``wgrad_plan``, ``wgrad_run``,
 ``wgrad_workspace_bytes``, ``wgrad_plan_query``, ``wgrad_plan_describe``,
-``wgrad_plan_destroy``, ``wgrad_last_error``); this module only marshals
-arguments. Every step of the computation runs in the HIP kernels; there is
+``wgrad_plan_destroy``, ``wgrad_last_error``, ``wgrad_dgrad_plan``,
+``wgrad_dgrad_run``); this module only marshals arguments. Every step of the computation runs in the HIP kernels; there is
 no CPU or PyTorch fallback, and loading fails loudly if the library has not
 been built (``python -m grouped_convolution_backward_amd.build``).
 
@@ -22,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libwgrad.so")
 
 BF16, FP16, FP32 = 0, 1, 2
 DTYPES = {"bf16": BF16, "fp16": FP16, "fp32": FP32}
-VARIANT_AUTO, VARIANT_MFMA, VARIANT_DEPTHWISE, VARIANT_ROWSLAB = 0, 1, 2, 3
+VARIANT_AUTO, VARIANT_MFMA, VARIANT_DEPTHWISE, VARIANT_ROWSLAB, VARIANT_DGRAD = 0, 1, 2, 3, 4
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 
 
@@ -61,7 +62,8 @@ class wgrad_plan_info(ctypes.Structure):
 
 # every symbol include/wgrad.h declares
 EXPORTS = ("wgrad_plan", "wgrad_workspace_bytes", "wgrad_run", "wgrad_run_stage", "wgrad_plan_query",
-           "wgrad_plan_describe", "wgrad_plan_destroy", "wgrad_last_error", "wgrad_version")
+           "wgrad_plan_describe", "wgrad_plan_destroy", "wgrad_last_error", "wgrad_version",
+           "wgrad_dgrad_plan", "wgrad_dgrad_run")
 
 _lib = None
 
@@ -101,6 +103,11 @@ def load_library():
     lib.wgrad_last_error.restype = ctypes.c_char_p
     lib.wgrad_version.argtypes = []
     lib.wgrad_version.restype = ctypes.c_char_p
+    lib.wgrad_dgrad_plan.argtypes = [ctypes.POINTER(wgrad_problem), ctypes.POINTER(wgrad_overrides),
+                                     ctypes.c_int, ctypes.POINTER(vp)]
+    lib.wgrad_dgrad_plan.restype = ctypes.c_int
+    lib.wgrad_dgrad_run.argtypes = [vp, vp, vp, vp, vp]
+    lib.wgrad_dgrad_run.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -175,8 +182,22 @@ def wgrad_run_stage(plan: "Plan", stage: int, x, dy, dw, ws=None, stream=None) -
     plan.run(x, dy, dw, ws, stream, stage=stage)
 
 
+def wgrad_dgrad_plan(problem: dict, variant: int = 0, tile: int = 0, split_k: int = 0, group_merge: int = 0,
+                     hip_device: int | None = None) -> "DgradPlan":
+    """Create a backward-data plan (same problem dict; in_dtype is dY's and
+    W's type, out_dtype dX's)."""
+    return DgradPlan(problem, split_k, group_merge, variant, tile, hip_device)
+
+
+def wgrad_dgrad_run(plan: "DgradPlan", dy, w, dx, stream=None) -> None:
+    """Enqueue dX = dgrad(dY, W) on the stream (torch tensors on the GPU)."""
+    plan.run(dy, w, dx, stream)
+
+
 class Plan:
     """Owns a wgrad_plan_t. Immutable; run() may be called many times."""
+
+    _create = "wgrad_plan"
 
     def __init__(self, problem: dict, split_k=0, group_merge=0, variant=0, tile=0, hip_device=None):
         lib = load_library()
@@ -186,8 +207,8 @@ class Plan:
             hip_device = torch.cuda.current_device()
         ov = wgrad_overrides(int(split_k), int(group_merge), int(variant), int(tile))
         h = ctypes.c_void_p()
-        _check(lib.wgrad_plan(ctypes.byref(make_problem(problem)), ctypes.byref(ov), int(hip_device),
-                              ctypes.byref(h)))
+        _check(getattr(lib, self._create)(ctypes.byref(make_problem(problem)), ctypes.byref(ov), int(hip_device),
+                                          ctypes.byref(h)))
         self.handle = h
         self.info = wgrad_plan_query(self)
         self.name = wgrad_plan_describe(self)
@@ -248,6 +269,44 @@ class Plan:
         import torch
         n = max(self.workspace_bytes, 16)
         return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+class DgradPlan(Plan):
+    """Owns a backward-data wgrad_plan_t (from wgrad_dgrad_plan)."""
+
+    _create = "wgrad_dgrad_plan"
+
+    def dx_shape(self):
+        return self.x_shape()
+
+    def w_shape(self):
+        return self.dw_shape()
+
+    def run(self, dy, w, dx, stream=None):
+        import torch
+        p = self.problem
+        in_t = torch.bfloat16 if p["in_dtype"] == "bf16" else torch.float16
+        out_t = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[p.get("out_dtype", p["in_dtype"])]
+        for name, t, shape, dt in (("dy", dy, self.dy_shape(), in_t), ("w", w, self.w_shape(), in_t),
+                                   ("dx", dx, self.dx_shape(), out_t)):
+            if not t.is_cuda or t.dtype != dt or not t.is_contiguous() or t.numel() != _prod(shape):
+                raise ValueError(f"{name}: need a contiguous {dt} GPU tensor with {_prod(shape)} elements "
+                                 f"(got {t.dtype}, {tuple(t.shape)}, cuda={t.is_cuda})")
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        _check(load_library().wgrad_dgrad_run(self.handle, dy.data_ptr() or None, w.data_ptr() or None,
+                                              dx.data_ptr() or None, sp or None))
+
+
+def dgrad(problem: dict, dy, w, **overrides):
+    """Convenience: plan, allocate dX with torch, run."""
+    import torch
+    plan = DgradPlan(problem, **overrides)
+    out_t = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[problem.get("out_dtype", problem["in_dtype"])]
+    dx = torch.empty(plan.dx_shape(), dtype=out_t, device=dy.device)
+    plan.run(dy, w, dx)
+    return dx
 
 
 def _prod(shape):

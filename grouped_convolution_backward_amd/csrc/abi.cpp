@@ -23,6 +23,21 @@ int set_error(int code, const std::string& msg) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// hip_device >= 0: size the plan for that device, which must be gfx950;
+// -1 keeps the MI355X model (256 CUs, 8 XCDs) without touching HIP.
+int device_model(int hip_device, wgrad::DeviceModel& dev) {
+    if (hip_device < 0) return WGRAD_OK;
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, hip_device);
+    if (e != hipSuccess)
+        return set_error(WGRAD_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return set_error(WGRAD_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName +
+                                                    ", kernels are built for gfx950 only");
+    dev.num_cus = prop.multiProcessorCount;
+    return WGRAD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -33,16 +48,7 @@ int wgrad_plan(const wgrad_problem* problem, const wgrad_overrides* overrides, i
     if (!problem || !out) return set_error(WGRAD_ERR_INVALID_ARG, "problem and out must not be NULL");
     *out = nullptr;
     wgrad::DeviceModel dev{256, 8};   // MI355X: 256 CUs in 8 XCDs
-    if (hip_device >= 0) {
-        hipDeviceProp_t prop;
-        hipError_t e = hipGetDeviceProperties(&prop, hip_device);
-        if (e != hipSuccess)
-            return set_error(WGRAD_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
-        if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
-            return set_error(WGRAD_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName +
-                                                        ", kernels are built for gfx950 only");
-        dev.num_cus = prop.multiProcessorCount;
-    }
+    if (int rc = device_model(hip_device, dev)) return rc;
     std::string msg;
     wgrad_plan_s* p = new (std::nothrow) wgrad_plan_s();
     if (!p) return set_error(WGRAD_ERR_INVALID_ARG, "out of host memory");
@@ -52,6 +58,44 @@ int wgrad_plan(const wgrad_problem* problem, const wgrad_overrides* overrides, i
         return set_error(rc, msg);
     }
     *out = p;
+    return WGRAD_OK;
+}
+
+int wgrad_dgrad_plan(const wgrad_problem* problem, const wgrad_overrides* overrides, int hip_device,
+                     wgrad_plan_t** out) {
+    g_last_error.clear();
+    if (!problem || !out) return set_error(WGRAD_ERR_INVALID_ARG, "problem and out must not be NULL");
+    *out = nullptr;
+    wgrad::DeviceModel dev{256, 8};
+    if (int rc = device_model(hip_device, dev)) return rc;
+    std::string msg;
+    wgrad_plan_s* p = new (std::nothrow) wgrad_plan_s();
+    if (!p) return set_error(WGRAD_ERR_INVALID_ARG, "out of host memory");
+    int rc = wgrad::build_dgrad_plan(*problem, overrides, dev, p->plan, &msg);
+    if (rc != WGRAD_OK) {
+        delete p;
+        return set_error(rc, msg);
+    }
+    *out = p;
+    return WGRAD_OK;
+}
+
+int wgrad_dgrad_run(const wgrad_plan_t* plan, const void* dy, const void* w, void* dx, void* stream) {
+    g_last_error.clear();
+    if (!plan) return set_error(WGRAD_ERR_INVALID_ARG, "plan is NULL");
+    const wgrad::Plan& P = plan->plan;
+    if (P.op != wgrad::OP_DGRAD) return set_error(WGRAD_ERR_INVALID_ARG, "not a backward-data plan");
+    if (P.dg.total_wg == 0) return WGRAD_OK;   // N = 0: dX is empty
+    if (!dx || !dy || !w) return set_error(WGRAD_ERR_INVALID_ARG, "dy, w and dx must not be NULL");
+    if (!aligned16(dy) || !aligned16(w) || !aligned16(dx))
+        return set_error(WGRAD_ERR_INVALID_ARG, "dy, w and dx must be 16-byte aligned");
+    wgrad::DgradArgs a = P.dg;
+    a.dy = static_cast<const uint16_t*>(dy);
+    a.w = static_cast<const uint16_t*>(w);
+    a.dx = dx;
+    const int e = wgrad::launch_dgrad(P, a, stream);
+    if (e != hipSuccess)
+        return set_error(WGRAD_ERR_HIP, std::string("dgrad kernel launch: ") + hipGetErrorString((hipError_t)e));
     return WGRAD_OK;
 }
 
@@ -68,6 +112,7 @@ int run_stages(const wgrad_plan_t* plan, int first, int last, const void* x, con
     g_last_error.clear();
     if (!plan) return set_error(WGRAD_ERR_INVALID_ARG, "plan is NULL");
     const wgrad::Plan& P = plan->plan;
+    if (P.op != wgrad::OP_WGRAD) return set_error(WGRAD_ERR_INVALID_ARG, "not a backward-weight plan");
     const bool empty_in = P.info.gemm_k == 0;
     if (!dw) return set_error(WGRAD_ERR_INVALID_ARG, "dw is NULL");
     if (!empty_in && (!x || !dy)) return set_error(WGRAD_ERR_INVALID_ARG, "x and dy must not be NULL");

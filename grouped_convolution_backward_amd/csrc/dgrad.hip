@@ -1,0 +1,217 @@
+// Backward data (dgrad) of the grouped convolution on gfx950.
+//
+// Per group the input gradient is a GEMM over the (filter tap, output
+// channel) pairs:
+//
+//   dX[m][c] = sum_{t, k} A[m][(t, k)] * B[(t, k)][c],
+//   A[m][(t, k)] = dY at the output position whose tap t reads position m
+//                  (zero when that position does not exist),
+//   B[(t, k)][c] = W[k][t][c]    (GK[Z]YXC),
+//
+// with m = (n, di, hi, wi) the input positions. The reduction runs one tap at
+// a time in chunks of BK output channels. As in the dgrad part of
+// rocm-libraries PR 11602 (transpose load for bwd weight and bwd data), only
+// the B tile is staged K-outer ([k][c], straight from the weight's
+// channel-contiguous rows) and read with the CDNA4 transposed LDS read
+// ds_read_b64_tr_b16; the A tile stays M-outer ([m][k], each row one
+// contiguous run of dY channels), which is already the MFMA operand layout,
+// so a plain 16-byte LDS read serves it.
+// Every dX element is written once: no workspace and no split of the
+// reduction, so the result is deterministic.
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+
+namespace wgrad {
+namespace {
+
+using namespace dev;
+
+template <int BM, int BN, int WM, int WN, int V, bool F16>
+__global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
+    typedef typename VecT<V>::T VT;
+    constexpr int BK = 32;                         // output channels per reduction chunk
+    constexpr int PA = BK + 8;                     // A row pitch (elements): 80-byte rows
+    constexpr int PB = BN + kLdsPad;               // B row pitch for the transposed reads
+    constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int AV = BK / V;                     // vectors per A row
+    constexpr int A_LOADS = BM * AV / 256;         // A vectors per thread
+    constexpr int BVR = BN / V;                    // vectors per B row
+    constexpr int B_LOADS = (BK * BVR + 255) / 256;
+    static_assert(WM * WN == 4 && FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+    static_assert((BM * AV) % 256 == 0, "A loads");
+
+    __shared__ __attribute__((aligned(16))) uint16_t sA[BM * PA];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[BK * PB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int L = xcd_logical_id(blockIdx.x, a.total_wg);
+    const int mt = L % a.tiles_m;
+    const int rest = L / a.tiles_m;
+    const int nt = rest % a.tiles_n;
+    const int g = rest / a.tiles_n;
+    const int m0 = mt * BM, c0 = nt * BN;
+
+    // A rows this thread loads: position m -> (n, di, hi, wi)
+    int a_n[A_LOADS], a_d[A_LOADS], a_h[A_LOADS], a_w[A_LOADS];
+    bool a_in[A_LOADS];
+    const int a_kv = (tid % AV) * V;
+#pragma unroll
+    for (int p = 0; p < A_LOADS; ++p) {
+        const int row = tid / AV + p * (256 / AV);
+        const int m = m0 + row;
+        a_in[p] = m < a.M;
+        const uint32_t mm = a_in[p] ? (uint32_t)m : 0u;
+        const uint32_t q1 = magic_div(mm, a.mWi);
+        a_w[p] = (int)(mm - q1 * (uint32_t)a.Wi);
+        const uint32_t q2 = magic_div(q1, a.mHi);
+        a_h[p] = (int)(q1 - q2 * (uint32_t)a.Hi);
+        const uint32_t q3 = magic_div(q2, a.mDi);
+        a_d[p] = (int)(q2 - q3 * (uint32_t)a.Di);
+        a_n[p] = (int)q3;
+    }
+    const uint16_t* dy_g = a.dy + g * a.kpg;
+    const uint16_t* w_g = a.w + (int64_t)g * a.kpg * a.taps * a.cpg;
+
+    // output coordinate along one axis whose tap offset reaches input i:
+    // (i + pad - t*dil) / stride when exact and in range, else -1
+    auto out_coord = [](int i, int pad, int tdil, int len, MagicU32 ms, int stride) {
+        const int num = i + pad - tdil;
+        if (num < 0) return -1;
+        const int q = (int)magic_div((uint32_t)num, ms);
+        if (q * stride != num || q >= len) return -1;
+        return q;
+    };
+
+    VT ra[A_LOADS], rb[B_LOADS];
+    auto gload = [&](int chunk) {
+        const int t = chunk / a.kchunks;
+        const int k0 = (chunk - t * a.kchunks) * BK;
+        const int tzy = t / a.Xf, tx = t - tzy * a.Xf;
+        const int tz = tzy / a.Yf, ty = tzy - tz * a.Yf;
+#pragma unroll
+        for (int p = 0; p < A_LOADS; ++p) {
+            VT v = 0;
+            const int k = k0 + a_kv;
+            if (a_in[p] && k < a.kpg) {
+                const int od = out_coord(a_d[p], a.pd, tz * a.dd, a.Do, a.msd, a.sd);
+                const int oh = out_coord(a_h[p], a.ph, ty * a.dh, a.Ho, a.msh, a.sh);
+                const int ow = out_coord(a_w[p], a.pw, tx * a.dw, a.Wo, a.msw, a.sw);
+                if (od >= 0 && oh >= 0 && ow >= 0)
+                    v = *reinterpret_cast<const VT*>(dy_g + (((a_n[p] * a.Do + od) * a.Ho + oh) * a.Wo + ow) * a.Ktot + k);
+            }
+            ra[p] = v;
+        }
+#pragma unroll
+        for (int p = 0; p < B_LOADS; ++p) {
+            VT v = 0;
+            const int idx = tid + p * 256;
+            const int row = idx / BVR, cv = (idx - row * BVR) * V;
+            const int k = k0 + row;
+            if (row < BK && k < a.kpg && c0 + cv < a.cpg)
+                v = *reinterpret_cast<const VT*>(w_g + ((int64_t)k * a.taps + t) * a.cpg + c0 + cv);
+            rb[p] = v;
+        }
+    };
+    auto sstore = [&]() {
+#pragma unroll
+        for (int p = 0; p < A_LOADS; ++p) {
+            const int row = tid / AV + p * (256 / AV);
+            *reinterpret_cast<VT*>(sA + row * PA + a_kv) = ra[p];
+        }
+#pragma unroll
+        for (int p = 0; p < B_LOADS; ++p) {
+            const int idx = tid + p * 256;
+            const int row = idx / BVR, cv = (idx - row * BVR) * V;
+            if (row < BK) *reinterpret_cast<VT*>(sB + row * PB + cv) = rb[p];
+        }
+    };
+
+    const int wm0 = (wave % WM) * WTM, wn0 = (wave / WM) * WTN;
+    const int g16 = lane >> 4;
+    const int frag_row = (g16 >> 1) * 8 + ((lane & 15) >> 2);   // transposed-read row
+    const int frag_col = (g16 & 1) * 16 + (lane & 3) * 4;
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{0};
+
+    const int nchunks = a.taps * a.kchunks;
+    if (nchunks > 0) {
+        gload(0);
+        sstore();
+        __syncthreads();
+    }
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const bool more = ch + 1 < nchunks;
+        if (more) gload(ch + 1);   // the next chunk waits in registers
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            i16x8 af[FM], bf[FN];
+            // A operand: row lane%32 of the wave's block, k = 8*(lane/32) .. +7
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const i16x8*>(sA + (wm0 + i * 32 + (lane & 31)) * PA + ks * 16 + 8 * (lane >> 5));
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bf[j] = tr_frag(sB + (ks * 16 + frag_row) * PB + wn0 + j * 32 + frag_col, PB);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) mfma_step32<F16>(af[i], bf[j], acc[i][j]);
+        }
+        if (more) {
+            __syncthreads();
+            sstore();
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: element (m, c) of the tile is dX[m][g*cpg + c]
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int c = c0 + wn0 + j * 32 + (lane & 31);
+        if (c >= a.cpg) continue;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + wm0 + i * 32 + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+                if (m < a.M) store_out(a.dx, a.out_mode, (int64_t)m * a.Ctot + g * a.cpg + c, acc[i][j][v]);
+            }
+    }
+}
+
+template <int BM, int BN, int WM, int WN, bool F16>
+int launch_v(const DgradArgs& a, int V, hipStream_t s) {
+    dim3 grid(a.total_wg), block(256);
+    switch (V) {
+        case 8: hipLaunchKernelGGL((dgrad_kernel<BM, BN, WM, WN, 8, F16>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((dgrad_kernel<BM, BN, WM, WN, 4, F16>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((dgrad_kernel<BM, BN, WM, WN, 2, F16>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((dgrad_kernel<BM, BN, WM, WN, 1, F16>), grid, block, 0, s, a); break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+template <bool F16>
+int launch_t(const Plan& plan, const DgradArgs& a, hipStream_t s) {
+    switch (plan.dg_bn) {
+        case 32: return launch_v<128, 32, 4, 1, F16>(a, plan.dg_v, s);
+        case 64: return launch_v<128, 64, 2, 2, F16>(a, plan.dg_v, s);
+        case 128: return launch_v<128, 128, 2, 2, F16>(a, plan.dg_v, s);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int launch_dgrad(const Plan& plan, const DgradArgs& a, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return plan.in_f16 ? launch_t<true>(plan, a, s) : launch_t<false>(plan, a, s);
+}
+
+}  // namespace wgrad

@@ -174,11 +174,9 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
     return true;
 }
 
-}  // namespace
-
-int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceModel& dev, Plan& out,
-               std::string* msg) {
-    const int E = WGRAD_ERR_INVALID_ARG, U = WGRAD_ERR_UNSUPPORTED;
+// Validation and spatial geometry shared by both directions.
+int check_problem(const wgrad_problem& p, Geo& g, std::string* msg) {
+    const int E = WGRAD_ERR_INVALID_ARG;
     if (p.ndim < 1 || p.ndim > 3) return fail(msg, E, "ndim must be 1, 2 or 3 (got %d)", p.ndim);
     if (p.reserved != 0) return fail(msg, E, "reserved field must be 0");
     if (p.in_dtype != WGRAD_BF16 && p.in_dtype != WGRAD_FP16)
@@ -212,7 +210,7 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
         if (span < 0) return fail(msg, E, "empty output: the dilated filter exceeds the padded input");
         ol[ax] = span / p.stride[i] + 1;
     }
-    Geo g{};
+    g = Geo{};
     g.Di = len[0]; g.Hi = len[1]; g.Wi = len[2];
     g.Z = fl[0];   g.Y = fl[1];   g.X = fl[2];
     g.sd = st[0];  g.sh = st[1];  g.sw = st[2];
@@ -230,6 +228,21 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
     if ((g.Do * g.sd + g.Z * g.dd) > kMax31 || (g.Ho * g.sh + g.Y * g.dh) > kMax31 ||
         (g.Wo * g.sw + g.X * g.dw) > kMax31)
         return fail(msg, E, "spatial index range must fit in 31 bits");
+    return WGRAD_OK;
+}
+
+}  // namespace
+
+int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceModel& dev, Plan& out,
+               std::string* msg) {
+    const int E = WGRAD_ERR_INVALID_ARG, U = WGRAD_ERR_UNSUPPORTED;
+    Geo g;
+    if (int rc = check_problem(p, g, msg)) return rc;
+    const int64_t cpg = p.C / p.G, kpg = p.K / p.G;
+    const int64_t R = p.N * g.Do * g.Ho * g.Wo;
+    const int64_t nx = p.N * g.Di * g.Hi * g.Wi * p.C;
+    const int64_t ndy = R * p.K;
+    const int64_t ndw = p.K * g.Z * g.Y * g.X * cpg;
 
     wgrad_overrides o{};
     if (ov) o = *ov;
@@ -259,6 +272,7 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
                         2 * nx < (int64_t{1} << 31) && 2 * ndy < (int64_t{1} << 31);
     const bool dw_filter = dw2_ok || (g.Y == 3 && g.X == 3) || (g.Y == 1 && (g.X == 3 || g.X == 5));
     int variant = o.variant;
+    if (variant == WGRAD_VARIANT_DGRAD) return fail(msg, U, "the DGRAD variant belongs to backward-data plans");
     if (variant < WGRAD_VARIANT_AUTO || variant > WGRAD_VARIANT_ROWSLAB)
         return fail(msg, E, "unknown variant %d", variant);
     std::string rs_why;
@@ -500,6 +514,83 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
     while (zl < 64 && zl * 2 <= info.split_k && ceil_div(nvec, 256 / zl) < 2 * dev.num_cus) zl *= 2;
     out.red = ReduceArgs{nullptr, nullptr, (int32_t)ndw, info.split_k, out_final, zl, vec4};
     if (info.split_k > 1) info.grid_reduce = ceil_div(nvec, 256 / zl);
+    return WGRAD_OK;
+}
+
+int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceModel& dev, Plan& out,
+                     std::string* msg) {
+    const int U = WGRAD_ERR_UNSUPPORTED;
+    Geo g;
+    if (int rc = check_problem(p, g, msg)) return rc;
+    wgrad_overrides o{};
+    if (ov) o = *ov;
+    if (o.split_k < 0 || o.group_merge < 0 || o.variant < 0 || o.tile < 0)
+        return fail(msg, WGRAD_ERR_INVALID_ARG, "overrides must be >= 0");
+    if (o.split_k > 1) return fail(msg, U, "backward data does not split its reduction");
+    if (o.group_merge > 1) return fail(msg, U, "backward data does not merge groups");
+    if (o.variant != WGRAD_VARIANT_AUTO && o.variant != WGRAD_VARIANT_DGRAD)
+        return fail(msg, U, "backward data plans use the DGRAD variant only");
+    const int64_t cpg = p.C / p.G, kpg = p.K / p.G;
+    const int64_t taps = g.Z * g.Y * g.X;
+    const int64_t M = p.N * g.Di * g.Hi * g.Wi;
+    int V = 8;
+    while (V > 1 && (kpg % V || cpg % V || p.K % V || p.C % V)) V >>= 1;
+    int tile_id = o.tile;
+    if (!tile_id) {
+        const int64_t tm = ceil_div(M, 128);
+        tile_id = cpg <= 32 ? 1 : cpg <= 64 ? 2 : (tm * ceil_div(cpg, 128) * p.G >= 2 * dev.num_cus ? 3 : 2);
+    }
+    const DgradTile* t = nullptr;
+    for (const auto& d : kDgradTiles)
+        if (d.id == tile_id) t = &d;
+    if (!t) return fail(msg, U, "unknown dgrad tile id %d", tile_id);
+    const int64_t tiles_m = ceil_div(M, t->bm), tiles_n = ceil_div(cpg, t->bn);
+    const int64_t total = tiles_m * tiles_n * p.G;
+    if (total > kMax31) return fail(msg, U, "grid too large");
+    out = Plan{};
+    out.op = OP_DGRAD;
+    out.prob = p;
+    out.in_f16 = p.in_dtype == WGRAD_FP16;
+    out.variant = WGRAD_VARIANT_DGRAD;
+    DgradArgs& a = out.dg;
+    a = DgradArgs{};
+    a.Ktot = (int32_t)p.K; a.Ctot = (int32_t)p.C; a.kpg = (int32_t)kpg; a.cpg = (int32_t)cpg;
+    a.Di = (int32_t)g.Di; a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi;
+    a.Do = (int32_t)g.Do; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo;
+    a.Xf = (int32_t)g.X; a.Yf = (int32_t)g.Y; a.taps = (int32_t)taps;
+    a.sd = (int32_t)g.sd; a.sh = (int32_t)g.sh; a.sw = (int32_t)g.sw;
+    a.dd = (int32_t)g.dd; a.dh = (int32_t)g.dh; a.dw = (int32_t)g.dw;
+    a.pd = (int32_t)g.pd; a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
+    a.M = (int32_t)M;
+    a.kchunks = (int32_t)ceil_div(kpg, 32);
+    a.tiles_m = (int32_t)tiles_m; a.tiles_n = (int32_t)tiles_n; a.total_wg = (int32_t)total;
+    a.out_mode = p.out_dtype == WGRAD_BF16 ? OUT_BF16 : p.out_dtype == WGRAD_FP16 ? OUT_FP16 : OUT_FP32;
+    a.mWi = make_magic((uint32_t)g.Wi); a.mHi = make_magic((uint32_t)g.Hi); a.mDi = make_magic((uint32_t)g.Di);
+    a.msd = make_magic((uint32_t)g.sd); a.msh = make_magic((uint32_t)g.sh); a.msw = make_magic((uint32_t)g.sw);
+    out.dg_bn = t->bn;
+    out.dg_v = V;
+    wgrad_plan_info& info = out.info;
+    {
+        const int64_t all[3] = {g.Do, g.Ho, g.Wo};
+        for (int i = 0; i < 3; ++i) info.out_len[i] = i < p.ndim ? all[3 - p.ndim + i] : 0;
+    }
+    info.gemm_m = M;
+    info.gemm_n = cpg;
+    info.gemm_k = kpg * taps;
+    info.variant = WGRAD_VARIANT_DGRAD;
+    info.tile = tile_id;
+    info.tile_m = t->bm; info.tile_n = t->bn; info.tile_k = 32;
+    info.split_k = 1;
+    info.group_merge = 1;
+    info.vector_width = V;
+    info.grid_main = total;
+    info.grid_reduce = 0;
+    info.workspace_bytes = 0;
+    info.num_cus = dev.num_cus;
+    char name[160];
+    snprintf(name, sizeof name, "dgrad_mfma_%s_t%d_%dx%dx32_v%d_kouterB", out.in_f16 ? "fp16" : "bf16", tile_id,
+             t->bm, t->bn, V);
+    out.name = name;
     return WGRAD_OK;
 }
 

@@ -182,6 +182,28 @@ struct Dw3Args {
     uint32_t x_bytes, dy_bytes;
 };
 
+// Backward data: flat MFMA implicit GEMM over input positions
+// m = (n, di, hi, wi), one group per grid slice, reduction over
+// (tap, output channel) in chunks of 32 channels of one tap.
+struct DgradArgs {
+    const uint16_t* dy;
+    const uint16_t* w;
+    void* dx;
+    int32_t Ktot, Ctot, kpg, cpg;
+    int32_t Di, Hi, Wi, Do, Ho, Wo;
+    int32_t Xf, Yf, taps;          // filter width, height and Z*Y*X
+    int32_t sd, sh, sw, dd, dh, dw, pd, ph, pw;
+    int32_t M;                     // N*Di*Hi*Wi
+    int32_t kchunks;               // ceil(kpg / 32)
+    int32_t tiles_m, tiles_n, total_wg, out_mode;
+    MagicU32 mWi, mHi, mDi, msd, msh, msw;
+};
+// dgrad tiles: id -> (BM, BN); 4 waves each
+struct DgradTile {
+    int id, bm, bn;
+};
+constexpr DgradTile kDgradTiles[] = {{1, 128, 32}, {2, 128, 64}, {3, 128, 128}};
+
 struct ReduceArgs {
     const float* ws;
     void* dw;
@@ -211,7 +233,10 @@ struct DeviceModel {
     int num_xcds;
 };
 
+enum PlanOp : int { OP_WGRAD = 0, OP_DGRAD = 1 };
+
 struct Plan {
+    int op;              // PlanOp
     wgrad_problem prob;
     wgrad_plan_info info;
     int variant;
@@ -227,12 +252,16 @@ struct Plan {
     int lds_bytes;               // dynamic LDS of the main kernel
     ReduceArgs red;
     int dw_tile_y, dw_tile_x;   // depthwise kernel filter instance
+    DgradArgs dg;
+    int dg_bn, dg_v;             // dgrad tile width and load vector width
     std::string name;
 };
 
 // Host planning (no HIP calls). Returns a wgrad_status and sets *msg on error.
 int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceModel& dev,
                Plan& out, std::string* msg);
+int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceModel& dev,
+                     Plan& out, std::string* msg);
 
 // Kernel launchers (kernels.hip). Return a hipError_t value (0 = success).
 int launch_mfma(const Plan& plan, const MfmaArgs& a, void* stream);
@@ -241,5 +270,6 @@ int launch_rowslab(const Plan& plan, const RowSlabArgs& a, void* stream);
 int launch_depthwise2(const Plan& plan, const Dw2Args& a, void* stream);
 int launch_depthwise3(const Plan& plan, const Dw3Args& a, void* stream);
 int launch_reduce(const ReduceArgs& a, int64_t grid, void* stream);
+int launch_dgrad(const Plan& plan, const DgradArgs& a, void* stream);   // dgrad.hip
 
 }  // namespace wgrad

@@ -79,9 +79,11 @@ typedef enum {
     WGRAD_VARIANT_AUTO = 0,
     WGRAD_VARIANT_MFMA = 1,      /* MFMA implicit GEMM over flat K tiles, any shape, optional group merge */
     WGRAD_VARIANT_DEPTHWISE = 2, /* C/G = K/G = 1: channel-vector direct kernel */
-    WGRAD_VARIANT_ROWSLAB = 3    /* MFMA implicit GEMM over slabs of output rows, one filter row per
-                                    tile, X staged once per row (filter width 3 or 5, w-dilation 1,
+    WGRAD_VARIANT_ROWSLAB = 3,   /* MFMA implicit GEMM over slabs of output rows, one filter row per
+                                    tile, X staged once per row (filter width 1, 3 or 5, w-dilation 1,
                                     channel runs multiple of 32), optional group merge */
+    WGRAD_VARIANT_DGRAD = 4      /* backward data (wgrad_dgrad_plan only): MFMA implicit GEMM over
+                                    input positions, reduction over (tap, K/G) */
 } wgrad_variant;
 
 /* Overrides for tests and benchmarks; 0 in a field means "the plan decides".
@@ -165,6 +167,46 @@ int wgrad_run(const wgrad_plan_t* plan, const void* x, const void* dy, void* dw,
  */
 int wgrad_run_stage(const wgrad_plan_t* plan, int stage, const void* x, const void* dy, void* dw,
                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward data of the same convolution (rocm-libraries PR 11602, "add
+ * transpose load for bwd weight and bwd data": its dgrad part, which reads
+ * the weight tile K-outer; the direction itself is the adjoint of the forward
+ * convolution that the backward-weight pages define):
+ *
+ *   dX[n,di,hi,wi,g,c] = sum_{k,z,y,x} dY[n,do,ho,wo,g,k] * W[g,k,z,y,x,c]
+ *   over the (do, ho, wo) with do*stride_d - pad_lo_d + z*dilation_d = di
+ *   (likewise ho with y, wo with x) and 0 <= do < Do, 0 <= ho < Ho, 0 <= wo < Wo.
+ *
+ * Same wgrad_problem; in_dtype is the type of dY and W, out_dtype the type
+ * of dX (in_dtype or FP32). Layouts: dY [N][Do][Ho][Wo][K] (NDHWGK), W
+ * [K][Z][Y][X][C/G] (GKZYXC), dX [N][Di][Hi][Wi][C] (NDHWGC); 2D and 1D drop
+ * the leading axes as for wgrad. Computed as one GEMM per group with
+ * M = N*Di*Hi*Wi input positions, N = C/G and a reduction of length
+ * (K/G)*Z*Y*X; every dX element is written exactly once (positions no tap
+ * reaches get 0), so there is no workspace and no split of the reduction.
+ *
+ * wgrad_dgrad_plan: validation and errors as wgrad_plan. Overrides: split_k
+ * and group_merge must be 0 or 1, variant AUTO or DGRAD, tile 0 (auto) or a
+ * dgrad tile id (1: 128x32, 2: 128x64, 3: 128x128 positions x channels);
+ * anything else is WGRAD_ERR_UNSUPPORTED. wgrad_plan_query reports
+ * variant DGRAD, gemm_m/n/k as above and workspace_bytes 0.
+ * The plan is released with wgrad_plan_destroy; wgrad_run and
+ * wgrad_run_stage reject it (and wgrad_dgrad_run rejects backward-weight
+ * plans) with WGRAD_ERR_INVALID_ARG.
+ */
+int wgrad_dgrad_plan(const wgrad_problem* problem, const wgrad_overrides* overrides,
+                     int hip_device, wgrad_plan_t** out);
+
+/*
+ * Enqueue dX = dgrad(dY, W) on stream (NULL = the null stream) and return
+ * without synchronising. dy, w, dx are device pointers aligned to 16 bytes
+ * (dy and w may be NULL only when N = 0); dX is overwritten. One kernel, no
+ * atomics: the same plan on the same inputs gives the same bits.
+ * Errors: WGRAD_ERR_INVALID_ARG (NULL or misaligned pointer, wrong plan
+ * kind), WGRAD_ERR_HIP (launch failure).
+ */
+int wgrad_dgrad_run(const wgrad_plan_t* plan, const void* dy, const void* w, void* dx, void* stream);
 
 /* Fill *info with the plan's decisions. */
 int wgrad_plan_query(const wgrad_plan_t* plan, wgrad_plan_info* info);

@@ -1,0 +1,167 @@
+"""GPU parity of backward data (dgrad): the HIP kernel through the C ABI
+(wgrad_dgrad_plan / wgrad_dgrad_run) against the CPU oracle's dgrad on the
+same seeded dY and W.
+
+Bars, as for backward weight:
+* integer inputs in {-2..2}: every product and partial sum is an integer far
+  below 2^24, so the fp32 accumulation is exact in any order and dX must equal
+  RNE_out(oracle) bit for bit;
+* random inputs: |gpu - oracle| <= tau*sum|dY*W| + 1e-6 with tau = 2^-7 (bf16
+  out), 2^-10 (fp16 out), 1e-5 (fp32 out);
+* dX is prefilled with NaN and a guard band after it must stay NaN (every
+  element written, nothing past the end); two runs give the same bits.
+Every case compares every dX element (the oracle's dgrad finishes the
+largest shape here in a few seconds).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+gcb = pytest.importorskip("grouped_convolution_backward_amd")
+
+pytestmark = pytest.mark.gpu
+
+OUT_T = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+GUARD = 4096
+
+
+def to_dev(bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).reshape(-1).copy())
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
+
+
+def draw(cfg, dist, seeds=None):
+    s0, s1 = seeds or cfg.get("seeds", (11, 12))
+    dys = (cfg["N"], *oracle.out_len(cfg), cfg["K"])
+    return (workloads.draw(dys, cfg["in_dtype"], dist, s0 + 100),
+            workloads.draw(oracle.dw_shape(cfg), cfg["in_dtype"], dist, s1 + 100))
+
+
+def run_dgrad(cfg, dyb, wb, **ov):
+    p = gcb.DgradPlan(cfg, **ov)
+    out_dtype = cfg.get("out_dtype", cfg["in_dtype"])
+    dy = to_dev(dyb, cfg["in_dtype"])
+    w = to_dev(wb, cfg["in_dtype"])
+    n = int(np.prod(p.dx_shape()))
+    buf = torch.full((n + GUARD,), float("nan"), dtype=OUT_T[out_dtype], device="cuda")
+    dx = buf[:n]
+    print(f"[gpu] dgrad {cfg.get('name', '?')} {p.name}", flush=True)
+    p.run(dy, w, dx)
+    torch.cuda.synchronize()
+    assert np.all(np.isnan(buf[n:].float().cpu().numpy())), "kernel wrote past the end of dX"
+    if out_dtype == "fp32":
+        bits = dx.cpu().numpy().view(np.uint32)
+        vals = bits.view(np.float32).astype(np.float64)
+    else:
+        bits = dx.view(torch.int16).cpu().numpy().view(np.uint16)
+        vals = oracle.widen(bits, out_dtype)
+    return vals, bits, p
+
+
+def check_exact(cfg, bits, dx64):
+    out_dtype = cfg.get("out_dtype", cfg["in_dtype"])
+    want = dx64.reshape(-1).astype(np.float32).view(np.uint32) if out_dtype == "fp32" \
+        else oracle.round_to_bits(dx64.reshape(-1), out_dtype)
+    bad = np.nonzero(bits.reshape(-1) != want)[0]
+    assert bad.size == 0, f"{bad.size} of {want.size} elements differ, first at {bad[:5]}"
+
+
+def check_tol(cfg, vals, dx64, ab64):
+    out_dtype = cfg.get("out_dtype", cfg["in_dtype"])
+    v, d, a = vals.reshape(-1), dx64.reshape(-1), ab64.reshape(-1)
+    assert not np.any(np.isnan(v)), "dX has unwritten (NaN) elements"
+    bad = np.nonzero(oracle.violations(v, d, a, out_dtype))[0]
+    assert bad.size == 0, (f"{bad.size} elements outside tau*sum|dY*W|+1e-6, e.g. gpu={v[bad[:3]]} "
+                           f"ref={d[bad[:3]]}")
+
+
+ALL = {**workloads.CONFIGS, **workloads.WIDER}
+
+
+@pytest.mark.parametrize("name", list(ALL))
+def test_dgrad_configs_exact_integer(name):
+    cfg = ALL[name]
+    dyb, wb = draw(cfg, "int")
+    _, bits, _ = run_dgrad(cfg, dyb, wb)
+    dx64, _ = oracle.dgrad(cfg, dyb, wb)
+    check_exact(cfg, bits, dx64)
+
+
+@pytest.mark.parametrize("name", list(ALL))
+def test_dgrad_configs_random_within_tolerance(name):
+    cfg = ALL[name]
+    dyb, wb = draw(cfg, cfg["dist"])
+    vals, bits, _ = run_dgrad(cfg, dyb, wb)
+    dx64, ab64 = oracle.dgrad(cfg, dyb, wb)
+    check_tol(cfg, vals, dx64, ab64)
+    # same plan, same inputs: same bits
+    _, bits2, _ = run_dgrad(cfg, dyb, wb)
+    assert np.array_equal(bits, bits2)
+
+
+def prob(ndim, G, N, cpg, kpg, in_len, filt, stride, pad_lo, pad_hi, dil, dtype="bf16", out=None, name="edge"):
+    return {"name": name, "ndim": ndim, "G": G, "N": N, "C": G * cpg, "K": G * kpg, "in_len": tuple(in_len),
+            "filt_len": tuple(filt), "stride": tuple(stride), "dilation": tuple(dil),
+            "pad_lo": tuple(pad_lo), "pad_hi": tuple(pad_hi), "in_dtype": dtype, "out_dtype": out or dtype}
+
+
+# (ndim, G, N, C/G, K/G, in_len, filt, stride, pad_lo, pad_hi, dil, dtype, out)
+EDGE = [
+    # ragged M (positions not a multiple of 128), K/G not a multiple of 32, C/G = 40
+    (2, 1, 3, 40, 72, (13, 11), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+    # strided and dilated, asymmetric pads, fp16 in, fp32 out
+    (2, 2, 2, 24, 48, (17, 15), (3, 5), (2, 3), (2, 1), (0, 2), (2, 1), "fp16", "fp32"),
+    # odd channel runs: 2-element then 1-element loads
+    (2, 3, 2, 6, 10, (9, 8), (3, 3), (1, 2), (1, 1), (1, 0), (1, 1), "bf16", None),
+    (2, 2, 1, 3, 5, (7, 9), (2, 3), (1, 1), (0, 1), (1, 1), (1, 2), "bf16", "fp32"),
+    # wide channel runs: two 128-wide tiles along C/G
+    (2, 1, 2, 200, 64, (10, 12), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+    # grouped, C/G = K/G = 8; depthwise C/G = K/G = 1
+    (2, 16, 4, 8, 8, (14, 14), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+    (2, 64, 2, 1, 1, (12, 12), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+    # 1x1 with stride 2: three quarters of dX receive no tap and must be 0
+    (2, 1, 2, 64, 32, (12, 10), (1, 1), (2, 2), (0, 0), (0, 0), (1, 1), "bf16", None),
+    # kernel larger than the stride gaps, pads larger than the dilated filter reach
+    (2, 1, 1, 32, 32, (6, 7), (5, 5), (3, 2), (4, 3), (4, 3), (1, 1), "fp16", None),
+    # 1D and 3D
+    (1, 4, 3, 16, 24, (37,), (5,), (2,), (2,), (1,), (1,), "bf16", None),
+    (3, 2, 2, 16, 32, (5, 6, 7), (3, 3, 3), (1, 2, 1), (1, 1, 1), (1, 0, 1), (1, 1, 2), "bf16", None),
+    (3, 1, 1, 8, 8, (3, 4, 5), (2, 1, 3), (2, 1, 1), (0, 0, 1), (1, 0, 1), (1, 1, 1), "fp16", "fp32"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(EDGE)))
+def test_dgrad_edge_shapes(i):
+    cfg = prob(*EDGE[i], name=f"edge{i}")
+    dyb, wb = draw(cfg, "int", (300 + i, 400 + i))
+    _, bits, _ = run_dgrad(cfg, dyb, wb)
+    dx64, _ = oracle.dgrad(cfg, dyb, wb)
+    check_exact(cfg, bits, dx64)
+    dyb, wb = draw(cfg, "uniform", (500 + i, 600 + i))
+    vals, _, _ = run_dgrad(cfg, dyb, wb)
+    dx64, ab64 = oracle.dgrad(cfg, dyb, wb)
+    check_tol(cfg, vals, dx64, ab64)
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3])
+def test_dgrad_every_tile(tile):
+    cfg = prob(2, 2, 2, 72, 40, (11, 13), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), name=f"tile{tile}")
+    dyb, wb = draw(cfg, "int", (71, 72))
+    _, bits, p = run_dgrad(cfg, dyb, wb, tile=tile)
+    assert p.info["tile"] == tile
+    dx64, _ = oracle.dgrad(cfg, dyb, wb)
+    check_exact(cfg, bits, dx64)
+
+
+def test_dgrad_empty_batch():
+    cfg = prob(2, 1, 0, 16, 16, (8, 8), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1))
+    p = gcb.DgradPlan(cfg)
+    assert p.info["grid_main"] == 0
+    e = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(p.w_shape(), dtype=torch.bfloat16, device="cuda")
+    p.run(e, w, e)
+    torch.cuda.synchronize()

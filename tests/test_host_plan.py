@@ -307,3 +307,61 @@ def test_3d_invalid_problems_rejected():
     _expect(gcb.ERR_INVALID_ARG, prob3(1, 1, 8, 8, (2, 4, 4), (3, 1, 1)))          # empty depth output
     _expect(gcb.ERR_INVALID_ARG, prob3(1, 1, 8, 8, (4, 4, 4), (1, 1, 1), stride=(0, 1, 1)))
     _expect(gcb.ERR_INVALID_ARG, dict(prob3(1, 1, 8, 8, (4, 4, 4), (1, 1, 1)), ndim=4))
+
+
+def dplan(cfg, **kw):
+    return gcb.DgradPlan(cfg, hip_device=-1, **kw)
+
+
+def test_dgrad_plans_sizes_and_tiles():
+    import oracle
+    cfg = workloads.CONFIGS["c2"]
+    p = dplan(cfg)
+    info = p.info
+    assert info["variant"] == gcb.VARIANT_DGRAD
+    assert info["gemm_m"] == 32 * 56 * 56 and info["gemm_n"] == 64 and info["gemm_k"] == 64 * 9
+    assert info["split_k"] == 1 and info["workspace_bytes"] == 0 and info["grid_reduce"] == 0
+    assert (info["tile_m"], info["tile_n"], info["tile_k"]) == (128, 64, 32)
+    assert info["grid_main"] == (32 * 56 * 56 + 127) // 128
+    assert info["vector_width"] == 8 and p.name.startswith("dgrad_mfma_bf16")
+    # grouped: one grid slice per group; odd channel runs narrow the loads
+    g = prob3(4, 1, 4 * 6, 4 * 10, (3, 5, 7), (2, 3, 3), stride=(1, 2, 1), pad=(0, 1, 1))
+    p = dplan(g)
+    assert p.info["vector_width"] == 2 and p.info["tile_n"] == 32
+    assert p.info["grid_main"] == ((3 * 5 * 7 + 127) // 128) * 4
+    assert p.info["out_len"] == oracle.out_len(g)
+    # explicit tiles; 128-wide channel tiles for wide groups
+    wide = dict(cfg, C=256)
+    assert dplan(wide).info["tile_n"] == 128
+    assert dplan(wide, tile=2).info["tile_n"] == 64
+    # the fp16 strided shape, fp32 output
+    p = dplan(dict(workloads.CONFIGS["c3"], out_dtype="fp32"))
+    assert p.info["gemm_m"] == 16 * 56 * 56 and p.info["gemm_k"] == 200 * 9 and "fp16" in p.name
+
+
+def test_dgrad_plan_rejections_and_plan_kinds():
+    lib = gcb.load_library()
+    cfg = workloads.CONFIGS["c2"]
+    for kw in ({"split_k": 2}, {"group_merge": 2}, {"variant": gcb.VARIANT_MFMA}, {"tile": 9}):
+        with pytest.raises(gcb.WgradError) as e:
+            dplan(cfg, **kw)
+        assert e.value.code == gcb.ERR_UNSUPPORTED
+    with pytest.raises(gcb.WgradError) as e:
+        plan(cfg, variant=gcb.VARIANT_DGRAD)
+    assert e.value.code == gcb.ERR_UNSUPPORTED
+    with pytest.raises(gcb.WgradError) as e:
+        dplan(dict(cfg, G=2, C=63))   # C not a multiple of G
+    assert e.value.code == gcb.ERR_INVALID_ARG
+    d, w = dplan(cfg), plan(cfg)
+    # each run entry point refuses the other direction's plan
+    assert lib.wgrad_dgrad_run(w.handle, 16, 16, 16, None) == gcb.ERR_INVALID_ARG
+    assert "backward-data" in gcb.wgrad_last_error()
+    assert lib.wgrad_run(d.handle, 16, 16, 16, None, 0, None) == gcb.ERR_INVALID_ARG
+    assert lib.wgrad_dgrad_run(None, 16, 16, 16, None) == gcb.ERR_INVALID_ARG
+    assert lib.wgrad_dgrad_run(d.handle, 16, 16, None, None) == gcb.ERR_INVALID_ARG
+    assert lib.wgrad_dgrad_run(d.handle, 16, 24, 16, None) == gcb.ERR_INVALID_ARG
+    assert "aligned" in gcb.wgrad_last_error()
+    # an empty batch enqueues nothing and accepts NULL pointers
+    e = dplan(dict(cfg, N=0))
+    assert e.info["grid_main"] == 0
+    assert lib.wgrad_dgrad_run(e.handle, None, None, None, None) == gcb.OK
