@@ -1,4 +1,5 @@
-"""Benchmark of grouped convolution backward-weight (wgrad) on one MI355X.
+"""Benchmark of grouped convolution backward-weight (wgrad) on one MI355X,
+with backward-data (dgrad) rows beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs c2,c5,...]
 
@@ -7,7 +8,8 @@ convert kernel when the plan splits the reduction) over one batch of
 synthetic, seeded input already resident in HBM. The headline workload is
 the dense split-K shape (G=1 N=32 56x56 C=64 K=64 3x3 s1 p1, bf16): value =
 its TFLOP/s over exactly K timed steps. Every other configuration is timed
-the same way and reported under "per_config".
+the same way and reported under "per_config"; "dgrad:<name>" rows time
+backward data (dX from dY and W) of that workload's convolution.
 
 Honest memory: each configuration cycles through enough copies of its inputs
 (> 512 MB in total) that no step finds its inputs in the 256 MB MALL left
@@ -204,6 +206,53 @@ class Case:
         }
 
 
+class DgradCase(Case):
+    """Backward data of a workload's convolution: dX = dgrad(dY, W), one
+    kernel per step. FLOPs as for wgrad (the same multiply-adds); bytes =
+    |dY| + |W| + |dX|, each once."""
+
+    def __init__(self, torch, gcb, workloads, name, cfg, overrides=None):
+        import numpy as np
+        self.name, self.cfg = name, cfg
+        self.torch = torch
+        self.plan = gcb.DgradPlan(cfg, **(overrides or {}))
+        dt = torch.bfloat16 if cfg["in_dtype"] == "bf16" else torch.float16
+        out_t = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[cfg["out_dtype"]]
+        s0, s1 = cfg["seeds"]
+        dy_bits = workloads.draw(self.plan.dy_shape(), cfg["in_dtype"], cfg["dist"], s0 + 100)
+        w_bits = workloads.draw(self.plan.w_shape(), cfg["in_dtype"], cfg["dist"], s1 + 100)
+        dy0 = torch.from_numpy(dy_bits.view(np.int16).reshape(-1).copy()).view(dt).cuda()
+        self.w = torch.from_numpy(w_bits.view(np.int16).reshape(-1).copy()).view(dt).cuda()
+        self.nsets = max(2, min(64, math.ceil(ROTATE_BYTES / max(1, dy0.numel() * 2))))
+        self.dys = [dy0] + [dy0.clone() for _ in range(self.nsets - 1)]
+        self.dx = torch.empty(self.plan.dx_shape(), dtype=out_t, device="cuda")
+        self.ws = None
+        flops, _ = algorithmic(cfg, gcb.Plan(cfg, hip_device=-1).info)
+        out_bytes = 4 if cfg["out_dtype"] == "fp32" else 2
+        self.flops = flops
+        self.bytes = 2 * (dy0.numel() + self.w.numel()) + out_bytes * self.dx.numel()
+
+    def step(self, i, stage=0):
+        self.plan.run(self.dys[i % self.nsets], self.w, self.dx)
+
+    def kernel_times(self, reps=4):
+        torch = self.torch
+        glen = self.graph_len()
+        g = self.capture(glen)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            g.replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(reps):
+                g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / (reps * glen), 0.0
+
+
 def cpu_baseline(workloads, cfg):
     import oracle
     x_bits, dy_bits = workloads.inputs(cfg)
@@ -225,7 +274,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="c1,c2,c3,c4a,c4b,c5,pw,c3d")
+    ap.add_argument("--configs", default="c1,c2,c3,c4a,c4b,c5,pw,c3d,dgrad:c2,dgrad:c3d",
+                    help="workload names; dgrad:<name> times backward data of that workload")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (for profilers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-merge", action="store_true", help="also time the depthwise shape over Gm and S")
@@ -254,8 +304,10 @@ def main():
     per = {}
     head = None
     for name in names:
-        cfg = workloads.get(name)
-        case = Case(torch, gcb, workloads, name, cfg)
+        if name.startswith("dgrad:"):
+            case = DgradCase(torch, gcb, workloads, name, workloads.get(name.split(":", 1)[1]))
+        else:
+            case = Case(torch, gcb, workloads, name, workloads.get(name))
         sec = case.time_steps(args.steps, args.warmup, use_graphs=not args.eager)
         t_main, t_red = case.kernel_times()
         per[name] = case.row(sec, t_main, t_red)

@@ -85,15 +85,24 @@ int wgrad_dgrad_run(const wgrad_plan_t* plan, const void* dy, const void* w, voi
     if (!plan) return set_error(WGRAD_ERR_INVALID_ARG, "plan is NULL");
     const wgrad::Plan& P = plan->plan;
     if (P.op != wgrad::OP_DGRAD) return set_error(WGRAD_ERR_INVALID_ARG, "not a backward-data plan");
-    if (P.dg.total_wg == 0) return WGRAD_OK;   // N = 0: dX is empty
+    if ((P.dg_dw ? P.dgdw.total_wg : P.dg.total_wg) == 0) return WGRAD_OK;   // N = 0: dX is empty
     if (!dx || !dy || !w) return set_error(WGRAD_ERR_INVALID_ARG, "dy, w and dx must not be NULL");
     if (!aligned16(dy) || !aligned16(w) || !aligned16(dx))
         return set_error(WGRAD_ERR_INVALID_ARG, "dy, w and dx must be 16-byte aligned");
-    wgrad::DgradArgs a = P.dg;
-    a.dy = static_cast<const uint16_t*>(dy);
-    a.w = static_cast<const uint16_t*>(w);
-    a.dx = dx;
-    const int e = wgrad::launch_dgrad(P, a, stream);
+    int e;
+    if (P.dg_dw) {
+        wgrad::DgradDwArgs a = P.dgdw;
+        a.dy = static_cast<const uint16_t*>(dy);
+        a.w = static_cast<const uint16_t*>(w);
+        a.dx = dx;
+        e = wgrad::launch_dgrad_dw(P, a, stream);
+    } else {
+        wgrad::DgradArgs a = P.dg;
+        a.dy = static_cast<const uint16_t*>(dy);
+        a.w = static_cast<const uint16_t*>(w);
+        a.dx = dx;
+        e = wgrad::launch_dgrad(P, a, stream);
+    }
     if (e != hipSuccess)
         return set_error(WGRAD_ERR_HIP, std::string("dgrad kernel launch: ") + hipGetErrorString((hipError_t)e));
     return WGRAD_OK;

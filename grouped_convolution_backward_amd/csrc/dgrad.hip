@@ -207,7 +207,131 @@ int launch_t(const Plan& plan, const DgradArgs& a, hipStream_t s) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Depthwise backward data (C/G = K/G = 1): no contraction over channels, so
+// no MFMA. dX[n,d,h,w,c] = sum over taps of dY at the output position the tap
+// maps back to, times W[c][tap]: a stencil per channel. A lane owns 8
+// channels (one 16-byte dY load per tap and position) of a strip of
+// kDgDwStrip input positions along w; lanes of a wave run along the channels
+// first, so each dY load instruction of a wave reads whole contiguous pixels.
+// The workgroup's weights sit in LDS as fp32 [tap][channel], read back as two
+// 16-byte reads per tap. Accumulation in fp32 in tap order (z, y, x).
+__device__ __forceinline__ void widen8(const u32x4& v, float* f, bool f16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t u = v[i];
+        if (f16) {
+            f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+            f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+        } else {
+            f[2 * i] = __uint_as_float(u << 16);
+            f[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ void store8(void* out, int mode, int64_t e, const float* v) {
+    if (mode == OUT_FP32) {
+        float* o = static_cast<float*>(out) + e;
+        *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        return;
+    }
+    u32x4 p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t lo, hi;
+        if (mode == OUT_FP16) {
+            lo = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i]);
+            hi = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1]);
+        } else {
+            lo = f32_to_bf16(v[2 * i]);
+            hi = f32_to_bf16(v[2 * i + 1]);
+        }
+        p[i] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e) = p;
+}
+
+template <bool F16>
+__global__ __launch_bounds__(256) void dgrad_dw_kernel(const DgradDwArgs a) {
+    extern __shared__ __attribute__((aligned(16))) float wlds[];   // [taps][cb]
+    const int tid = threadIdx.x;
+    const int L = xcd_logical_id(blockIdx.x, a.total_wg);
+    const int sg = L % a.sgroups, cbk = L / a.sgroups;
+    const int c_base = cbk * a.cb;
+    // stage the block's weights, transposed to [tap][channel]
+    for (int e = tid; e < a.cb * a.taps; e += 256) {
+        const int cl = e / a.taps, t = e - cl * a.taps;
+        const uint16_t u = a.w[(int64_t)(c_base + cl) * a.taps + t];
+        wlds[t * a.cb + cl] = F16 ? (float)__builtin_bit_cast(_Float16, u) : __uint_as_float((uint32_t)u << 16);
+    }
+    __syncthreads();
+    const int cvl = tid % a.cbv, sl = tid / a.cbv;
+    const int s = sg * a.spw + sl;
+    if (sl >= a.spw || s >= a.strips) return;   // no barrier follows
+    int r = s / a.nstrip;
+    const int w0 = (s - r * a.nstrip) * kDgDwStrip;
+    const int h = r % a.Hi;
+    r /= a.Hi;
+    const int d = r % a.Di;
+    const int n = r / a.Di;
+    const int c = c_base + cvl * 8;
+    auto out_coord = [](int i, int pad, int tdil, int len, MagicU32 ms, int stride) {
+        const int num = i + pad - tdil;
+        if (num < 0) return -1;
+        const int q = (int)magic_div((uint32_t)num, ms);
+        if (q * stride != num || q >= len) return -1;
+        return q;
+    };
+    float acc[kDgDwStrip][8];
+#pragma unroll
+    for (int j = 0; j < kDgDwStrip; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[j][i] = 0.f;
+    for (int z = 0; z < a.Zf; ++z) {
+        const int od = out_coord(d, a.pd, z * a.dd, a.Do, a.msd, a.sd);
+        if (od < 0) continue;
+        for (int y = 0; y < a.Yf; ++y) {
+            const int oh = out_coord(h, a.ph, y * a.dh, a.Ho, a.msh, a.sh);
+            if (oh < 0) continue;
+            const int row = (n * a.Do + od) * a.Ho + oh;
+            const int tbase = (z * a.Yf + y) * a.Xf;
+            for (int x = 0; x < a.Xf; ++x) {
+                const float* wp = wlds + (tbase + x) * a.cb + cvl * 8;
+                const f32x4 wa = *reinterpret_cast<const f32x4*>(wp);
+                const f32x4 wb = *reinterpret_cast<const f32x4*>(wp + 4);
+                const float wv[8] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3]};
+#pragma unroll
+                for (int j = 0; j < kDgDwStrip; ++j) {
+                    const int ow = w0 + j < a.Wi ? out_coord(w0 + j, a.pw, x * a.dw, a.Wo, a.msw, a.sw) : -1;
+                    if (ow < 0) continue;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(a.dy + (int64_t)(row * a.Wo + ow) * a.C + c);
+                    float f[8];
+                    widen8(v, f, F16);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[j][i] = __builtin_fmaf(f[i], wv[i], acc[j][i]);
+                }
+            }
+        }
+    }
+    const int64_t pix = (((int64_t)n * a.Di + d) * a.Hi + h) * a.Wi;
+#pragma unroll
+    for (int j = 0; j < kDgDwStrip; ++j)
+        if (w0 + j < a.Wi) store8(a.dx, a.out_mode, (pix + w0 + j) * a.C + c, acc[j]);
+}
+
 }  // namespace
+
+int launch_dgrad_dw(const Plan& plan, const DgradDwArgs& a, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t lds = (size_t)a.taps * a.cb * 4;
+    if (plan.in_f16)
+        hipLaunchKernelGGL(dgrad_dw_kernel<true>, dim3(a.total_wg), dim3(256), lds, s, a);
+    else
+        hipLaunchKernelGGL(dgrad_dw_kernel<false>, dim3(a.total_wg), dim3(256), lds, s, a);
+    return (int)hipGetLastError();
+}
 
 int launch_dgrad(const Plan& plan, const DgradArgs& a, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -533,6 +533,57 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     const int64_t cpg = p.C / p.G, kpg = p.K / p.G;
     const int64_t taps = g.Z * g.Y * g.X;
     const int64_t M = p.N * g.Di * g.Hi * g.Wi;
+    // depthwise direct kernel (tile id 4): channel block cb = the largest
+    // power of two <= 512 dividing C whose fp32 weights fit the LDS budget
+    int dw_cb = 0;
+    if (cpg == 1 && kpg == 1 && p.C % 8 == 0)
+        for (int cb = 512; cb >= 8 && !dw_cb; cb >>= 1)
+            if (p.C % cb == 0 && taps * cb * 4 <= kDgDwLdsMax) dw_cb = cb;
+    if (o.tile == 4 && !dw_cb)
+        return fail(msg, U, "the depthwise dgrad kernel needs C/G = K/G = 1, C %% 8 == 0 and at most %d taps",
+                    kDgDwLdsMax / 32);
+    if (dw_cb && (o.tile == 0 || o.tile == 4)) {
+        out = Plan{};
+        out.op = OP_DGRAD;
+        out.prob = p;
+        out.in_f16 = p.in_dtype == WGRAD_FP16;
+        out.variant = WGRAD_VARIANT_DGRAD;
+        out.dg_dw = 1;
+        DgradDwArgs& a = out.dgdw;
+        a = DgradDwArgs{};
+        a.C = (int32_t)p.C;
+        a.Di = (int32_t)g.Di; a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi;
+        a.Do = (int32_t)g.Do; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo;
+        a.Zf = (int32_t)g.Z; a.Yf = (int32_t)g.Y; a.Xf = (int32_t)g.X; a.taps = (int32_t)taps;
+        a.sd = (int32_t)g.sd; a.sh = (int32_t)g.sh; a.sw = (int32_t)g.sw;
+        a.dd = (int32_t)g.dd; a.dh = (int32_t)g.dh; a.dw = (int32_t)g.dw;
+        a.pd = (int32_t)g.pd; a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
+        a.cb = dw_cb; a.cbv = dw_cb / 8; a.spw = 256 / a.cbv;
+        a.nstrip = (int32_t)ceil_div(g.Wi, kDgDwStrip);
+        const int64_t strips = p.N * g.Di * g.Hi * a.nstrip;
+        const int64_t cblocks = p.C / dw_cb, sgroups = ceil_div(strips, a.spw);
+        if (strips > kMax31 || cblocks * sgroups > kMax31) return fail(msg, U, "grid too large");
+        a.strips = (int32_t)strips;
+        a.cblocks = (int32_t)cblocks; a.sgroups = (int32_t)sgroups; a.total_wg = (int32_t)(cblocks * sgroups);
+        a.out_mode = p.out_dtype == WGRAD_BF16 ? OUT_BF16 : p.out_dtype == WGRAD_FP16 ? OUT_FP16 : OUT_FP32;
+        a.msd = make_magic((uint32_t)g.sd); a.msh = make_magic((uint32_t)g.sh); a.msw = make_magic((uint32_t)g.sw);
+        wgrad_plan_info& info = out.info;
+        {
+            const int64_t all[3] = {g.Do, g.Ho, g.Wo};
+            for (int i = 0; i < 3; ++i) info.out_len[i] = i < p.ndim ? all[3 - p.ndim + i] : 0;
+        }
+        info.gemm_m = M; info.gemm_n = 1; info.gemm_k = taps;
+        info.variant = WGRAD_VARIANT_DGRAD;
+        info.tile = 4;
+        info.tile_m = kDgDwStrip * a.spw; info.tile_n = dw_cb; info.tile_k = (int32_t)taps;
+        info.split_k = 1; info.group_merge = 1; info.vector_width = 8;
+        info.grid_main = a.total_wg;
+        info.num_cus = dev.num_cus;
+        char name[160];
+        snprintf(name, sizeof name, "dgrad_dw_%s_cb%d_s%d", out.in_f16 ? "fp16" : "bf16", dw_cb, kDgDwStrip);
+        out.name = name;
+        return WGRAD_OK;
+    }
     int V = 8;
     while (V > 1 && (kpg % V || cpg % V || p.K % V || p.C % V)) V >>= 1;
     int tile_id = o.tile;

@@ -198,6 +198,24 @@ struct DgradArgs {
     int32_t tiles_m, tiles_n, total_wg, out_mode;
     MagicU32 mWi, mHi, mDi, msd, msh, msw;
 };
+// Depthwise backward data (C/G = K/G = 1, C % 8 == 0): a lane owns 8
+// channels of a 4-wide strip of one input row; a workgroup covers a channel
+// block of cb channels (weights staged in LDS as fp32 [tap][channel]) and
+// 256 / (cb / 8) strips.
+constexpr int kDgDwStrip = 4;
+constexpr int kDgDwLdsMax = 64 * 1024;
+struct DgradDwArgs {
+    const uint16_t* dy;
+    const uint16_t* w;
+    void* dx;
+    int32_t C, Di, Hi, Wi, Do, Ho, Wo;
+    int32_t Zf, Yf, Xf, taps;
+    int32_t sd, sh, sw, dd, dh, dw, pd, ph, pw;
+    int32_t cb, cbv, spw;          // channels per block, channel vectors per block (cb/8), strips per workgroup
+    int32_t nstrip, strips;        // strips per input row, N*Di*Hi*nstrip
+    int32_t cblocks, sgroups, total_wg, out_mode;
+    MagicU32 msd, msh, msw;
+};
 // dgrad tiles: id -> (BM, BN); 4 waves each
 struct DgradTile {
     int id, bm, bn;
@@ -254,6 +272,8 @@ struct Plan {
     int dw_tile_y, dw_tile_x;   // depthwise kernel filter instance
     DgradArgs dg;
     int dg_bn, dg_v;             // dgrad tile width and load vector width
+    DgradDwArgs dgdw;
+    int dg_dw;                   // 1: the depthwise dgrad kernel
     std::string name;
 };
 
@@ -271,5 +291,6 @@ int launch_depthwise2(const Plan& plan, const Dw2Args& a, void* stream);
 int launch_depthwise3(const Plan& plan, const Dw3Args& a, void* stream);
 int launch_reduce(const ReduceArgs& a, int64_t grid, void* stream);
 int launch_dgrad(const Plan& plan, const DgradArgs& a, void* stream);   // dgrad.hip
+int launch_dgrad_dw(const Plan& plan, const DgradDwArgs& a, void* stream);
 
 }  // namespace wgrad

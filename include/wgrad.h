@@ -188,7 +188,9 @@ int wgrad_run_stage(const wgrad_plan_t* plan, int stage, const void* x, const vo
  *
  * wgrad_dgrad_plan: validation and errors as wgrad_plan. Overrides: split_k
  * and group_merge must be 0 or 1, variant AUTO or DGRAD, tile 0 (auto) or a
- * dgrad tile id (1: 128x32, 2: 128x64, 3: 128x128 positions x channels);
+ * dgrad kernel id: 1, 2, 3 = the MFMA kernel with 128x32, 128x64, 128x128
+ * (positions x channels) tiles; 4 = the depthwise direct kernel (C/G = K/G
+ * = 1, C % 8 == 0, at most 2048 taps), which auto picks for such shapes;
  * anything else is WGRAD_ERR_UNSUPPORTED. wgrad_plan_query reports
  * variant DGRAD, gemm_m/n/k as above and workspace_bytes 0.
  * The plan is released with wgrad_plan_destroy; wgrad_run and

@@ -157,6 +157,35 @@ def test_dgrad_every_tile(tile):
     check_exact(cfg, bits, dx64)
 
 
+# depthwise direct kernel (C/G = K/G = 1)
+DW = [
+    (2, 512, 2, 1, 1, (13, 11), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+    (2, 24, 2, 1, 1, (9, 10), (5, 5), (2, 2), (2, 1), (1, 2), (1, 1), "fp16", "fp32"),
+    (2, 64, 1, 1, 1, (10, 9), (3, 3), (1, 1), (2, 2), (2, 2), (2, 2), "bf16", None),
+    (1, 40, 3, 1, 1, (50,), (7,), (3,), (3,), (3,), (1,), "bf16", None),
+    (3, 32, 1, 1, 1, (5, 6, 7), (3, 3, 3), (2, 1, 1), (1, 1, 1), (1, 1, 1), (1, 1, 1), "fp16", None),
+    (2, 16, 1, 1, 1, (3, 3), (1, 1), (2, 2), (0, 0), (0, 0), (1, 1), "bf16", None),
+    (2, 1024, 1, 1, 1, (6, 5), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", "fp32"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DW)))
+def test_dgrad_depthwise_kernel(i):
+    cfg = prob(*DW[i], name=f"dw{i}")
+    dyb, wb = draw(cfg, "int", (700 + i, 800 + i))
+    _, bits, p = run_dgrad(cfg, dyb, wb)
+    assert p.info["tile"] == 4 and p.name.startswith("dgrad_dw")
+    dx64, _ = oracle.dgrad(cfg, dyb, wb)
+    check_exact(cfg, bits, dx64)
+    # the MFMA kernel on the same shape gives the same (exact) bits
+    _, bits_mfma, p1 = run_dgrad(cfg, dyb, wb, tile=1)
+    assert p1.info["tile"] == 1 and np.array_equal(bits, bits_mfma)
+    dyb, wb = draw(cfg, "uniform", (900 + i, 1000 + i))
+    vals, _, _ = run_dgrad(cfg, dyb, wb)
+    dx64, ab64 = oracle.dgrad(cfg, dyb, wb)
+    check_tol(cfg, vals, dx64, ab64)
+
+
 def test_dgrad_empty_batch():
     cfg = prob(2, 1, 0, 16, 16, (8, 8), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1))
     p = gcb.DgradPlan(cfg)

@@ -334,6 +334,15 @@ def test_dgrad_plans_sizes_and_tiles():
     wide = dict(cfg, C=256)
     assert dplan(wide).info["tile_n"] == 128
     assert dplan(wide, tile=2).info["tile_n"] == 64
+    # depthwise shapes take the direct kernel; forcing it elsewhere is unsupported
+    p = dplan(workloads.CONFIGS["c5"])
+    assert p.info["tile"] == 4 and p.name.startswith("dgrad_dw") and p.info["tile_n"] == 512
+    assert p.info["grid_main"] == (16 * 56 * 14 + 3) // 4
+    assert dplan(workloads.CONFIGS["c5"], tile=1).info["tile"] == 1
+    assert dplan(dict(workloads.CONFIGS["c5"], G=24, C=24, K=24)).info["tile_n"] == 8
+    with pytest.raises(gcb.WgradError) as e:
+        dplan(cfg, tile=4)
+    assert e.value.code == gcb.ERR_UNSUPPORTED
     # the fp16 strided shape, fp32 output
     p = dplan(dict(workloads.CONFIGS["c3"], out_dtype="fp32"))
     assert p.info["gemm_m"] == 16 * 56 * 56 and p.info["gemm_k"] == 200 * 9 and "fp16" in p.name
