@@ -17,7 +17,11 @@
 // contiguous run of dY channels), which is already the MFMA operand layout,
 // so a plain 16-byte LDS read serves it.
 // Every dX element is written once: no workspace and no split of the
-// reduction, so the result is deterministic.
+// reduction, so the result is deterministic. Small groups are merged Gm at a
+// time into one block-diagonal GEMM (the group merging that rocm-libraries
+// PR 12359 applies to backward weight): the A tile is then a contiguous run
+// of Gm*K/G dY channels and the B tile holds zeros where a row's group
+// differs from a column's.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -50,7 +54,7 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     const int mt = L % a.tiles_m;
     const int rest = L / a.tiles_m;
     const int nt = rest % a.tiles_n;
-    const int g = rest / a.tiles_n;
+    const int gb = rest / a.tiles_n;   // block of Gm merged groups
     const int m0 = mt * BM, c0 = nt * BN;
 
     // A rows this thread loads: position m -> (n, di, hi, wi)
@@ -71,8 +75,8 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
         a_d[p] = (int)(q2 - q3 * (uint32_t)a.Di);
         a_n[p] = (int)q3;
     }
-    const uint16_t* dy_g = a.dy + g * a.kpg;
-    const uint16_t* w_g = a.w + (int64_t)g * a.kpg * a.taps * a.cpg;
+    const uint16_t* dy_g = a.dy + gb * a.gkpg;
+    const uint16_t* w_g = a.w + (int64_t)gb * a.gkpg * a.taps * a.cpg;
 
     // output coordinate along one axis whose tap offset reaches input i:
     // (i + pad - t*dil) / stride when exact and in range, else -1
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
         for (int p = 0; p < A_LOADS; ++p) {
             VT v = 0;
             const int k = k0 + a_kv;
-            if (a_in[p] && k < a.kpg) {
+            if (a_in[p] && k < a.gkpg) {
                 const int od = out_coord(a_d[p], a.pd, tz * a.dd, a.Do, a.msd, a.sd);
                 const int oh = out_coord(a_h[p], a.ph, ty * a.dh, a.Ho, a.msh, a.sh);
                 const int ow = out_coord(a_w[p], a.pw, tx * a.dw, a.Wo, a.msw, a.sw);
@@ -108,9 +112,13 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
             VT v = 0;
             const int idx = tid + p * 256;
             const int row = idx / BVR, cv = (idx - row * BVR) * V;
-            const int k = k0 + row;
-            if (row < BK && k < a.kpg && c0 + cv < a.cpg)
-                v = *reinterpret_cast<const VT*>(w_g + ((int64_t)k * a.taps + t) * a.cpg + c0 + cv);
+            const int k = k0 + row, c = c0 + cv;
+            if (row < BK && k < a.gkpg && c < a.gcpg) {
+                // block diagonal: row k (group k/kpg) meets column c (group c/cpg)
+                const int gc = (int)magic_div((uint32_t)c, a.mcpg);
+                if ((int)magic_div((uint32_t)k, a.mkpg) == gc)
+                    v = *reinterpret_cast<const VT*>(w_g + ((int64_t)k * a.taps + t) * a.cpg + c - gc * a.cpg);
+            }
             rb[p] = v;
         }
     };
@@ -169,17 +177,17 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
         }
     }
 
-    // ---- epilogue: element (m, c) of the tile is dX[m][g*cpg + c]
+    // ---- epilogue: element (m, c) of the tile is dX[m][gb*gcpg + c]
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int c = c0 + wn0 + j * 32 + (lane & 31);
-        if (c >= a.cpg) continue;
+        if (c >= a.gcpg) continue;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int m = m0 + wm0 + i * 32 + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
-                if (m < a.M) store_out(a.dx, a.out_mode, (int64_t)m * a.Ctot + g * a.cpg + c, acc[i][j][v]);
+                if (m < a.M) store_out(a.dx, a.out_mode, (int64_t)m * a.Ctot + gb * a.gcpg + c, acc[i][j][v]);
             }
     }
 }

@@ -527,7 +527,8 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     if (o.split_k < 0 || o.group_merge < 0 || o.variant < 0 || o.tile < 0)
         return fail(msg, WGRAD_ERR_INVALID_ARG, "overrides must be >= 0");
     if (o.split_k > 1) return fail(msg, U, "backward data does not split its reduction");
-    if (o.group_merge > 1) return fail(msg, U, "backward data does not merge groups");
+    if (o.group_merge && (!is_pow2(o.group_merge) || p.G % o.group_merge))
+        return fail(msg, U, "group_merge %d must be a power of two dividing G = %lld", o.group_merge, (long long)p.G);
     if (o.variant != WGRAD_VARIANT_AUTO && o.variant != WGRAD_VARIANT_DGRAD)
         return fail(msg, U, "backward data plans use the DGRAD variant only");
     const int64_t cpg = p.C / p.G, kpg = p.K / p.G;
@@ -539,10 +540,11 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     if (cpg == 1 && kpg == 1 && p.C % 8 == 0)
         for (int cb = 512; cb >= 8 && !dw_cb; cb >>= 1)
             if (p.C % cb == 0 && taps * cb * 4 <= kDgDwLdsMax) dw_cb = cb;
+    if (o.tile == 4 && o.group_merge > 1) return fail(msg, U, "the depthwise dgrad kernel does not merge groups");
     if (o.tile == 4 && !dw_cb)
         return fail(msg, U, "the depthwise dgrad kernel needs C/G = K/G = 1, C %% 8 == 0 and at most %d taps",
                     kDgDwLdsMax / 32);
-    if (dw_cb && (o.tile == 0 || o.tile == 4)) {
+    if (dw_cb && (o.tile == 4 || (o.tile == 0 && o.group_merge <= 1))) {
         out = Plan{};
         out.op = OP_DGRAD;
         out.prob = p;
@@ -584,19 +586,27 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
         out.name = name;
         return WGRAD_OK;
     }
+    // merge adjacent groups until both merged runs fill the 32-wide MFMA
+    // edges (at most 8: the block-diagonal GEMM does Gm times the useful work)
+    int64_t Gm = o.group_merge;
+    if (!Gm) {
+        Gm = 1;
+        while (Gm * 2 <= 8 && p.G % (Gm * 2) == 0 && (Gm * cpg < 32 || Gm * kpg < 32)) Gm *= 2;
+    }
+    const int64_t gkpg = Gm * kpg, gcpg = Gm * cpg;
     int V = 8;
     while (V > 1 && (kpg % V || cpg % V || p.K % V || p.C % V)) V >>= 1;
     int tile_id = o.tile;
     if (!tile_id) {
         const int64_t tm = ceil_div(M, 128);
-        tile_id = cpg <= 32 ? 1 : cpg <= 64 ? 2 : (tm * ceil_div(cpg, 128) * p.G >= 2 * dev.num_cus ? 3 : 2);
+        tile_id = gcpg <= 32 ? 1 : gcpg <= 64 ? 2 : (tm * ceil_div(gcpg, 128) * (p.G / Gm) >= 2 * dev.num_cus ? 3 : 2);
     }
     const DgradTile* t = nullptr;
     for (const auto& d : kDgradTiles)
         if (d.id == tile_id) t = &d;
     if (!t) return fail(msg, U, "unknown dgrad tile id %d", tile_id);
-    const int64_t tiles_m = ceil_div(M, t->bm), tiles_n = ceil_div(cpg, t->bn);
-    const int64_t total = tiles_m * tiles_n * p.G;
+    const int64_t tiles_m = ceil_div(M, t->bm), tiles_n = ceil_div(gcpg, t->bn);
+    const int64_t total = tiles_m * tiles_n * (p.G / Gm);
     if (total > kMax31) return fail(msg, U, "grid too large");
     out = Plan{};
     out.op = OP_DGRAD;
@@ -606,6 +616,7 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     DgradArgs& a = out.dg;
     a = DgradArgs{};
     a.Ktot = (int32_t)p.K; a.Ctot = (int32_t)p.C; a.kpg = (int32_t)kpg; a.cpg = (int32_t)cpg;
+    a.Gm = (int32_t)Gm; a.gkpg = (int32_t)gkpg; a.gcpg = (int32_t)gcpg;
     a.Di = (int32_t)g.Di; a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi;
     a.Do = (int32_t)g.Do; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo;
     a.Xf = (int32_t)g.X; a.Yf = (int32_t)g.Y; a.taps = (int32_t)taps;
@@ -613,11 +624,12 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     a.dd = (int32_t)g.dd; a.dh = (int32_t)g.dh; a.dw = (int32_t)g.dw;
     a.pd = (int32_t)g.pd; a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
     a.M = (int32_t)M;
-    a.kchunks = (int32_t)ceil_div(kpg, 32);
+    a.kchunks = (int32_t)ceil_div(gkpg, 32);
     a.tiles_m = (int32_t)tiles_m; a.tiles_n = (int32_t)tiles_n; a.total_wg = (int32_t)total;
     a.out_mode = p.out_dtype == WGRAD_BF16 ? OUT_BF16 : p.out_dtype == WGRAD_FP16 ? OUT_FP16 : OUT_FP32;
     a.mWi = make_magic((uint32_t)g.Wi); a.mHi = make_magic((uint32_t)g.Hi); a.mDi = make_magic((uint32_t)g.Di);
     a.msd = make_magic((uint32_t)g.sd); a.msh = make_magic((uint32_t)g.sh); a.msw = make_magic((uint32_t)g.sw);
+    a.mkpg = make_magic((uint32_t)kpg); a.mcpg = make_magic((uint32_t)cpg);
     out.dg_bn = t->bn;
     out.dg_v = V;
     wgrad_plan_info& info = out.info;
@@ -632,15 +644,15 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     info.tile = tile_id;
     info.tile_m = t->bm; info.tile_n = t->bn; info.tile_k = 32;
     info.split_k = 1;
-    info.group_merge = 1;
+    info.group_merge = (int32_t)Gm;
     info.vector_width = V;
     info.grid_main = total;
     info.grid_reduce = 0;
     info.workspace_bytes = 0;
     info.num_cus = dev.num_cus;
     char name[160];
-    snprintf(name, sizeof name, "dgrad_mfma_%s_t%d_%dx%dx32_v%d_kouterB", out.in_f16 ? "fp16" : "bf16", tile_id,
-             t->bm, t->bn, V);
+    snprintf(name, sizeof name, "dgrad_mfma_%s_t%d_%dx%dx32_v%d_kouterB_gm%lld", out.in_f16 ? "fp16" : "bf16", tile_id,
+             t->bm, t->bn, V, (long long)Gm);
     out.name = name;
     return WGRAD_OK;
 }

@@ -183,20 +183,23 @@ struct Dw3Args {
 };
 
 // Backward data: flat MFMA implicit GEMM over input positions
-// m = (n, di, hi, wi), one group per grid slice, reduction over
-// (tap, output channel) in chunks of 32 channels of one tap.
+// m = (n, di, hi, wi), one block of Gm adjacent groups per grid slice,
+// reduction over (tap, output channel) in chunks of 32 channels of one tap.
+// Merged groups form one block-diagonal GEMM: their dY and dX channel runs
+// are contiguous, and weight entries that pair different groups are zero.
 struct DgradArgs {
     const uint16_t* dy;
     const uint16_t* w;
     void* dx;
     int32_t Ktot, Ctot, kpg, cpg;
+    int32_t Gm, gkpg, gcpg;        // merge degree, Gm*kpg, Gm*cpg
     int32_t Di, Hi, Wi, Do, Ho, Wo;
     int32_t Xf, Yf, taps;          // filter width, height and Z*Y*X
     int32_t sd, sh, sw, dd, dh, dw, pd, ph, pw;
     int32_t M;                     // N*Di*Hi*Wi
-    int32_t kchunks;               // ceil(kpg / 32)
+    int32_t kchunks;               // ceil(gkpg / 32)
     int32_t tiles_m, tiles_n, total_wg, out_mode;
-    MagicU32 mWi, mHi, mDi, msd, msh, msw;
+    MagicU32 mWi, mHi, mDi, msd, msh, msw, mkpg, mcpg;
 };
 // Depthwise backward data (C/G = K/G = 1, C % 8 == 0): a lane owns 8
 // channels of a 4-wide strip of one input row; a workgroup covers a channel

@@ -186,8 +186,13 @@ int wgrad_run_stage(const wgrad_plan_t* plan, int stage, const void* x, const vo
  * (K/G)*Z*Y*X; every dX element is written exactly once (positions no tap
  * reaches get 0), so there is no workspace and no split of the reduction.
  *
+ * Small groups are merged Gm at a time into one block-diagonal GEMM (N =
+ * Gm*C/G, reduction (Gm*K/G)*Z*Y*X, zero weight blocks between different
+ * groups); wgrad_plan_query reports Gm in group_merge.
+ *
  * wgrad_dgrad_plan: validation and errors as wgrad_plan. Overrides: split_k
- * and group_merge must be 0 or 1, variant AUTO or DGRAD, tile 0 (auto) or a
+ * must be 0 or 1, group_merge 0 (auto) or a power of two dividing G (the
+ * MFMA kernel), variant AUTO or DGRAD, tile 0 (auto) or a
  * dgrad kernel id: 1, 2, 3 = the MFMA kernel with 128x32, 128x64, 128x128
  * (positions x channels) tiles; 4 = the depthwise direct kernel (C/G = K/G
  * = 1, C % 8 == 0, at most 2048 taps), which auto picks for such shapes;

@@ -186,6 +186,24 @@ def test_dgrad_depthwise_kernel(i):
     check_tol(cfg, vals, dx64, ab64)
 
 
+@pytest.mark.parametrize("gm", [1, 2, 4, 8])
+def test_dgrad_group_merge(gm):
+    # C/G = 8, K/G = 12 (merged rows and columns of different widths), and a
+    # ragged tail of positions; every merge degree gives the exact sums
+    cfg = prob(2, 8, 2, 8, 12, (9, 11), (3, 3), (1, 2), (1, 1), (1, 1), (1, 1), name=f"gm{gm}")
+    dyb, wb = draw(cfg, "int", (81, 82))
+    _, bits, p = run_dgrad(cfg, dyb, wb, group_merge=gm)
+    assert p.info["group_merge"] == gm
+    dx64, _ = oracle.dgrad(cfg, dyb, wb)
+    check_exact(cfg, bits, dx64)
+    # depthwise through the merged MFMA kernel
+    cfg = prob(2, 16, 1, 1, 1, (7, 6), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), name=f"dwgm{gm}")
+    dyb, wb = draw(cfg, "uniform", (83, 84))
+    vals, _, p = run_dgrad(cfg, dyb, wb, group_merge=gm, tile=1)
+    dx64, ab64 = oracle.dgrad(cfg, dyb, wb)
+    check_tol(cfg, vals, dx64, ab64)
+
+
 def test_dgrad_empty_batch():
     cfg = prob(2, 1, 0, 16, 16, (8, 8), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1))
     p = gcb.DgradPlan(cfg)

@@ -326,14 +326,23 @@ def test_dgrad_plans_sizes_and_tiles():
     assert info["vector_width"] == 8 and p.name.startswith("dgrad_mfma_bf16")
     # grouped: one grid slice per group; odd channel runs narrow the loads
     g = prob3(4, 1, 4 * 6, 4 * 10, (3, 5, 7), (2, 3, 3), stride=(1, 2, 1), pad=(0, 1, 1))
-    p = dplan(g)
+    p = dplan(g, group_merge=1)
     assert p.info["vector_width"] == 2 and p.info["tile_n"] == 32
     assert p.info["grid_main"] == ((3 * 5 * 7 + 127) // 128) * 4
+    assert dplan(g).info["group_merge"] == 4 and dplan(g).info["grid_main"] == 1
     assert p.info["out_len"] == oracle.out_len(g)
     # explicit tiles; 128-wide channel tiles for wide groups
     wide = dict(cfg, C=256)
     assert dplan(wide).info["tile_n"] == 128
     assert dplan(wide, tile=2).info["tile_n"] == 64
+    # small groups merge until both merged runs reach 32 channels
+    p = dplan(workloads.CONFIGS["c4a"])
+    assert p.info["group_merge"] == 4 and p.info["tile_n"] == 32 and p.name.endswith("gm4")
+    assert p.info["grid_main"] == ((32 * 28 * 28 + 127) // 128) * 8
+    assert dplan(workloads.CONFIGS["c4a"], group_merge=8).info["group_merge"] == 8
+    for bad in (3, 64):
+        with pytest.raises(gcb.WgradError):
+            dplan(workloads.CONFIGS["c4a"], group_merge=bad)
     # depthwise shapes take the direct kernel; forcing it elsewhere is unsupported
     p = dplan(workloads.CONFIGS["c5"])
     assert p.info["tile"] == 4 and p.name.startswith("dgrad_dw") and p.info["tile_n"] == 512
