@@ -66,25 +66,35 @@ def algorithmic(cfg, info):
     return flops, nbytes
 
 
-def kernel_source_hash():
+# the source files each kernel family is built from (besides the shared
+# device helpers and argument headers); a traffic record is valid only for
+# the exact bytes of these files
+_FAMILY_SOURCES = (("wgrad_rowslab", "rowslab.hip"), ("wgrad_mfma", "kernels.hip"), ("wgrad_dw", "depthwise.hip"),
+                   ("dgrad_", "dgrad.hip"))
+_SHARED_SOURCES = ("device_common.hpp", "wgrad_internal.hpp", "dgrad_internal.hpp", "magic.hpp")
+
+
+def kernel_source_hash(plan_name):
+    """Hash of the sources the named plan's main kernel is compiled from."""
+    own = [f for pre, f in _FAMILY_SOURCES if plan_name.startswith(pre)]
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "grouped_convolution_backward_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".cpp", ".hpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+    for f in sorted(own + list(_SHARED_SOURCES)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, kernel_prefix):
+def measured_traffic(workload, plan_name):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources (else None)."""
+    taken on the same plan (kernel, split, merge) built from the current
+    sources of its kernel (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
         e = t[workload]
-        if e.get("source_hash") != kernel_source_hash() or not e.get("kernel", "").startswith(kernel_prefix):
+        if e.get("kernel") != plan_name or e.get("source_hash") != kernel_source_hash(plan_name):
             return None
         return e["bytes_per_launch"]
     except (OSError, KeyError, ValueError):
@@ -203,6 +213,7 @@ class Case:
             "split_k": self.plan.info["split_k"],
             "group_merge": self.plan.info["group_merge"],
             "input_sets": self.nsets,
+            "hbm_bytes_measured": measured_traffic(self.name, self.plan.name),
         }
 
 
@@ -340,7 +351,7 @@ def main():
         achieved, peak, unit = nbytes / t_main / 1e9, PEAK_HBM / 1e9, "GB/s"
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(HEADLINE, case.plan.name.split("_spk")[0]),
+            "traffic": measured_traffic(HEADLINE, case.plan.name),
             "kernel": case.plan.name, "kernel_us": round(t_main * 1e6, 3)}
     out = {
         "metric": METRIC,

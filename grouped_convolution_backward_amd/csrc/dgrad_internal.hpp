@@ -1,0 +1,54 @@
+// Kernel-argument blocks of the backward-data (dgrad) kernels (dgrad.hip),
+// kept apart from the backward-weight ones. Not part of the public interface.
+#pragma once
+
+#include <cstdint>
+
+#include "magic.hpp"
+
+namespace wgrad {
+
+// Backward data: flat MFMA implicit GEMM over input positions
+// m = (n, di, hi, wi), one block of Gm adjacent groups per grid slice,
+// reduction over (tap, output channel) in chunks of 32 channels of one tap.
+// Merged groups form one block-diagonal GEMM: their dY and dX channel runs
+// are contiguous, and weight entries that pair different groups are zero.
+struct DgradArgs {
+    const uint16_t* dy;
+    const uint16_t* w;
+    void* dx;
+    int32_t Ktot, Ctot, kpg, cpg;
+    int32_t Gm, gkpg, gcpg;        // merge degree, Gm*kpg, Gm*cpg
+    int32_t Di, Hi, Wi, Do, Ho, Wo;
+    int32_t Xf, Yf, taps;          // filter width, height and Z*Y*X
+    int32_t sd, sh, sw, dd, dh, dw, pd, ph, pw;
+    int32_t M;                     // N*Di*Hi*Wi
+    int32_t kchunks;               // ceil(gkpg / 32)
+    int32_t tiles_m, tiles_n, total_wg, out_mode;
+    MagicU32 mWi, mHi, mDi, msd, msh, msw, mkpg, mcpg;
+};
+// Depthwise backward data (C/G = K/G = 1, C % 8 == 0): a lane owns 8
+// channels of a 4-wide strip of one input row; a workgroup covers a channel
+// block of cb channels (weights staged in LDS as fp32 [tap][channel]) and
+// 256 / (cb / 8) strips.
+constexpr int kDgDwStrip = 4;
+constexpr int kDgDwLdsMax = 64 * 1024;
+struct DgradDwArgs {
+    const uint16_t* dy;
+    const uint16_t* w;
+    void* dx;
+    int32_t C, Di, Hi, Wi, Do, Ho, Wo;
+    int32_t Zf, Yf, Xf, taps;
+    int32_t sd, sh, sw, dd, dh, dw, pd, ph, pw;
+    int32_t cb, cbv, spw;          // channels per block, channel vectors per block (cb/8), strips per workgroup
+    int32_t nstrip, strips;        // strips per input row, N*Di*Hi*nstrip
+    int32_t cblocks, sgroups, total_wg, out_mode;
+    MagicU32 msd, msh, msw;
+};
+// dgrad tiles: id -> (BM, BN); 4 waves each
+struct DgradTile {
+    int id, bm, bn;
+};
+constexpr DgradTile kDgradTiles[] = {{1, 128, 32}, {2, 128, 64}, {3, 128, 128}};
+
+}  // namespace wgrad
