@@ -24,18 +24,44 @@
 // differs from a column's.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
+
+#ifndef DGRAD_BK
+#define DGRAD_BK 32
+#endif
 
 namespace wgrad {
 namespace {
 
 using namespace dev;
 
-template <int BM, int BN, int WM, int WN, int V, bool F16>
+// V 16-bit elements (V = 8, 4, 2, 1) from a raw buffer; an out-of-range
+// offset returns zeros without touching memory
+template <int V> struct BufVec;
+template <> struct BufVec<8> {
+    static __device__ __forceinline__ u32x4 load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return buf_load16(r, o); }
+};
+template <> struct BufVec<4> {
+    static __device__ __forceinline__ u32x2 load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return buf_load8(r, o); }
+};
+template <> struct BufVec<2> {
+    static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0);
+    }
+};
+template <> struct BufVec<1> {
+    static __device__ __forceinline__ uint16_t load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, 0);
+    }
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int V, bool S1, bool F16>
 __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     typedef typename VecT<V>::T VT;
-    constexpr int BK = 32;                         // output channels per reduction chunk
-    constexpr int PA = BK + 8;                     // A row pitch (elements): 80-byte rows
+    // BK output channels per reduction chunk; A rows padded by 16 bytes
+    constexpr int PA = BK + 8;
     constexpr int PB = BN + kLdsPad;               // B row pitch for the transposed reads
     constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -45,9 +71,12 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     constexpr int B_LOADS = (BK * BVR + 255) / 256;
     static_assert(WM * WN == 4 && FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
     static_assert((BM * AV) % 256 == 0, "A loads");
+    static_assert(A_LOADS + B_LOADS <= 63, "vmcnt range");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sA[BM * PA];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[BK * PB];
+    // two LDS stages: chunk c is computed from stage c % 2 while chunk c + 1
+    // is stored into the other one
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * PA];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BK * PB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = xcd_logical_id(blockIdx.x, a.total_wg);
@@ -58,9 +87,9 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     const int m0 = mt * BM, c0 = nt * BN;
 
     // A rows this thread loads: position m -> (n, di, hi, wi)
+    const int a_kv = (tid % AV) * V;
     int a_n[A_LOADS], a_d[A_LOADS], a_h[A_LOADS], a_w[A_LOADS];
     bool a_in[A_LOADS];
-    const int a_kv = (tid % AV) * V;
 #pragma unroll
     for (int p = 0; p < A_LOADS; ++p) {
         const int row = tid / AV + p * (256 / AV);
@@ -68,71 +97,121 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
         a_in[p] = m < a.M;
         const uint32_t mm = a_in[p] ? (uint32_t)m : 0u;
         const uint32_t q1 = magic_div(mm, a.mWi);
-        a_w[p] = (int)(mm - q1 * (uint32_t)a.Wi);
         const uint32_t q2 = magic_div(q1, a.mHi);
-        a_h[p] = (int)(q1 - q2 * (uint32_t)a.Hi);
         const uint32_t q3 = magic_div(q2, a.mDi);
+        a_w[p] = (int)(mm - q1 * (uint32_t)a.Wi);
+        a_h[p] = (int)(q1 - q2 * (uint32_t)a.Hi);
         a_d[p] = (int)(q2 - q3 * (uint32_t)a.Di);
         a_n[p] = (int)q3;
     }
-    const uint16_t* dy_g = a.dy + gb * a.gkpg;
-    const uint16_t* w_g = a.w + (int64_t)gb * a.gkpg * a.taps * a.cpg;
+    const __amdgpu_buffer_rsrc_t dy_rs = buf_rsrc(a.dy, a.dy_bytes);
+    const __amdgpu_buffer_rsrc_t w_rs = buf_rsrc(a.w, a.w_bytes);
+    const int dy_g = gb * a.gkpg;                                   // element offsets of the group block
+    const int w_g = gb * a.gkpg * a.taps * a.cpg;
+    // unit strides: tap (z, y, x) of input (d, h, w) reads output
+    // (d + pd - z*dd, h + ph - y*dh, w + pw - x*dw), so a row's dY offset is
+    // a fixed base minus a per-tap constant, and validity is three range
+    // checks against per-tap constants
+    // (unsigned arithmetic: the base of a padded coordinate may pass 2^31,
+    // the difference for a valid tap is a true offset)
+    uint32_t a_base[A_LOADS];
+#pragma unroll
+    for (int p = 0; p < A_LOADS; ++p) {
+        a_d[p] += a.pd;
+        a_h[p] += a.ph;
+        a_w[p] += a.pw;
+        a_base[p] = (uint32_t)dy_g +
+                    (((uint32_t)(a_n[p] * a.Do + a_d[p]) * a.Ho + a_h[p]) * a.Wo + a_w[p]) * (uint32_t)a.Ktot + a_kv;
+    }
+    // B rows and columns this thread loads; merged groups: row k carries
+    // weights only for the columns of its own group, [wlo, wlo + kpg)
+    int b_base[B_LOADS], b_row[B_LOADS], b_lo[B_LOADS];
+    bool b_ok[B_LOADS];
+#pragma unroll
+    for (int p = 0; p < B_LOADS; ++p) {
+        const int idx = tid + p * 256;
+        const int row = idx / BVR, cv = (idx - row * BVR) * V;
+        const int c = c0 + cv;
+        const int gc = (int)magic_div((uint32_t)c, a.mcpg);
+        b_row[p] = row;
+        b_lo[p] = gc * a.kpg;
+        b_ok[p] = row < BK && c < a.gcpg;
+        b_base[p] = w_g + row * a.taps * a.cpg + c - gc * a.cpg;
+    }
+    const int w_kstride = a.taps * a.cpg;
 
-    // output coordinate along one axis whose tap offset reaches input i:
-    // (i + pad - t*dil) / stride when exact and in range, else -1
-    auto out_coord = [](int i, int pad, int tdil, int len, MagicU32 ms, int stride) {
-        const int num = i + pad - tdil;
-        if (num < 0) return -1;
-        const int q = (int)magic_div((uint32_t)num, ms);
-        if (q * stride != num || q >= len) return -1;
-        return q;
+    // the chunk the next gload fetches: k-chunk kc of tap (tz, ty, tx),
+    // advanced one chunk per call (uniform across the workgroup)
+    int cur_kc = 0, cur_t = 0, cur_tx = 0, cur_ty = 0, cur_tz = 0;
+    auto advance = [&]() {
+        if (++cur_kc == a.kchunks) {
+            cur_kc = 0;
+            ++cur_t;
+            if (++cur_tx == a.Xf) {
+                cur_tx = 0;
+                if (++cur_ty == a.Yf) {
+                    cur_ty = 0;
+                    ++cur_tz;
+                }
+            }
+        }
     };
 
-    VT ra[A_LOADS], rb[B_LOADS];
-    auto gload = [&](int chunk) {
-        const int t = chunk / a.kchunks;
-        const int k0 = (chunk - t * a.kchunks) * BK;
-        const int tzy = t / a.Xf, tx = t - tzy * a.Xf;
-        const int tz = tzy / a.Yf, ty = tzy - tz * a.Yf;
+    // two register sets: chunk c + 2 is loaded into the set chunk c came in.
+    // Every load is issued (a masked element reads at an out-of-range
+    // offset, which returns zeros), chunks past the last included, so each
+    // chunk issues the same number of loads and the waits stay exact.
+    VT ra[2][A_LOADS], rb[2][B_LOADS];
+    auto gload = [&](VT* ra, VT* rb) {
+        const bool live = cur_t < a.taps;
+        const int k0 = cur_kc * BK;
+        const int tdz = cur_tz * a.dd, tdy = cur_ty * a.dh, tdx = cur_tx * a.dw;
+        if constexpr (S1) {
+            const uint32_t toff = ((uint32_t)(tdz * a.Ho + tdy) * a.Wo + tdx) * (uint32_t)a.Ktot - k0;
+            const bool kok = live && k0 + a_kv < a.gkpg;
 #pragma unroll
-        for (int p = 0; p < A_LOADS; ++p) {
-            VT v = 0;
-            const int k = k0 + a_kv;
-            if (a_in[p] && k < a.gkpg) {
-                const int od = out_coord(a_d[p], a.pd, tz * a.dd, a.Do, a.msd, a.sd);
-                const int oh = out_coord(a_h[p], a.ph, ty * a.dh, a.Ho, a.msh, a.sh);
-                const int ow = out_coord(a_w[p], a.pw, tx * a.dw, a.Wo, a.msw, a.sw);
-                if (od >= 0 && oh >= 0 && ow >= 0)
-                    v = *reinterpret_cast<const VT*>(dy_g + (((a_n[p] * a.Do + od) * a.Ho + oh) * a.Wo + ow) * a.Ktot + k);
+            for (int p = 0; p < A_LOADS; ++p) {
+                const bool ok = kok && a_in[p] && (unsigned)(a_d[p] - tdz) < (unsigned)a.Do &&
+                                (unsigned)(a_h[p] - tdy) < (unsigned)a.Ho && (unsigned)(a_w[p] - tdx) < (unsigned)a.Wo;
+                ra[p] = BufVec<V>::load(dy_rs, ok ? (a_base[p] - toff) * 2u : kBufOob);
             }
-            ra[p] = v;
+        } else {
+            // general strides: the output coordinate must divide exactly
+            auto out_coord = [](int num, int len, MagicU32 ms, int stride) {
+                const int q = (int)magic_div((uint32_t)max(num, 0), ms);
+                return num >= 0 && q * stride == num && q < len ? q : -1;
+            };
+            const int k = k0 + a_kv;
+#pragma unroll
+            for (int p = 0; p < A_LOADS; ++p) {
+                const int od = out_coord(a_d[p] - tdz, a.Do, a.msd, a.sd);
+                const int oh = out_coord(a_h[p] - tdy, a.Ho, a.msh, a.sh);
+                const int ow = out_coord(a_w[p] - tdx, a.Wo, a.msw, a.sw);
+                const bool ok = live && a_in[p] && k < a.gkpg && od >= 0 && oh >= 0 && ow >= 0;
+                const int e = dy_g + (((a_n[p] * a.Do + od) * a.Ho + oh) * a.Wo + ow) * a.Ktot + k;
+                ra[p] = BufVec<V>::load(dy_rs, ok ? (uint32_t)e * 2u : kBufOob);
+            }
         }
+        const int wofs = k0 * w_kstride + cur_t * a.cpg;
 #pragma unroll
         for (int p = 0; p < B_LOADS; ++p) {
-            VT v = 0;
-            const int idx = tid + p * 256;
-            const int row = idx / BVR, cv = (idx - row * BVR) * V;
-            const int k = k0 + row, c = c0 + cv;
-            if (row < BK && k < a.gkpg && c < a.gcpg) {
-                // block diagonal: row k (group k/kpg) meets column c (group c/cpg)
-                const int gc = (int)magic_div((uint32_t)c, a.mcpg);
-                if ((int)magic_div((uint32_t)k, a.mkpg) == gc)
-                    v = *reinterpret_cast<const VT*>(w_g + ((int64_t)k * a.taps + t) * a.cpg + c - gc * a.cpg);
-            }
-            rb[p] = v;
+            const int k = k0 + b_row[p];
+            const bool ok = live && b_ok[p] && (unsigned)(k - b_lo[p]) < (unsigned)a.kpg;
+            rb[p] = BufVec<V>::load(w_rs, ok ? (uint32_t)(b_base[p] + wofs) * 2u : kBufOob);
         }
+        advance();
     };
-    auto sstore = [&]() {
+    auto sstore = [&](const VT* ra, const VT* rb, uint16_t* sa, uint16_t* sb) {
 #pragma unroll
         for (int p = 0; p < A_LOADS; ++p) {
             const int row = tid / AV + p * (256 / AV);
-            *reinterpret_cast<VT*>(sA + row * PA + a_kv) = ra[p];
+            *reinterpret_cast<VT*>(sa + row * PA + a_kv) = ra[p];
         }
 #pragma unroll
         for (int p = 0; p < B_LOADS; ++p) {
             const int idx = tid + p * 256;
             const int row = idx / BVR, cv = (idx - row * BVR) * V;
-            if (row < BK) *reinterpret_cast<VT*>(sB + row * PB + cv) = rb[p];
+            if (row < BK) *reinterpret_cast<VT*>(sb + row * PB + cv) = rb[p];
         }
     };
 
@@ -147,34 +226,43 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{0};
 
-    const int nchunks = a.taps * a.kchunks;
-    if (nchunks > 0) {
-        gload(0);
-        sstore();
-        __syncthreads();
-    }
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const bool more = ch + 1 < nchunks;
-        if (more) gload(ch + 1);   // the next chunk waits in registers
+    // Chunk c: its loads were issued two chunks earlier; compute it from LDS
+    // stage c % 2, then store chunk c + 1 (loaded one chunk earlier) into the
+    // other stage. One barrier per chunk: every thread has finished computing
+    // from a stage before any thread stores into it again. The chunk count is
+    // padded to even with an all-zero chunk, so the loop body has no branch.
+    auto step = [&](int c, auto stage_tag) {
+        constexpr int P = decltype(stage_tag)::value;
+        gload(ra[P], rb[P]);   // chunk c + 2
+        const uint16_t* sa = sA[P];
+        const uint16_t* sb = sB[P];
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             i16x8 af[FM], bf[FN];
             // A operand: row lane%32 of the wave's block, k = 8*(lane/32) .. +7
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const i16x8*>(sA + (wm0 + i * 32 + (lane & 31)) * PA + ks * 16 + 8 * (lane >> 5));
+                af[i] = *reinterpret_cast<const i16x8*>(sa + (wm0 + i * 32 + (lane & 31)) * PA + ks * 16 + 8 * (lane >> 5));
 #pragma unroll
-            for (int j = 0; j < FN; ++j) bf[j] = tr_frag(sB + (ks * 16 + frag_row) * PB + wn0 + j * 32 + frag_col, PB);
+            for (int j = 0; j < FN; ++j) bf[j] = tr_frag(sb + (ks * 16 + frag_row) * PB + wn0 + j * 32 + frag_col, PB);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) mfma_step32<F16>(af[i], bf[j], acc[i][j]);
         }
-        if (more) {
-            __syncthreads();
-            sstore();
-            __syncthreads();
-        }
+        // the loads of chunk c + 2 (issued above) may stay in flight
+        __builtin_amdgcn_s_waitcnt(kWaitVm<A_LOADS + B_LOADS>);
+        sstore(ra[1 - P], rb[1 - P], sA[1 - P], sB[1 - P]);
+        __syncthreads();
+    };
+    gload(ra[0], rb[0]);
+    gload(ra[1], rb[1]);
+    __builtin_amdgcn_s_waitcnt(kWaitVm<A_LOADS + B_LOADS>);
+    sstore(ra[0], rb[0], sA[0], sB[0]);
+    __syncthreads();
+    for (int c = 0; c < a.nchunks; c += 2) {
+        step(c, std::integral_constant<int, 0>{});
+        step(c + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- epilogue: element (m, c) of the tile is dX[m][gb*gcpg + c]
@@ -192,25 +280,32 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool F16>
+template <int BM, int BN, int WM, int WN, bool S1, bool F16>
 int launch_v(const DgradArgs& a, int V, hipStream_t s) {
+    constexpr int BK = DGRAD_BK;
     dim3 grid(a.total_wg), block(256);
     switch (V) {
-        case 8: hipLaunchKernelGGL((dgrad_kernel<BM, BN, WM, WN, 8, F16>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((dgrad_kernel<BM, BN, WM, WN, 4, F16>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((dgrad_kernel<BM, BN, WM, WN, 2, F16>), grid, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL((dgrad_kernel<BM, BN, WM, WN, 1, F16>), grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 8, S1, F16>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 4, S1, F16>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 2, S1, F16>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 1, S1, F16>), grid, block, 0, s, a); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, bool F16>
+int launch_s(const DgradArgs& a, int V, hipStream_t s) {
+    const bool s1 = a.sd == 1 && a.sh == 1 && a.sw == 1;
+    return s1 ? launch_v<BM, BN, WM, WN, true, F16>(a, V, s) : launch_v<BM, BN, WM, WN, false, F16>(a, V, s);
+}
+
 template <bool F16>
 int launch_t(const Plan& plan, const DgradArgs& a, hipStream_t s) {
     switch (plan.dg_bn) {
-        case 32: return launch_v<128, 32, 4, 1, F16>(a, plan.dg_v, s);
-        case 64: return launch_v<128, 64, 2, 2, F16>(a, plan.dg_v, s);
-        case 128: return launch_v<128, 128, 2, 2, F16>(a, plan.dg_v, s);
+        case 32: return launch_s<128, 32, 4, 1, F16>(a, plan.dg_v, s);
+        case 64: return launch_s<128, 64, 2, 2, F16>(a, plan.dg_v, s);
+        case 128: return launch_s<128, 128, 2, 2, F16>(a, plan.dg_v, s);
         default: return (int)hipErrorInvalidValue;
     }
 }

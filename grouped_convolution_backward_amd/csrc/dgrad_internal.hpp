@@ -24,6 +24,8 @@ struct DgradArgs {
     int32_t sd, sh, sw, dd, dh, dw, pd, ph, pw;
     int32_t M;                     // N*Di*Hi*Wi
     int32_t kchunks;               // ceil(gkpg / 32)
+    int32_t nchunks;               // taps * kchunks
+    uint32_t dy_bytes, w_bytes;    // buffer sizes for the bounds-checked loads
     int32_t tiles_m, tiles_n, total_wg, out_mode;
     MagicU32 mWi, mHi, mDi, msd, msh, msw, mkpg, mcpg;
 };

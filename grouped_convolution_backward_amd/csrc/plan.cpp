@@ -114,7 +114,9 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
         while (sw > 1 && !fits(sw)) --sw;
         if (!fits(sw)) continue;
         int64_t pr = sw == g.Wo ? std::min<int64_t>({ks / sw, (int64_t)r.nxr, std::max<int64_t>(1, NHo)}) : 1;
-        const double eff = double(pr * sw) / double(ks);
+        // useful fraction of the slab slots over whole rows: a row cut into
+        // segments of sw fills ceil(Wo / sw) slabs
+        const double eff = double(pr * g.Wo) / double(ceil_div(g.Wo, sw) * ks);
         if (eff > best + 1e-9) { best = eff; inst = i; PR = pr; SW = sw; }
     }
     if (inst < 0) return no("row-slab: no kernel instance fits this slab geometry");
@@ -607,6 +609,9 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     if (!t) return fail(msg, U, "unknown dgrad tile id %d", tile_id);
     const int64_t tiles_m = ceil_div(M, t->bm), tiles_n = ceil_div(gcpg, t->bn);
     const int64_t total = tiles_m * tiles_n * (p.G / Gm);
+    const int64_t ndy = p.N * g.Do * g.Ho * g.Wo * p.K, nw = p.K * taps * cpg;
+    if (2 * ndy >= (int64_t{1} << 31) || 2 * nw >= (int64_t{1} << 31))
+        return fail(msg, U, "the dgrad kernel needs dY and W below 2 GiB each");
     if (total > kMax31) return fail(msg, U, "grid too large");
     out = Plan{};
     out.op = OP_DGRAD;
@@ -625,6 +630,9 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     a.pd = (int32_t)g.pd; a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
     a.M = (int32_t)M;
     a.kchunks = (int32_t)ceil_div(gkpg, 32);
+    a.nchunks = (int32_t)(taps * a.kchunks);
+    a.dy_bytes = (uint32_t)(2 * ndy);
+    a.w_bytes = (uint32_t)(2 * nw);
     a.tiles_m = (int32_t)tiles_m; a.tiles_n = (int32_t)tiles_n; a.total_wg = (int32_t)total;
     a.out_mode = p.out_dtype == WGRAD_BF16 ? OUT_BF16 : p.out_dtype == WGRAD_FP16 ? OUT_FP16 : OUT_FP32;
     a.mWi = make_magic((uint32_t)g.Wi); a.mHi = make_magic((uint32_t)g.Hi); a.mDi = make_magic((uint32_t)g.Di);
