@@ -28,10 +28,6 @@
 
 #include "device_common.hpp"
 
-#ifndef DGRAD_BK
-#define DGRAD_BK 32
-#endif
-
 namespace wgrad {
 namespace {
 
@@ -57,6 +53,43 @@ template <> struct BufVec<1> {
     }
 };
 
+__device__ __forceinline__ void widen8(const u32x4& v, float* f, bool f16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t u = v[i];
+        if (f16) {
+            f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+            f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+        } else {
+            f[2 * i] = __uint_as_float(u << 16);
+            f[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ void store8(void* out, int mode, int64_t e, const float* v) {
+    if (mode == OUT_FP32) {
+        float* o = static_cast<float*>(out) + e;
+        *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        return;
+    }
+    u32x4 p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t lo, hi;
+        if (mode == OUT_FP16) {
+            lo = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i]);
+            hi = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1]);
+        } else {
+            lo = f32_to_bf16(v[2 * i]);
+            hi = f32_to_bf16(v[2 * i + 1]);
+        }
+        p[i] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e) = p;
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int V, bool S1, bool F16>
 __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     typedef typename VecT<V>::T VT;
@@ -74,9 +107,11 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     static_assert(A_LOADS + B_LOADS <= 63, "vmcnt range");
 
     // two LDS stages: chunk c is computed from stage c % 2 while chunk c + 1
-    // is stored into the other one
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * PA];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BK * PB];
+    // is stored into the other one; the epilogue reuses the space
+    constexpr int LDS_ELEMS = 2 * BM * PA + 2 * BK * PB;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+    uint16_t* const sA[2] = {lds, lds + BM * PA};
+    uint16_t* const sB[2] = {lds + 2 * BM * PA, lds + 2 * BM * PA + BK * PB};
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = xcd_logical_id(blockIdx.x, a.total_wg);
@@ -266,23 +301,59 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     }
 
     // ---- epilogue: element (m, c) of the tile is dX[m][gb*gcpg + c]
+    if constexpr (V == 8) {
+        // 8-channel runs are whole and aligned: stage the tile in LDS as fp32
+        // [m][c], EPC columns at a time, and write 16-byte (32-byte for
+        // fp32) vectors of consecutive channels
+        constexpr int EPC0 = (LDS_ELEMS * 2 / (BM * 4)) / 32 * 32;
+        constexpr int EPC = EPC0 < BN ? EPC0 : BN;
+        static_assert(EPC >= 32 && BN % EPC == 0, "epilogue passes");
+        float* const stage = reinterpret_cast<float*>(lds);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int c = c0 + wn0 + j * 32 + (lane & 31);
-        if (c >= a.gcpg) continue;
+        for (int pc = 0; pc < BN; pc += EPC) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+            for (int j = 0; j < FN; ++j) {
+                const int col = wn0 + j * 32;
+                if (col < pc || col >= pc + EPC) continue;   // uniform per wave
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + wm0 + i * 32 + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
-                if (m < a.M) store_out(a.dx, a.out_mode, (int64_t)m * a.Ctot + gb * a.gcpg + c, acc[i][j][v]);
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = wm0 + i * 32 + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+                        stage[row * EPC + col - pc + (lane & 31)] = acc[i][j][v];
+                    }
             }
+            __syncthreads();
+            for (int e = tid; e < BM * EPC / 8; e += 256) {
+                const int row = e / (EPC / 8), cg = (e - row * (EPC / 8)) * 8;
+                const int m = m0 + row, c = c0 + pc + cg;
+                if (m < a.M && c < a.gcpg) {
+                    const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + row * EPC + cg);
+                    const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + row * EPC + cg + 4);
+                    const float v8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    store8(a.dx, a.out_mode, (int64_t)m * a.Ctot + gb * a.gcpg + c, v8);
+                }
+            }
+            __syncthreads();
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int c = c0 + wn0 + j * 32 + (lane & 31);
+            if (c >= a.gcpg) continue;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int m = m0 + wm0 + i * 32 + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+                    if (m < a.M) store_out(a.dx, a.out_mode, (int64_t)m * a.Ctot + gb * a.gcpg + c, acc[i][j][v]);
+                }
+        }
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool S1, bool F16>
+template <int BM, int BN, int BK, int WM, int WN, bool S1, bool F16>
 int launch_v(const DgradArgs& a, int V, hipStream_t s) {
-    constexpr int BK = DGRAD_BK;
     dim3 grid(a.total_wg), block(256);
     switch (V) {
         case 8: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 8, S1, F16>), grid, block, 0, s, a); break;
@@ -295,17 +366,21 @@ int launch_v(const DgradArgs& a, int V, hipStream_t s) {
 }
 
 template <int BM, int BN, int WM, int WN, bool F16>
-int launch_s(const DgradArgs& a, int V, hipStream_t s) {
+int launch_s(const Plan& plan, const DgradArgs& a, hipStream_t s) {
+    // 32-channel chunks: 64 measured slower on every shape here (half the
+    // workgroups per CU for the doubled LDS stages)
     const bool s1 = a.sd == 1 && a.sh == 1 && a.sw == 1;
-    return s1 ? launch_v<BM, BN, WM, WN, true, F16>(a, V, s) : launch_v<BM, BN, WM, WN, false, F16>(a, V, s);
+    if (plan.dg_bk != 32) return (int)hipErrorInvalidValue;
+    return s1 ? launch_v<BM, BN, 32, WM, WN, true, F16>(a, plan.dg_v, s)
+              : launch_v<BM, BN, 32, WM, WN, false, F16>(a, plan.dg_v, s);
 }
 
 template <bool F16>
 int launch_t(const Plan& plan, const DgradArgs& a, hipStream_t s) {
     switch (plan.dg_bn) {
-        case 32: return launch_s<128, 32, 4, 1, F16>(a, plan.dg_v, s);
-        case 64: return launch_s<128, 64, 2, 2, F16>(a, plan.dg_v, s);
-        case 128: return launch_s<128, 128, 2, 2, F16>(a, plan.dg_v, s);
+        case 32: return launch_s<128, 32, 4, 1, F16>(plan, a, s);
+        case 64: return launch_s<128, 64, 2, 2, F16>(plan, a, s);
+        case 128: return launch_s<128, 128, 2, 2, F16>(plan, a, s);
         default: return (int)hipErrorInvalidValue;
     }
 }
@@ -319,43 +394,6 @@ int launch_t(const Plan& plan, const DgradArgs& a, hipStream_t s) {
 // first, so each dY load instruction of a wave reads whole contiguous pixels.
 // The workgroup's weights sit in LDS as fp32 [tap][channel], read back as two
 // 16-byte reads per tap. Accumulation in fp32 in tap order (z, y, x).
-__device__ __forceinline__ void widen8(const u32x4& v, float* f, bool f16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t u = v[i];
-        if (f16) {
-            f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
-            f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
-        } else {
-            f[2 * i] = __uint_as_float(u << 16);
-            f[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
-        }
-    }
-}
-
-__device__ __forceinline__ void store8(void* out, int mode, int64_t e, const float* v) {
-    if (mode == OUT_FP32) {
-        float* o = static_cast<float*>(out) + e;
-        *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
-        return;
-    }
-    u32x4 p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t lo, hi;
-        if (mode == OUT_FP16) {
-            lo = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i]);
-            hi = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1]);
-        } else {
-            lo = f32_to_bf16(v[2 * i]);
-            hi = f32_to_bf16(v[2 * i + 1]);
-        }
-        p[i] = lo | (hi << 16);
-    }
-    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e) = p;
-}
-
 template <bool F16>
 __global__ __launch_bounds__(256) void dgrad_dw_kernel(const DgradDwArgs a) {
     extern __shared__ __attribute__((aligned(16))) float wlds[];   // [taps][cb]

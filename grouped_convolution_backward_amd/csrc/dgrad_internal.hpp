@@ -10,7 +10,7 @@ namespace wgrad {
 
 // Backward data: flat MFMA implicit GEMM over input positions
 // m = (n, di, hi, wi), one block of Gm adjacent groups per grid slice,
-// reduction over (tap, output channel) in chunks of 32 channels of one tap.
+// reduction over (tap, output channel) in chunks of 32 or 64 channels of one tap.
 // Merged groups form one block-diagonal GEMM: their dY and dX channel runs
 // are contiguous, and weight entries that pair different groups are zero.
 struct DgradArgs {
@@ -23,7 +23,7 @@ struct DgradArgs {
     int32_t Xf, Yf, taps;          // filter width, height and Z*Y*X
     int32_t sd, sh, sw, dd, dh, dw, pd, ph, pw;
     int32_t M;                     // N*Di*Hi*Wi
-    int32_t kchunks;               // ceil(gkpg / 32)
+    int32_t kchunks;               // ceil(gkpg / BK), BK = 32 or 64 channels per chunk
     int32_t nchunks;               // taps * kchunks
     uint32_t dy_bytes, w_bytes;    // buffer sizes for the bounds-checked loads
     int32_t tiles_m, tiles_n, total_wg, out_mode;

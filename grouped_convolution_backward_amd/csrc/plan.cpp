@@ -629,7 +629,8 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     a.dd = (int32_t)g.dd; a.dh = (int32_t)g.dh; a.dw = (int32_t)g.dw;
     a.pd = (int32_t)g.pd; a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
     a.M = (int32_t)M;
-    a.kchunks = (int32_t)ceil_div(gkpg, 32);
+    const int bk = 32;   // channels per reduction chunk (the kernel's BK)
+    a.kchunks = (int32_t)ceil_div(gkpg, bk);
     a.nchunks = (int32_t)(taps * a.kchunks);
     a.dy_bytes = (uint32_t)(2 * ndy);
     a.w_bytes = (uint32_t)(2 * nw);
@@ -639,6 +640,7 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     a.msd = make_magic((uint32_t)g.sd); a.msh = make_magic((uint32_t)g.sh); a.msw = make_magic((uint32_t)g.sw);
     a.mkpg = make_magic((uint32_t)kpg); a.mcpg = make_magic((uint32_t)cpg);
     out.dg_bn = t->bn;
+    out.dg_bk = bk;
     out.dg_v = V;
     wgrad_plan_info& info = out.info;
     {
@@ -650,7 +652,7 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     info.gemm_k = kpg * taps;
     info.variant = WGRAD_VARIANT_DGRAD;
     info.tile = tile_id;
-    info.tile_m = t->bm; info.tile_n = t->bn; info.tile_k = 32;
+    info.tile_m = t->bm; info.tile_n = t->bn; info.tile_k = bk;
     info.split_k = 1;
     info.group_merge = (int32_t)Gm;
     info.vector_width = V;
@@ -659,8 +661,8 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     info.workspace_bytes = 0;
     info.num_cus = dev.num_cus;
     char name[160];
-    snprintf(name, sizeof name, "dgrad_mfma_%s_t%d_%dx%dx32_v%d_kouterB_gm%lld", out.in_f16 ? "fp16" : "bf16", tile_id,
-             t->bm, t->bn, V, (long long)Gm);
+    snprintf(name, sizeof name, "dgrad_mfma_%s_t%d_%dx%dx%d_v%d_kouterB_gm%lld", out.in_f16 ? "fp16" : "bf16", tile_id,
+             t->bm, t->bn, bk, V, (long long)Gm);
     out.name = name;
     return WGRAD_OK;
 }

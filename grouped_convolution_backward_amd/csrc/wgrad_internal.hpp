@@ -209,7 +209,7 @@ struct Plan {
     ReduceArgs red;
     int dw_tile_y, dw_tile_x;   // depthwise kernel filter instance
     DgradArgs dg;
-    int dg_bn, dg_v;             // dgrad tile width and load vector width
+    int dg_bn, dg_v, dg_bk;      // dgrad tile width, load vector width, channels per reduction chunk
     DgradDwArgs dgdw;
     int dg_dw;                   // 1: the depthwise dgrad kernel
     std::string name;
