@@ -90,7 +90,7 @@ __device__ __forceinline__ void store8(void* out, int mode, int64_t e, const flo
     *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e) = p;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int V, bool S1, bool F16>
+template <int BM, int BN, int BK, int WM, int WN, int V, bool PH, bool F16>
 __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     typedef typename VecT<V>::T VT;
     // BK output channels per reduction chunk; A rows padded by 16 bytes
@@ -115,49 +115,55 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = xcd_logical_id(blockIdx.x, a.total_wg);
-    const int mt = L % a.tiles_m;
-    const int rest = L / a.tiles_m;
-    const int nt = rest % a.tiles_n;
-    const int gb = rest / a.tiles_n;   // block of Gm merged groups
+    // phase fastest: the phases of one tile read the same dY rows (PH: the
+    // problem has a stride above 1; without, one phase and every tap)
+    int r = L;
+    const int phase = PH ? r % a.phases : 0;
+    if (PH) r /= a.phases;
+    const int mt = r % a.tiles_m;
+    r /= a.tiles_m;
+    const int nt = r % a.tiles_n;
+    const int gb = r / a.tiles_n;   // block of Gm merged groups
     const int m0 = mt * BM, c0 = nt * BN;
+    const int ph_w = PH ? phase % a.sw : 0, ph_dh = PH ? phase / a.sw : 0;
+    const int ph_h = PH ? ph_dh % a.sh : 0, ph_d = PH ? ph_dh / a.sh : 0;
 
-    // A rows this thread loads: position m -> (n, di, hi, wi)
+    // this phase's taps per axis (host tables): first tap, count, and the
+    // output offset od = i_d + o0 of the first one
+    const int z0 = PH ? a.t0[0][ph_d] : 0, y0 = PH ? a.t0[1][ph_h] : 0, x0 = PH ? a.t0[2][ph_w] : 0;
+    const int nz = PH ? a.nt[0][ph_d] : a.Zf, ny = PH ? a.nt[1][ph_h] : a.Yf, nx = PH ? a.nt[2][ph_w] : a.Xf;
+    const int od0 = PH ? a.o0[0][ph_d] : a.pd, oh0 = PH ? a.o0[1][ph_h] : a.ph, ow0 = PH ? a.o0[2][ph_w] : a.pw;
+    const int nchunks = nz * ny * nx * a.kchunks;
+
+    // A rows this thread loads: phase-grid position m -> (n, i_d, i_h, i_w),
+    // input (n, ph_d + i_d*sd, ph_h + i_h*sh, ph_w + i_w*sw)
     const int a_kv = (tid % AV) * V;
-    int a_n[A_LOADS], a_d[A_LOADS], a_h[A_LOADS], a_w[A_LOADS];
+    int a_qd[A_LOADS], a_qh[A_LOADS], a_qw[A_LOADS];
     bool a_in[A_LOADS];
+    // dY offset of output (n, i_d, i_h, i_w); a tap adds a constant. Unsigned
+    // arithmetic: only the sum for a valid tap is a true offset.
+    uint32_t a_base[A_LOADS];
+    const int dy_g = gb * a.gkpg;   // element offsets of the group block
+    const int w_g = gb * a.gkpg * a.taps * a.cpg;
 #pragma unroll
     for (int p = 0; p < A_LOADS; ++p) {
         const int row = tid / AV + p * (256 / AV);
         const int m = m0 + row;
-        a_in[p] = m < a.M;
-        const uint32_t mm = a_in[p] ? (uint32_t)m : 0u;
-        const uint32_t q1 = magic_div(mm, a.mWi);
-        const uint32_t q2 = magic_div(q1, a.mHi);
-        const uint32_t q3 = magic_div(q2, a.mDi);
-        a_w[p] = (int)(mm - q1 * (uint32_t)a.Wi);
-        a_h[p] = (int)(q1 - q2 * (uint32_t)a.Hi);
-        a_d[p] = (int)(q2 - q3 * (uint32_t)a.Di);
-        a_n[p] = (int)q3;
+        const uint32_t mm = m < a.M ? (uint32_t)m : 0u;
+        const uint32_t q1 = magic_div(mm, a.mqw);
+        const uint32_t q2 = magic_div(q1, a.mqh);
+        const uint32_t q3 = magic_div(q2, a.mqd);
+        a_qw[p] = (int)(mm - q1 * (uint32_t)a.qw);
+        a_qh[p] = (int)(q1 - q2 * (uint32_t)a.qh);
+        a_qd[p] = (int)(q2 - q3 * (uint32_t)a.qd);
+        const int n = (int)q3;
+        const int di = ph_d + a_qd[p] * a.sd, hi = ph_h + a_qh[p] * a.sh, wi = ph_w + a_qw[p] * a.sw;
+        a_in[p] = m < a.M && di < a.Di && hi < a.Hi && wi < a.Wi;
+        a_base[p] = (uint32_t)dy_g +
+                    (((uint32_t)(n * a.Do + a_qd[p]) * a.Ho + a_qh[p]) * a.Wo + a_qw[p]) * (uint32_t)a.Ktot + a_kv;
     }
     const __amdgpu_buffer_rsrc_t dy_rs = buf_rsrc(a.dy, a.dy_bytes);
     const __amdgpu_buffer_rsrc_t w_rs = buf_rsrc(a.w, a.w_bytes);
-    const int dy_g = gb * a.gkpg;                                   // element offsets of the group block
-    const int w_g = gb * a.gkpg * a.taps * a.cpg;
-    // unit strides: tap (z, y, x) of input (d, h, w) reads output
-    // (d + pd - z*dd, h + ph - y*dh, w + pw - x*dw), so a row's dY offset is
-    // a fixed base minus a per-tap constant, and validity is three range
-    // checks against per-tap constants
-    // (unsigned arithmetic: the base of a padded coordinate may pass 2^31,
-    // the difference for a valid tap is a true offset)
-    uint32_t a_base[A_LOADS];
-#pragma unroll
-    for (int p = 0; p < A_LOADS; ++p) {
-        a_d[p] += a.pd;
-        a_h[p] += a.ph;
-        a_w[p] += a.pw;
-        a_base[p] = (uint32_t)dy_g +
-                    (((uint32_t)(a_n[p] * a.Do + a_d[p]) * a.Ho + a_h[p]) * a.Wo + a_w[p]) * (uint32_t)a.Ktot + a_kv;
-    }
     // B rows and columns this thread loads; merged groups: row k carries
     // weights only for the columns of its own group, [wlo, wlo + kpg)
     int b_base[B_LOADS], b_row[B_LOADS], b_lo[B_LOADS];
@@ -173,23 +179,53 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
         b_ok[p] = row < BK && c < a.gcpg;
         b_base[p] = w_g + row * a.taps * a.cpg + c - gc * a.cpg;
     }
-    const int w_kstride = a.taps * a.cpg;
 
-    // the chunk the next gload fetches: k-chunk kc of tap (tz, ty, tx),
-    // advanced one chunk per call (uniform across the workgroup)
-    int cur_kc = 0, cur_t = 0, cur_tx = 0, cur_ty = 0, cur_tz = 0;
+    // the chunk the next gload fetches: k-chunk kc of the phase's tap
+    // (iz, iy, ix), advanced one chunk per call. Uniform across the
+    // workgroup and kept incrementally (the scalar unit is shared by every
+    // wave of the CU): a new k-chunk adds to k0 and kw, a new tap adjusts the
+    // output offsets (od, oh, ow), the dY tap offset and the weight tap offset.
+    int cur = 0, cur_kc = 0, cur_iz = 0, cur_iy = 0, cur_ix = 0;
+    int k0 = 0, kw = 0;                                     // k0 * taps * cpg
+    int od = od0, oh = oh0, ow = ow0;
+    uint32_t tapoff = ((uint32_t)(od0 * a.Ho + oh0) * a.Wo + ow0) * (uint32_t)a.Ktot;
+    int wt = ((z0 * a.Yf + y0) * a.Xf + x0) * a.cpg;       // weight offset of the tap
+    const uint32_t ost_w = (uint32_t)(a.xdo * a.Ktot), ost_h = (uint32_t)(a.ydo * a.Wo * a.Ktot),
+                   ost_d = (uint32_t)(a.zdo * a.Ho * a.Wo * a.Ktot);
+    const int wst_x = a.xstep * a.cpg, wst_y = a.ystep * a.Xf * a.cpg, wst_z = a.zstep * a.Yf * a.Xf * a.cpg;
+    const int w_kstride = a.taps * a.cpg;
     auto advance = [&]() {
-        if (++cur_kc == a.kchunks) {
-            cur_kc = 0;
-            ++cur_t;
-            if (++cur_tx == a.Xf) {
-                cur_tx = 0;
-                if (++cur_ty == a.Yf) {
-                    cur_ty = 0;
-                    ++cur_tz;
-                }
-            }
+        ++cur;
+        k0 += BK;
+        kw += BK * w_kstride;
+        if (++cur_kc < a.kchunks) return;
+        cur_kc = 0;
+        k0 = 0;
+        kw = 0;
+        if (++cur_ix < nx) {
+            ow -= a.xdo;
+            tapoff -= ost_w;
+            wt += wst_x;
+            return;
         }
+        cur_ix = 0;
+        ow = ow0;
+        tapoff += (uint32_t)(nx - 1) * ost_w;
+        wt -= (nx - 1) * wst_x;
+        if (++cur_iy < ny) {
+            oh -= a.ydo;
+            tapoff -= ost_h;
+            wt += wst_y;
+            return;
+        }
+        cur_iy = 0;
+        oh = oh0;
+        tapoff += (uint32_t)(ny - 1) * ost_h;
+        wt -= (ny - 1) * wst_y;
+        ++cur_iz;
+        od -= a.zdo;
+        tapoff -= ost_d;
+        wt += wst_z;
     };
 
     // two register sets: chunk c + 2 is loaded into the set chunk c came in.
@@ -198,36 +234,16 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     // chunk issues the same number of loads and the waits stay exact.
     VT ra[2][A_LOADS], rb[2][B_LOADS];
     auto gload = [&](VT* ra, VT* rb) {
-        const bool live = cur_t < a.taps;
-        const int k0 = cur_kc * BK;
-        const int tdz = cur_tz * a.dd, tdy = cur_ty * a.dh, tdx = cur_tx * a.dw;
-        if constexpr (S1) {
-            const uint32_t toff = ((uint32_t)(tdz * a.Ho + tdy) * a.Wo + tdx) * (uint32_t)a.Ktot - k0;
-            const bool kok = live && k0 + a_kv < a.gkpg;
+        const bool live = cur < nchunks;
+        const uint32_t toff = tapoff + k0;
+        const bool kok = live && k0 + a_kv < a.gkpg;
 #pragma unroll
-            for (int p = 0; p < A_LOADS; ++p) {
-                const bool ok = kok && a_in[p] && (unsigned)(a_d[p] - tdz) < (unsigned)a.Do &&
-                                (unsigned)(a_h[p] - tdy) < (unsigned)a.Ho && (unsigned)(a_w[p] - tdx) < (unsigned)a.Wo;
-                ra[p] = BufVec<V>::load(dy_rs, ok ? (a_base[p] - toff) * 2u : kBufOob);
-            }
-        } else {
-            // general strides: the output coordinate must divide exactly
-            auto out_coord = [](int num, int len, MagicU32 ms, int stride) {
-                const int q = (int)magic_div((uint32_t)max(num, 0), ms);
-                return num >= 0 && q * stride == num && q < len ? q : -1;
-            };
-            const int k = k0 + a_kv;
-#pragma unroll
-            for (int p = 0; p < A_LOADS; ++p) {
-                const int od = out_coord(a_d[p] - tdz, a.Do, a.msd, a.sd);
-                const int oh = out_coord(a_h[p] - tdy, a.Ho, a.msh, a.sh);
-                const int ow = out_coord(a_w[p] - tdx, a.Wo, a.msw, a.sw);
-                const bool ok = live && a_in[p] && k < a.gkpg && od >= 0 && oh >= 0 && ow >= 0;
-                const int e = dy_g + (((a_n[p] * a.Do + od) * a.Ho + oh) * a.Wo + ow) * a.Ktot + k;
-                ra[p] = BufVec<V>::load(dy_rs, ok ? (uint32_t)e * 2u : kBufOob);
-            }
+        for (int p = 0; p < A_LOADS; ++p) {
+            const bool ok = kok && a_in[p] && (unsigned)(a_qd[p] + od) < (unsigned)a.Do &&
+                            (unsigned)(a_qh[p] + oh) < (unsigned)a.Ho && (unsigned)(a_qw[p] + ow) < (unsigned)a.Wo;
+            ra[p] = BufVec<V>::load(dy_rs, ok ? (a_base[p] + toff) * 2u : kBufOob);
         }
-        const int wofs = k0 * w_kstride + cur_t * a.cpg;
+        const int wofs = kw + wt;
 #pragma unroll
         for (int p = 0; p < B_LOADS; ++p) {
             const int k = k0 + b_row[p];
@@ -295,12 +311,27 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVm<A_LOADS + B_LOADS>);
     sstore(ra[0], rb[0], sA[0], sB[0]);
     __syncthreads();
-    for (int c = 0; c < a.nchunks; c += 2) {
+    for (int c = 0; c < nchunks; c += 2) {
         step(c, std::integral_constant<int, 0>{});
         step(c + 1, std::integral_constant<int, 1>{});
     }
 
-    // ---- epilogue: element (m, c) of the tile is dX[m][gb*gcpg + c]
+    // ---- epilogue: element (row, c) of the tile is dX[xpos(row)][gb*gcpg + c]
+    // input position of tile row `row` (-1: none); one phase: the rows are
+    // consecutive positions
+    auto xpos = [&](int row) {
+        const int m = m0 + row;
+        if (!PH) return m < a.M ? m : -1;
+        const uint32_t mm = m < a.M ? (uint32_t)m : 0u;
+        const uint32_t q1 = magic_div(mm, a.mqw);
+        const uint32_t q2 = magic_div(q1, a.mqh);
+        const uint32_t q3 = magic_div(q2, a.mqd);
+        const int wi = ph_w + (int)(mm - q1 * (uint32_t)a.qw) * a.sw;
+        const int hi = ph_h + (int)(q1 - q2 * (uint32_t)a.qh) * a.sh;
+        const int di = ph_d + (int)(q2 - q3 * (uint32_t)a.qd) * a.sd;
+        const bool in = m < a.M && di < a.Di && hi < a.Hi && wi < a.Wi;
+        return in ? (((int)q3 * a.Di + di) * a.Hi + hi) * a.Wi + wi : -1;
+    };
     if constexpr (V == 8) {
         // 8-channel runs are whole and aligned: stage the tile in LDS as fp32
         // [m][c], EPC columns at a time, and write 16-byte (32-byte for
@@ -326,12 +357,12 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
             __syncthreads();
             for (int e = tid; e < BM * EPC / 8; e += 256) {
                 const int row = e / (EPC / 8), cg = (e - row * (EPC / 8)) * 8;
-                const int m = m0 + row, c = c0 + pc + cg;
-                if (m < a.M && c < a.gcpg) {
+                const int pos = xpos(row), c = c0 + pc + cg;
+                if (pos >= 0 && c < a.gcpg) {
                     const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + row * EPC + cg);
                     const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + row * EPC + cg + 4);
                     const float v8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    store8(a.dx, a.out_mode, (int64_t)m * a.Ctot + gb * a.gcpg + c, v8);
+                    store8(a.dx, a.out_mode, (int64_t)pos * a.Ctot + gb * a.gcpg + c, v8);
                 }
             }
             __syncthreads();
@@ -345,42 +376,41 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int m = m0 + wm0 + i * 32 + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
-                    if (m < a.M) store_out(a.dx, a.out_mode, (int64_t)m * a.Ctot + gb * a.gcpg + c, acc[i][j][v]);
+                    const int pos = xpos(wm0 + i * 32 + 8 * (v / 4) + 4 * (lane / 32) + (v % 4));
+                    if (pos >= 0) store_out(a.dx, a.out_mode, (int64_t)pos * a.Ctot + gb * a.gcpg + c, acc[i][j][v]);
                 }
         }
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool S1, bool F16>
-int launch_v(const DgradArgs& a, int V, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, bool PH, bool F16>
+int launch_v(const Plan& plan, const DgradArgs& a, hipStream_t s) {
+    // 32-channel chunks: 64 measured slower on every shape here (half the
+    // workgroups per CU for the doubled LDS stages)
+    constexpr int BK = 32;
+    if (plan.dg_bk != BK) return (int)hipErrorInvalidValue;
     dim3 grid(a.total_wg), block(256);
-    switch (V) {
-        case 8: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 8, S1, F16>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 4, S1, F16>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 2, S1, F16>), grid, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 1, S1, F16>), grid, block, 0, s, a); break;
+    switch (plan.dg_v) {
+        case 8: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 8, PH, F16>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 4, PH, F16>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 2, PH, F16>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((dgrad_kernel<BM, BN, BK, WM, WN, 1, PH, F16>), grid, block, 0, s, a); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN, bool F16>
-int launch_s(const Plan& plan, const DgradArgs& a, hipStream_t s) {
-    // 32-channel chunks: 64 measured slower on every shape here (half the
-    // workgroups per CU for the doubled LDS stages)
-    const bool s1 = a.sd == 1 && a.sh == 1 && a.sw == 1;
-    if (plan.dg_bk != 32) return (int)hipErrorInvalidValue;
-    return s1 ? launch_v<BM, BN, 32, WM, WN, true, F16>(a, plan.dg_v, s)
-              : launch_v<BM, BN, 32, WM, WN, false, F16>(a, plan.dg_v, s);
+int launch_p(const Plan& plan, const DgradArgs& a, hipStream_t s) {
+    return a.phases > 1 ? launch_v<BM, BN, WM, WN, true, F16>(plan, a, s) : launch_v<BM, BN, WM, WN, false, F16>(plan, a, s);
 }
 
 template <bool F16>
 int launch_t(const Plan& plan, const DgradArgs& a, hipStream_t s) {
     switch (plan.dg_bn) {
-        case 32: return launch_s<128, 32, 4, 1, F16>(plan, a, s);
-        case 64: return launch_s<128, 64, 2, 2, F16>(plan, a, s);
-        case 128: return launch_s<128, 128, 2, 2, F16>(plan, a, s);
+        case 32: return launch_p<128, 32, 4, 1, F16>(plan, a, s);
+        case 64: return launch_p<128, 64, 2, 2, F16>(plan, a, s);
+        case 128: return launch_p<128, 128, 2, 2, F16>(plan, a, s);
         default: return (int)hipErrorInvalidValue;
     }
 }

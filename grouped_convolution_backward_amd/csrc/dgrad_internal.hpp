@@ -8,11 +8,19 @@
 
 namespace wgrad {
 
-// Backward data: flat MFMA implicit GEMM over input positions
-// m = (n, di, hi, wi), one block of Gm adjacent groups per grid slice,
-// reduction over (tap, output channel) in chunks of 32 or 64 channels of one tap.
-// Merged groups form one block-diagonal GEMM: their dY and dX channel runs
-// are contiguous, and weight entries that pair different groups are zero.
+// Backward data: flat MFMA implicit GEMM over input positions, one block of
+// Gm adjacent groups per grid slice, reduction over (tap, output channel) in
+// chunks of 32 channels of one tap. Merged groups form one block-diagonal
+// GEMM: their dY and dX channel runs are contiguous, and weight entries that
+// pair different groups are zero.
+//
+// Stride phases: input positions are split by (di mod sd, hi mod sh,
+// wi mod sw). Within a phase, tap z either reaches an output position for
+// every input of the phase, at od = i_d + (ph_d + pd - z*dd) / sd with
+// di = ph_d + i_d*sd, or for none of them. A workgroup covers positions of
+// one phase and walks only that phase's taps: the valid z form the
+// progression z0, z0 + zstep, ... with zstep = sd / gcd(sd, dd).
+constexpr int kDgMaxStride = 16;   // per-axis stride limit of the phase tables
 struct DgradArgs {
     const uint16_t* dy;
     const uint16_t* w;
@@ -20,14 +28,20 @@ struct DgradArgs {
     int32_t Ktot, Ctot, kpg, cpg;
     int32_t Gm, gkpg, gcpg;        // merge degree, Gm*kpg, Gm*cpg
     int32_t Di, Hi, Wi, Do, Ho, Wo;
-    int32_t Xf, Yf, taps;          // filter width, height and Z*Y*X
+    int32_t Zf, Yf, Xf, taps;      // filter depth, height, width and Z*Y*X
     int32_t sd, sh, sw, dd, dh, dw, pd, ph, pw;
-    int32_t M;                     // N*Di*Hi*Wi
-    int32_t kchunks;               // ceil(gkpg / BK), BK = 32 or 64 channels per chunk
-    int32_t nchunks;               // taps * kchunks
+    int32_t zstep, ystep, xstep;   // s / gcd(s, dilation) per axis: taps between valid taps
+    int32_t zdo, ydo, xdo;         // dilation / gcd(s, dilation): output step between valid taps
+    // per axis (d, h, w) and phase residue r < stride: first valid tap, number
+    // of valid taps and the output offset (r + pad - t0*dil) / stride of the first
+    int16_t t0[3][kDgMaxStride], nt[3][kDgMaxStride], o0[3][kDgMaxStride];
+    int32_t qd, qh, qw;            // phase grid: ceil(Di / sd), ceil(Hi / sh), ceil(Wi / sw)
+    int32_t phases;                // sd * sh * sw
+    int32_t M;                     // N * qd * qh * qw positions per phase
+    int32_t kchunks;               // ceil(gkpg / 32)
     uint32_t dy_bytes, w_bytes;    // buffer sizes for the bounds-checked loads
     int32_t tiles_m, tiles_n, total_wg, out_mode;
-    MagicU32 mWi, mHi, mDi, msd, msh, msw, mkpg, mcpg;
+    MagicU32 mqw, mqh, mqd, mkpg, mcpg;
 };
 // Depthwise backward data (C/G = K/G = 1, C % 8 == 0): a lane owns 8
 // channels of a 4-wide strip of one input row; a workgroup covers a channel

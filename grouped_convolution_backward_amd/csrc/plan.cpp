@@ -607,12 +607,23 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     for (const auto& d : kDgradTiles)
         if (d.id == tile_id) t = &d;
     if (!t) return fail(msg, U, "unknown dgrad tile id %d", tile_id);
-    const int64_t tiles_m = ceil_div(M, t->bm), tiles_n = ceil_div(gcpg, t->bn);
-    const int64_t total = tiles_m * tiles_n * (p.G / Gm);
+    // stride phases: one grid slice per (di mod sd, hi mod sh, wi mod sw),
+    // each over the phase grid of ceil(Di/sd) x ceil(Hi/sh) x ceil(Wi/sw)
+    if (g.sd > kDgMaxStride || g.sh > kDgMaxStride || g.sw > kDgMaxStride)
+        return fail(msg, U, "the dgrad kernel supports strides up to %d", kDgMaxStride);
+    // the phase tables hold 16-bit tap indices and output offsets
+    if (g.Z > 32767 || g.Y > 32767 || g.X > 32767 || g.pd > 32767 || g.ph > 32767 || g.pw > 32767 ||
+        g.dd * g.Z > 32767 || g.dh * g.Y > 32767 || g.dw * g.X > 32767)
+        return fail(msg, U, "filter, pad or dilation too large for the dgrad kernel");
+    const int64_t qd = ceil_div(g.Di, g.sd), qh = ceil_div(g.Hi, g.sh), qw = ceil_div(g.Wi, g.sw);
+    const int64_t phases = g.sd * g.sh * g.sw;
+    const int64_t Mq = p.N * qd * qh * qw;
+    const int64_t tiles_m = ceil_div(Mq, t->bm), tiles_n = ceil_div(gcpg, t->bn);
+    const int64_t total = phases * tiles_m * tiles_n * (p.G / Gm);
     const int64_t ndy = p.N * g.Do * g.Ho * g.Wo * p.K, nw = p.K * taps * cpg;
     if (2 * ndy >= (int64_t{1} << 31) || 2 * nw >= (int64_t{1} << 31))
         return fail(msg, U, "the dgrad kernel needs dY and W below 2 GiB each");
-    if (total > kMax31) return fail(msg, U, "grid too large");
+    if (total > kMax31 || Mq > kMax31) return fail(msg, U, "grid too large");
     out = Plan{};
     out.op = OP_DGRAD;
     out.prob = p;
@@ -624,20 +635,40 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     a.Gm = (int32_t)Gm; a.gkpg = (int32_t)gkpg; a.gcpg = (int32_t)gcpg;
     a.Di = (int32_t)g.Di; a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi;
     a.Do = (int32_t)g.Do; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo;
-    a.Xf = (int32_t)g.X; a.Yf = (int32_t)g.Y; a.taps = (int32_t)taps;
+    a.Zf = (int32_t)g.Z; a.Yf = (int32_t)g.Y; a.Xf = (int32_t)g.X; a.taps = (int32_t)taps;
     a.sd = (int32_t)g.sd; a.sh = (int32_t)g.sh; a.sw = (int32_t)g.sw;
     a.dd = (int32_t)g.dd; a.dh = (int32_t)g.dh; a.dw = (int32_t)g.dw;
     a.pd = (int32_t)g.pd; a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
-    a.M = (int32_t)M;
+    a.zstep = (int32_t)(g.sd / gcd64(g.sd, g.dd)); a.zdo = (int32_t)(g.dd / gcd64(g.sd, g.dd));
+    a.ystep = (int32_t)(g.sh / gcd64(g.sh, g.dh)); a.ydo = (int32_t)(g.dh / gcd64(g.sh, g.dh));
+    a.xstep = (int32_t)(g.sw / gcd64(g.sw, g.dw)); a.xdo = (int32_t)(g.dw / gcd64(g.sw, g.dw));
+    {
+        // per axis and residue r: the taps t with (r + pad - t*dil) divisible
+        // by the stride form t0, t0 + step, ... below the filter length
+        const int64_t fl[3] = {g.Z, g.Y, g.X}, st[3] = {g.sd, g.sh, g.sw}, dl[3] = {g.dd, g.dh, g.dw},
+                      pl[3] = {g.pd, g.ph, g.pw};
+        for (int ax = 0; ax < 3; ++ax) {
+            const int64_t step = st[ax] / gcd64(st[ax], dl[ax]);
+            for (int64_t r = 0; r < st[ax]; ++r) {
+                int64_t t0 = 0;
+                while (t0 < step && t0 < fl[ax] && (r + pl[ax] - t0 * dl[ax]) % st[ax] != 0) ++t0;
+                const bool any = t0 < step && t0 < fl[ax];
+                a.t0[ax][r] = (int16_t)(any ? t0 : 0);
+                a.nt[ax][r] = (int16_t)(any ? (fl[ax] - 1 - t0) / step + 1 : 0);
+                a.o0[ax][r] = (int16_t)(any ? (r + pl[ax] - t0 * dl[ax]) / st[ax] : 0);
+            }
+        }
+    }
+    a.qd = (int32_t)qd; a.qh = (int32_t)qh; a.qw = (int32_t)qw;
+    a.phases = (int32_t)phases;
+    a.M = (int32_t)Mq;
     const int bk = 32;   // channels per reduction chunk (the kernel's BK)
     a.kchunks = (int32_t)ceil_div(gkpg, bk);
-    a.nchunks = (int32_t)(taps * a.kchunks);
     a.dy_bytes = (uint32_t)(2 * ndy);
     a.w_bytes = (uint32_t)(2 * nw);
     a.tiles_m = (int32_t)tiles_m; a.tiles_n = (int32_t)tiles_n; a.total_wg = (int32_t)total;
     a.out_mode = p.out_dtype == WGRAD_BF16 ? OUT_BF16 : p.out_dtype == WGRAD_FP16 ? OUT_FP16 : OUT_FP32;
-    a.mWi = make_magic((uint32_t)g.Wi); a.mHi = make_magic((uint32_t)g.Hi); a.mDi = make_magic((uint32_t)g.Di);
-    a.msd = make_magic((uint32_t)g.sd); a.msh = make_magic((uint32_t)g.sh); a.msw = make_magic((uint32_t)g.sw);
+    a.mqw = make_magic((uint32_t)qw); a.mqh = make_magic((uint32_t)qh); a.mqd = make_magic((uint32_t)qd);
     a.mkpg = make_magic((uint32_t)kpg); a.mcpg = make_magic((uint32_t)cpg);
     out.dg_bn = t->bn;
     out.dg_bk = bk;

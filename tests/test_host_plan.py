@@ -328,8 +328,9 @@ def test_dgrad_plans_sizes_and_tiles():
     g = prob3(4, 1, 4 * 6, 4 * 10, (3, 5, 7), (2, 3, 3), stride=(1, 2, 1), pad=(0, 1, 1))
     p = dplan(g, group_merge=1)
     assert p.info["vector_width"] == 2 and p.info["tile_n"] == 32
-    assert p.info["grid_main"] == ((3 * 5 * 7 + 127) // 128) * 4
-    assert dplan(g).info["group_merge"] == 4 and dplan(g).info["grid_main"] == 1
+    # h-stride 2: two stride phases, each over a 3 x 3 x 7 phase grid
+    assert p.info["grid_main"] == 2 * ((3 * 3 * 7 + 127) // 128) * 4
+    assert dplan(g).info["group_merge"] == 4 and dplan(g).info["grid_main"] == 2
     assert p.info["out_len"] == oracle.out_len(g)
     # explicit tiles; 128-wide channel tiles for wide groups
     wide = dict(cfg, C=256)
