@@ -131,6 +131,10 @@ EDGE = [
     (1, 4, 3, 16, 24, (37,), (5,), (2,), (2,), (1,), (1,), "bf16", None),
     (3, 2, 2, 16, 32, (5, 6, 7), (3, 3, 3), (1, 2, 1), (1, 1, 1), (1, 0, 1), (1, 1, 2), "bf16", None),
     (3, 1, 1, 8, 8, (3, 4, 5), (2, 1, 3), (2, 1, 1), (0, 0, 1), (1, 0, 1), (1, 1, 1), "fp16", "fp32"),
+    # stride and dilation sharing a factor: valid taps every other tap (s 4,
+    # d 2) or every tap with unit output steps (s 3, d 3)
+    (2, 1, 2, 16, 24, (17, 13), (5, 3), (4, 3), (3, 2), (2, 0), (2, 3), "bf16", None),
+    (1, 2, 2, 8, 40, (29,), (4,), (3,), (5,), (4,), (3,), "fp16", None),
 ]
 
 

@@ -353,6 +353,12 @@ def test_dgrad_plans_sizes_and_tiles():
     with pytest.raises(gcb.WgradError) as e:
         dplan(cfg, tile=4)
     assert e.value.code == gcb.ERR_UNSUPPORTED
+    # stride phases: one grid slice per phase; strides above 16 are refused
+    p = dplan(workloads.CONFIGS["c3"])
+    assert p.info["grid_main"] == 4 * ((16 * 28 * 28 + 127) // 128) * (128 // p.info["tile_n"])
+    with pytest.raises(gcb.WgradError) as e:
+        dplan(dict(cfg, stride=(17, 1), in_len=(70, 56)))
+    assert e.value.code == gcb.ERR_UNSUPPORTED
     # the fp16 strided shape, fp32 output
     p = dplan(dict(workloads.CONFIGS["c3"], out_dtype="fp32"))
     assert p.info["gemm_m"] == 16 * 56 * 56 and p.info["gemm_k"] == 200 * 9 and "fp16" in p.name
