@@ -492,10 +492,152 @@ __global__ __launch_bounds__(256) void dgrad_dw_kernel(const DgradDwArgs a) {
         if (w0 + j < a.Wi) store8(a.dx, a.out_mode, (pix + w0 + j) * a.C + c, acc[j]);
 }
 
+// Row-walking form (3x3 filter, unit stride and dilation). A lane group
+// (the lanes of one channel block, kDgRingCh channels per lane) owns one
+// 4-wide strip of one row chunk and walks its rows downward: input row h
+// needs dY rows h + ph - y, y = 0..2, each over the 6 columns
+// w0 + pw - 2 .. w0 + pw + 3, so every step loads one new dY row segment (two
+// steps ahead) into a 5-slot register ring and computes 4 positions x 9 taps
+// from registers. The block's weights sit in LDS as fp32 [tap][channel].
+// Chunks are numbered strip-fastest with aligned row ranges, so neighbouring
+// strips read their shared columns at the same time (one HBM fetch, one L2
+// hit).
+__device__ __forceinline__ void widen4(const u32x2& v, float* f, bool f16) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t u = v[i];
+        if (f16) {
+            f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+            f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+        } else {
+            f[2 * i] = __uint_as_float(u << 16);
+            f[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ void store4v(void* out, int mode, int64_t e, const float* v) {
+    if (mode == OUT_FP32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + e) = f32x4{v[0], v[1], v[2], v[3]};
+        return;
+    }
+    u32x2 p;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        uint32_t lo, hi;
+        if (mode == OUT_FP16) {
+            lo = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i]);
+            hi = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1]);
+        } else {
+            lo = f32_to_bf16(v[2 * i]);
+            hi = f32_to_bf16(v[2 * i + 1]);
+        }
+        p[i] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e) = p;
+}
+
+template <bool F16>
+__global__ __launch_bounds__(256) void dgrad_dw_ring_kernel(const DgradDwArgs a) {
+    constexpr int S = kDgDwStrip, XF = 3, COLS = S + XF - 1, SLOTS = 5, CH = kDgRingCh;
+    __shared__ __attribute__((aligned(16))) float wlds[9 * kDgRingMaxCb];   // [tap][channel of the block]
+    const int tid = threadIdx.x;
+    const int L = xcd_logical_id(blockIdx.x, a.total_wg);
+    const int sg = L % a.sgroups, cbk = L / a.sgroups;
+    // the block's weights, transposed to [tap][channel]
+    for (int e = tid; e < a.cb * 9; e += 256) {
+        const int cl = e / 9, t = e - cl * 9;
+        const uint16_t u = a.w[(int64_t)(cbk * a.cb + cl) * 9 + t];
+        wlds[t * a.cb + cl] = F16 ? (float)__builtin_bit_cast(_Float16, u) : __uint_as_float((uint32_t)u << 16);
+    }
+    __syncthreads();
+    const int cvl = tid % a.cbv, sl = tid / a.cbv;
+    const int it = sg * a.spw + sl;
+    if (it >= a.items) return;   // no barrier follows
+    const int strip = it % a.nstrip;
+    int r = it / a.nstrip;
+    const int chunk = r % a.nch;
+    const int n = r / a.nch;
+    const int r0 = (int)((int64_t)chunk * a.Hi / a.nch), r1 = (int)((int64_t)(chunk + 1) * a.Hi / a.nch);
+    const int w0 = strip * S;
+    const int c = cbk * a.cb + cvl * CH;
+    const float* wl = wlds + cvl * CH;
+
+    const __amdgpu_buffer_rsrc_t dy_rs = buf_rsrc(a.dy, a.dy_bytes);
+    // column validity and byte offsets within a row, fixed for the lane
+    bool col_ok[COLS];
+#pragma unroll
+    for (int jj = 0; jj < COLS; ++jj) col_ok[jj] = (unsigned)(w0 + a.pw - (XF - 1) + jj) < (unsigned)a.Wo;
+    const uint32_t col0 = (uint32_t)(((w0 + a.pw - (XF - 1)) * a.C + c) * 2), colstep = (uint32_t)(a.C * 2);
+    const uint32_t rowbytes = (uint32_t)(a.Wo * a.C * 2);
+    // dY row `oh` (zeros outside), columns w0 + pw - 2 + jj
+    auto load_row = [&](int oh, u32x2* dst) {
+        const bool rok = (unsigned)oh < (unsigned)a.Ho;
+        const uint32_t base = (uint32_t)(n * a.Ho + oh) * rowbytes + col0;
+#pragma unroll
+        for (int jj = 0; jj < COLS; ++jj) dst[jj] = buf_load8(dy_rs, rok && col_ok[jj] ? base + jj * colstep : kBufOob);
+    };
+    u32x2 ring[SLOTS][COLS];
+    // the row entering at step i is dY row r0 + i + ph and lives in slot i % 5;
+    // steps -2 and -1 hold the two rows above the first
+    load_row(r0 + a.ph - 2, ring[3]);
+    load_row(r0 + a.ph - 1, ring[4]);
+    load_row(r0 + a.ph, ring[0]);
+    load_row(r0 + a.ph + 1, ring[1]);
+    const int nsteps = r1 - r0;
+    const int64_t pix0 = ((int64_t)n * a.Hi) * a.Wi;
+    auto step = [&](int i, auto rot) {
+        constexpr int R = decltype(rot)::value;   // i % 5
+        // the prefetch is issued on every step, past the chunk's end too
+        // (rows below are in bounds or read as zeros), so no branch sits
+        // between a load and its use and the waits stay exact
+        load_row(r0 + i + 2 + a.ph, ring[(R + 2) % SLOTS]);   // two steps ahead
+        if (i >= nsteps) return;
+        float acc[S][CH];
+#pragma unroll
+        for (int j = 0; j < S; ++j)
+#pragma unroll
+            for (int k = 0; k < CH; ++k) acc[j][k] = 0.f;
+#pragma unroll
+        for (int y = 0; y < 3; ++y) {
+            const u32x2* row = ring[(R - y + SLOTS) % SLOTS];
+            float f[COLS][CH];
+#pragma unroll
+            for (int jj = 0; jj < COLS; ++jj) widen4(row[jj], f[jj], F16);
+#pragma unroll
+            for (int x = 0; x < XF; ++x) {
+                const f32x4 wv = *reinterpret_cast<const f32x4*>(wl + (y * 3 + x) * a.cb);
+#pragma unroll
+                for (int j = 0; j < S; ++j)
+#pragma unroll
+                    for (int k = 0; k < CH; ++k) acc[j][k] = __builtin_fmaf(f[j + XF - 1 - x][k], wv[k], acc[j][k]);
+            }
+        }
+        const int64_t pix = pix0 + (int64_t)(r0 + i) * a.Wi;
+#pragma unroll
+        for (int j = 0; j < S; ++j)
+            if (w0 + j < a.Wi) store4v(a.dx, a.out_mode, (pix + w0 + j) * a.C + c, acc[j]);
+    };
+    for (int i = 0; i < nsteps; i += SLOTS) {
+        step(i, std::integral_constant<int, 0>{});
+        step(i + 1, std::integral_constant<int, 1>{});
+        step(i + 2, std::integral_constant<int, 2>{});
+        step(i + 3, std::integral_constant<int, 3>{});
+        step(i + 4, std::integral_constant<int, 4>{});
+    }
+}
+
 }  // namespace
 
 int launch_dgrad_dw(const Plan& plan, const DgradDwArgs& a, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (a.form == 2) {
+        if (plan.in_f16)
+            hipLaunchKernelGGL(dgrad_dw_ring_kernel<true>, dim3(a.total_wg), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(dgrad_dw_ring_kernel<false>, dim3(a.total_wg), dim3(256), 0, s, a);
+        return (int)hipGetLastError();
+    }
     const size_t lds = (size_t)a.taps * a.cb * 4;
     if (plan.in_f16)
         hipLaunchKernelGGL(dgrad_dw_kernel<true>, dim3(a.total_wg), dim3(256), lds, s, a);

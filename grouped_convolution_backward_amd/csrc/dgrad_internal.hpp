@@ -48,6 +48,8 @@ struct DgradArgs {
 // block of cb channels (weights staged in LDS as fp32 [tap][channel]) and
 // 256 / (cb / 8) strips.
 constexpr int kDgDwStrip = 4;
+// row-walking form: channels per lane and the widest channel block (64 lanes)
+constexpr int kDgRingCh = 4, kDgRingMaxCb = 64 * kDgRingCh;
 constexpr int kDgDwLdsMax = 64 * 1024;
 struct DgradDwArgs {
     const uint16_t* dy;
@@ -60,6 +62,11 @@ struct DgradDwArgs {
     int32_t nstrip, strips;        // strips per input row, N*Di*Hi*nstrip
     int32_t cblocks, sgroups, total_wg, out_mode;
     MagicU32 msd, msh, msw;
+    // row-walking form (3x3, unit stride and dilation, 2D/1D): strips are cut
+    // into nch chunks of rows; items = N * nch * nstrip per channel block
+    int32_t form;                  // 1: per-tap loads, 2: row walk
+    int32_t nch, items;
+    uint32_t dy_bytes;
 };
 // dgrad tiles: id -> (BM, BN); 4 waves each
 struct DgradTile {

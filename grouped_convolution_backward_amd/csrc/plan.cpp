@@ -542,11 +542,15 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     if (cpg == 1 && kpg == 1 && p.C % 8 == 0)
         for (int cb = 512; cb >= 8 && !dw_cb; cb >>= 1)
             if (p.C % cb == 0 && taps * cb * 4 <= kDgDwLdsMax) dw_cb = cb;
-    if (o.tile == 4 && o.group_merge > 1) return fail(msg, U, "the depthwise dgrad kernel does not merge groups");
-    if (o.tile == 4 && !dw_cb)
+    // row-walking form: 3x3 in 2D, unit stride and dilation
+    const bool ring_ok = dw_cb && g.Di == 1 && g.Z == 1 && g.Y == 3 && g.X == 3 && g.sh == 1 && g.sw == 1 &&
+                         g.dh == 1 && g.dw == 1 && 2 * p.N * g.Ho * g.Wo * p.C < (int64_t{1} << 31);
+    const bool dw_tile = o.tile == 4 || o.tile == 5;
+    if (dw_tile && o.group_merge > 1) return fail(msg, U, "the depthwise dgrad kernel does not merge groups");
+    if (dw_tile && !dw_cb)
         return fail(msg, U, "the depthwise dgrad kernel needs C/G = K/G = 1, C %% 8 == 0 and at most %d taps",
                     kDgDwLdsMax / 32);
-    if (dw_cb && (o.tile == 4 || (o.tile == 0 && o.group_merge <= 1))) {
+    if (dw_cb && (dw_tile || (o.tile == 0 && o.group_merge <= 1))) {
         out = Plan{};
         out.op = OP_DGRAD;
         out.prob = p;
@@ -562,13 +566,44 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
         a.sd = (int32_t)g.sd; a.sh = (int32_t)g.sh; a.sw = (int32_t)g.sw;
         a.dd = (int32_t)g.dd; a.dh = (int32_t)g.dh; a.dw = (int32_t)g.dw;
         a.pd = (int32_t)g.pd; a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
-        a.cb = dw_cb; a.cbv = dw_cb / 8; a.spw = 256 / a.cbv;
+        a.form = ring_ok && o.tile != 5 ? 2 : 1;
+        // channel block: 8 channels per lane (per-tap form) or kDgRingCh
+        // (row walk), at most 64 lanes
+        int cb = dw_cb;
+        if (a.form == 2) {
+            cb = kDgRingMaxCb;
+            while (p.C % cb) cb >>= 1;
+        }
+        const int lane_ch = a.form == 2 ? kDgRingCh : 8;
+        a.cb = cb; a.cbv = cb / lane_ch; a.spw = 256 / a.cbv;
         a.nstrip = (int32_t)ceil_div(g.Wi, kDgDwStrip);
         const int64_t strips = p.N * g.Di * g.Hi * a.nstrip;
-        const int64_t cblocks = p.C / dw_cb, sgroups = ceil_div(strips, a.spw);
-        if (strips > kMax31 || cblocks * sgroups > kMax31) return fail(msg, U, "grid too large");
+        const int64_t cblocks = p.C / cb;
+        if (strips > kMax31) return fail(msg, U, "grid too large");
         a.strips = (int32_t)strips;
+        int64_t sgroups;
+        if (a.form == 2) {
+            // row chunks per strip: about eight waves per CU (two per SIMD at
+            // the kernel's register use) in as few passes as possible, each
+            // chunk paying two extra rows to fill its window
+            const int64_t per_chunk = p.N * a.nstrip;
+            int64_t best = 1, best_cost = INT64_MAX;
+            for (int64_t nch = 1; nch <= g.Hi; ++nch) {
+                const int64_t waves = cblocks * ceil_div(per_chunk * nch * a.cbv, 64);
+                const int64_t cost = ceil_div(waves, 8 * (int64_t)dev.num_cus) * (ceil_div(g.Hi, nch) + 2);
+                if (cost <= best_cost) { best_cost = cost; best = nch; }
+            }
+            a.nch = (int32_t)best;
+            const int64_t items = per_chunk * best;
+            if (items > kMax31) return fail(msg, U, "grid too large");
+            a.items = (int32_t)items;
+            sgroups = ceil_div(items, a.spw);
+        } else {
+            sgroups = ceil_div(strips, a.spw);
+        }
+        if (cblocks * sgroups > kMax31) return fail(msg, U, "grid too large");
         a.cblocks = (int32_t)cblocks; a.sgroups = (int32_t)sgroups; a.total_wg = (int32_t)(cblocks * sgroups);
+        a.dy_bytes = (uint32_t)(2 * p.N * g.Do * g.Ho * g.Wo * p.C);
         a.out_mode = p.out_dtype == WGRAD_BF16 ? OUT_BF16 : p.out_dtype == WGRAD_FP16 ? OUT_FP16 : OUT_FP32;
         a.msd = make_magic((uint32_t)g.sd); a.msh = make_magic((uint32_t)g.sh); a.msw = make_magic((uint32_t)g.sw);
         wgrad_plan_info& info = out.info;
@@ -578,13 +613,16 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
         }
         info.gemm_m = M; info.gemm_n = 1; info.gemm_k = taps;
         info.variant = WGRAD_VARIANT_DGRAD;
-        info.tile = 4;
-        info.tile_m = kDgDwStrip * a.spw; info.tile_n = dw_cb; info.tile_k = (int32_t)taps;
-        info.split_k = 1; info.group_merge = 1; info.vector_width = 8;
+        info.tile = a.form == 2 ? 4 : 5;
+        info.tile_m = kDgDwStrip * a.spw; info.tile_n = cb; info.tile_k = (int32_t)taps;
+        info.split_k = 1; info.group_merge = 1; info.vector_width = lane_ch;
         info.grid_main = a.total_wg;
         info.num_cus = dev.num_cus;
         char name[160];
-        snprintf(name, sizeof name, "dgrad_dw_%s_cb%d_s%d", out.in_f16 ? "fp16" : "bf16", dw_cb, kDgDwStrip);
+        if (a.form == 2)
+            snprintf(name, sizeof name, "dgrad_dwring_%s_cb%d_s%d_ch%d", out.in_f16 ? "fp16" : "bf16", cb, kDgDwStrip, a.nch);
+        else
+            snprintf(name, sizeof name, "dgrad_dw_%s_cb%d_s%d", out.in_f16 ? "fp16" : "bf16", cb, kDgDwStrip);
         out.name = name;
         return WGRAD_OK;
     }

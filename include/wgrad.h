@@ -195,8 +195,10 @@ int wgrad_run_stage(const wgrad_plan_t* plan, int stage, const void* x, const vo
  * MFMA kernel), variant AUTO or DGRAD, tile 0 (auto) or a
  * dgrad kernel id: 1, 2, 3 = the MFMA kernel with 128x32, 128x64, 128x128
  * (positions x channels) tiles; 4 = the depthwise direct kernel (C/G = K/G
- * = 1, C % 8 == 0, at most 2048 taps), which auto picks for such shapes;
- * anything else is WGRAD_ERR_UNSUPPORTED. wgrad_plan_query reports
+ * = 1, C % 8 == 0, at most 2048 taps), which auto picks for such shapes, in
+ * its row-walking form for 2D 3x3 filters with unit stride and dilation; 5 =
+ * the depthwise kernel's per-tap form for any depthwise shape. Anything else
+ * is WGRAD_ERR_UNSUPPORTED. wgrad_plan_query reports
  * variant DGRAD, gemm_m/n/k as above and workspace_bytes 0.
  * The plan is released with wgrad_plan_destroy; wgrad_run and
  * wgrad_run_stage reject it (and wgrad_dgrad_run rejects backward-weight

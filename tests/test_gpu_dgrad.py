@@ -161,8 +161,13 @@ def test_dgrad_every_tile(tile):
     check_exact(cfg, bits, dx64)
 
 
-# depthwise direct kernel (C/G = K/G = 1)
+# depthwise direct kernel (C/G = K/G = 1); the 3x3 unit-stride shapes take
+# the row-walking form (ragged widths, one-row images, chunks of one row)
 DW = [
+    (2, 64, 3, 1, 1, (9, 10), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+    (2, 128, 1, 1, 1, (1, 7), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "fp16", "fp32"),
+    (2, 32, 2, 1, 1, (6, 5), (3, 3), (1, 1), (0, 2), (2, 0), (1, 1), "bf16", None),
+    (2, 24, 1, 1, 1, (40, 3), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
     (2, 512, 2, 1, 1, (13, 11), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
     (2, 24, 2, 1, 1, (9, 10), (5, 5), (2, 2), (2, 1), (1, 2), (1, 1), "fp16", "fp32"),
     (2, 64, 1, 1, 1, (10, 9), (3, 3), (1, 1), (2, 2), (2, 2), (2, 2), "bf16", None),
@@ -178,7 +183,10 @@ def test_dgrad_depthwise_kernel(i):
     cfg = prob(*DW[i], name=f"dw{i}")
     dyb, wb = draw(cfg, "int", (700 + i, 800 + i))
     _, bits, p = run_dgrad(cfg, dyb, wb)
-    assert p.info["tile"] == 4 and p.name.startswith("dgrad_dw")
+    assert p.info["tile"] in (4, 5) and p.name.startswith("dgrad_dw")
+    # both depthwise forms (row walk where it applies) agree bitwise
+    _, bits5, p5 = run_dgrad(cfg, dyb, wb, tile=5)
+    assert p5.info["tile"] == 5 and np.array_equal(bits, bits5)
     dx64, _ = oracle.dgrad(cfg, dyb, wb)
     check_exact(cfg, bits, dx64)
     # the MFMA kernel on the same shape gives the same (exact) bits
