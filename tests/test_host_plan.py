@@ -345,11 +345,20 @@ def test_dgrad_plans_sizes_and_tiles():
         with pytest.raises(gcb.WgradError):
             dplan(workloads.CONFIGS["c4a"], group_merge=bad)
     # depthwise shapes take the direct kernel; forcing it elsewhere is unsupported
+    # 3x3 unit stride: the row-walking form, 256-channel blocks of 4-channel
+    # lanes, 4 strips per workgroup, row chunks per strip from the planner
     p = dplan(workloads.CONFIGS["c5"])
-    assert p.info["tile"] == 4 and p.name.startswith("dgrad_dw") and p.info["tile_n"] == 512
-    assert p.info["grid_main"] == (16 * 56 * 14 + 3) // 4
+    assert p.info["tile"] == 4 and p.name.startswith("dgrad_dwring") and p.info["tile_n"] == 256
+    nch = int(p.name.rsplit("_ch", 1)[1])
+    assert p.info["grid_main"] == 2 * ((16 * 14 * nch + 3) // 4)
+    # the per-tap form: 512-channel blocks of 8-channel lanes, one strip of a row each
+    p5 = dplan(workloads.CONFIGS["c5"], tile=5)
+    assert p5.info["tile"] == 5 and p5.info["tile_n"] == 512
+    assert p5.info["grid_main"] == (16 * 56 * 14 + 3) // 4
     assert dplan(workloads.CONFIGS["c5"], tile=1).info["tile"] == 1
     assert dplan(dict(workloads.CONFIGS["c5"], G=24, C=24, K=24)).info["tile_n"] == 8
+    # strided depthwise keeps the per-tap form
+    assert dplan(dict(workloads.CONFIGS["c5"], stride=(2, 2))).info["tile"] == 5
     with pytest.raises(gcb.WgradError) as e:
         dplan(cfg, tile=4)
     assert e.value.code == gcb.ERR_UNSUPPORTED
