@@ -21,7 +21,10 @@
 // time into one block-diagonal GEMM (the group merging that rocm-libraries
 // PR 12359 applies to backward weight): the A tile is then a contiguous run
 // of Gm*K/G dY channels and the B tile holds zeros where a row's group
-// differs from a column's.
+// differs from a column's. Strided problems are split into stride phases
+// (see DgradArgs), so every workgroup walks only taps that reach its
+// positions. Depthwise shapes (C/G = K/G = 1) have their own channel-vector
+// kernels at the end of this file.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
