@@ -60,7 +60,7 @@ __device__ __forceinline__ void store4(void* out, int mode, int64_t e, const f32
                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e) = p;
     } else {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + e) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(out) + e));
     }
 }
 
@@ -245,6 +245,10 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
     // swizzle swaps the two 32-column fragments of a 64-wide row
     const int a_sw = MB == 64 ? ((lane >> 3) & 1) : 0;
 
+    // X fragments are the MFMA's first operand and dY fragments its second,
+    // so acc[i][j] holds the transposed 32x32 block: each lane's registers
+    // 4q..4q+3 are four consecutive dW columns of one dW row, which the
+    // epilogue stores to LDS as one 16-byte write.
     f32x16 acc[FM][FNW];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
 #pragma unroll
                 for (int j = 0; j < FNW; ++j)
 #pragma unroll
-                    for (int i2 = 0; i2 < FM; ++i2) mfma_step32<F16>(af[cur][i2], bf[cur][j], acc[i2][j]);
+                    for (int i2 = 0; i2 < FM; ++i2) mfma_step32<F16>(bf[cur][j], af[cur][i2], acc[i2][j]);
 #pragma unroll
                 for (int m = 0; m < FM * FNW; ++m) {
                     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
@@ -313,10 +317,12 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
 #pragma unroll
             for (int fc = 0; fc < FCW; ++fc)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = i * 32 + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
-                    const int col = (half * FCW + fc) * 32 + (lane & 31);
-                    red[pair * TILE + row * RP + col] = acc[i][x * FCW + fc][v];
+                for (int vq = 0; vq < 4; ++vq) {
+                    const int row = i * 32 + (lane & 31);
+                    const int col = (half * FCW + fc) * 32 + 8 * vq + 4 * (lane / 32);
+                    const f32x16& c = acc[i][x * FCW + fc];
+                    *reinterpret_cast<f32x4*>(red + pair * TILE + row * RP + col) =
+                        f32x4{c[4 * vq], c[4 * vq + 1], c[4 * vq + 2], c[4 * vq + 3]};
                 }
         lds_barrier();
         // thread t sums the float4 at row t/(CB/4) + u*(NT/(CB/4)), columns
