@@ -138,7 +138,13 @@ int run_stages(const wgrad_plan_t* plan, int first, int last, const void* x, con
     int e = hipSuccess;
     if (first <= 1) {
         void* main_out = P.info.split_k > 1 ? ws : dw;
-        if (P.variant == WGRAD_VARIANT_ROWSLAB) {
+        if (P.variant == WGRAD_VARIANT_ROWSLAB && P.ring_inst >= 0) {
+            wgrad::RingArgs a = P.ring;
+            a.x = static_cast<const uint16_t*>(x);
+            a.dy = static_cast<const uint16_t*>(dy);
+            a.out = main_out;
+            e = wgrad::launch_ring(P, a, stream);
+        } else if (P.variant == WGRAD_VARIANT_ROWSLAB) {
             wgrad::RowSlabArgs a = P.rs;
             a.x = static_cast<const uint16_t*>(x);
             a.dy = static_cast<const uint16_t*>(dy);

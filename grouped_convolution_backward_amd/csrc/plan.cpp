@@ -176,6 +176,91 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
     return true;
 }
 
+// Filter-row ring plan: 2D, 3x3 filter, dilation 1, h-stride 1..3, w-stride
+// 1 or 2, whole output rows up to 64 positions, merged channel runs that are
+// a multiple of 32. Returns false (with a reason) when the shape does not fit.
+bool plan_ring(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o, const DeviceModel& dev,
+               int out_final, Plan& out, std::string* why) {
+    const int64_t cpg = p.C / p.G, kpg = p.K / p.G;
+    auto no = [&](const char* m) { if (why) *why = m; return false; };
+    if (p.ndim != 2) return no("filter-row ring form needs a 2D problem");
+    if (g.Y != 3 || g.X != 3 || g.dh != 1 || g.dw != 1) return no("filter-row ring form needs a 3x3 filter with dilation 1");
+    if (g.sh > 3 || g.sw > 2) return no("filter-row ring form needs an h-stride of at most 3 and a w-stride of 1 or 2");
+    if (2 * p.N * g.Hi * g.Wi * p.C >= (int64_t{1} << 31) || 2 * p.N * g.Ho * g.Wo * p.K >= (int64_t{1} << 31))
+        return no("filter-row ring form needs X and dY below 2 GiB");
+    int64_t Gm = o.group_merge;
+    if (!Gm) {
+        Gm = 1;
+        while (Gm * cpg < 32 && Gm * 2 <= 8 && p.G % (Gm * 2) == 0) Gm *= 2;
+    }
+    if (!is_pow2(Gm) || p.G % Gm) return no("group_merge must be a power of two dividing G");
+    const int64_t gkpg = Gm * kpg, gcpg = Gm * cpg;
+    if (cpg % 4 || gkpg % 8 || p.K % 8 || p.C % 8) return no("filter-row ring form needs 16-byte channel vectors");
+    if (gcpg % kRingCB) return no("filter-row ring form needs a merged channel run that is a multiple of 32");
+    const int mb = gkpg > 32 ? 64 : 32;
+    const int stride = (int)g.sw;
+    // the smallest row tile that holds a whole output row and its input columns
+    int inst = -1;
+    for (int i = 0; i < kNumRingInstances; ++i) {
+        const RingInstance& r = kRingInstances[i];
+        if (r.mb != mb || r.stride != stride) continue;
+        if (16 * r.nks < g.Wo) continue;
+        if (stride == 1 ? g.Wo + 2 > r.xwp : g.Wo + 1 > r.xwp / 2) continue;
+        if (ring_lds_bytes(r) > kRsLdsMax) continue;
+        if (inst < 0 || 16 * r.nks < 16 * kRingInstances[inst].nks) inst = i;
+    }
+    if (inst < 0) return no("filter-row ring form: no instance holds a whole output row");
+    const RingInstance& ri = kRingInstances[inst];
+    const int64_t NHo = p.N * g.Ho;
+    const int64_t mblocks = ceil_div(gkpg, mb), cblocks = gcpg / kRingCB, gblocks = p.G / Gm;
+    const int64_t tiles = gblocks * mblocks * cblocks;
+    int64_t S;
+    if (NHo == 0) S = 1;
+    else if (o.split_k) S = std::min<int64_t>(o.split_k, NHo);
+    else S = std::max<int64_t>(1, std::min<int64_t>(NHo, (int64_t)dev.num_cus / std::max<int64_t>(1, tiles)));
+    const int64_t rpw = NHo ? ceil_div(NHo, S) : 0;
+    if (NHo) S = ceil_div(NHo, rpw);
+    if (tiles * S > kMax31 || S > 65535) return no("filter-row ring grid too large");
+    const int64_t ndw = p.K * 9 * cpg;
+    RingArgs& a = out.ring;
+    a = RingArgs{};
+    a.Ktot = (int32_t)p.K; a.Ctot = (int32_t)p.C; a.kpg = (int32_t)kpg; a.cpg = (int32_t)cpg;
+    a.gkpg = (int32_t)gkpg; a.gcpg = (int32_t)gcpg;
+    a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo;
+    a.sh = (int32_t)g.sh; a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
+    a.NHo = (int32_t)NHo; a.Mm = (int32_t)gkpg; a.row_len = (int32_t)(9 * cpg);
+    a.mblocks = (int32_t)mblocks; a.cblocks = (int32_t)cblocks; a.tiles = (int32_t)tiles;
+    a.XW = (int32_t)((g.Wo - 1) * g.sw + 3);
+    a.rpw = (int32_t)rpw;
+    a.S = (int32_t)S; a.total_wg = (int32_t)(tiles * S);
+    a.out_mode = S == 1 ? out_final : OUT_WORKSPACE;
+    a.slice_elems = (int32_t)ndw;
+    a.x_bytes = (uint32_t)(2 * p.N * g.Hi * g.Wi * p.C);
+    a.dy_bytes = (uint32_t)(2 * NHo * g.Wo * p.K);
+    a.mHo = make_magic((uint32_t)g.Ho); a.mCpg = make_magic((uint32_t)cpg);
+    out.ring_inst = inst;
+    out.lds_bytes = ring_lds_bytes(ri);
+    wgrad_plan_info& info = out.info;
+    info.tile = 2;
+    info.tile_m = mb; info.tile_n = 9 * kRingCB; info.tile_k = 16 * ri.nks;
+    info.split_k = (int32_t)S;
+    info.group_merge = (int32_t)Gm;
+    info.vector_width = 8;
+    info.grid_main = a.total_wg;
+    info.workspace_bytes = S > 1 ? S * ndw * 4 : 0;
+    return true;
+}
+
+// Auto choice between the two row-slab forms: the ring form stages each
+// row once per workgroup instead of once per filter row, but its workgroup
+// partial spans all nine taps, so it pays off where the stored partial is
+// small (merged groups store only their diagonal blocks).
+bool ring_preferred(const wgrad_problem& p, const Geo& g) {
+    (void)g;
+    const int64_t cpg = p.C / p.G;
+    return cpg < 32 && p.G > 1;
+}
+
 // Validation and spatial geometry shared by both directions.
 int check_problem(const wgrad_problem& p, Geo& g, std::string* msg) {
     const int E = WGRAD_ERR_INVALID_ARG;
@@ -254,6 +339,7 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
     out = Plan{};
     out.prob = p;
     out.in_f16 = p.in_dtype == WGRAD_FP16;
+    out.ring_inst = -1;
     wgrad_plan_info& info = out.info;
     {
         const int64_t all[3] = {g.Do, g.Ho, g.Wo};
@@ -278,9 +364,17 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
     if (variant < WGRAD_VARIANT_AUTO || variant > WGRAD_VARIANT_ROWSLAB)
         return fail(msg, E, "unknown variant %d", variant);
     std::string rs_why;
+    // row-slab forms: the filter-row ring (tile 2) where it applies and is
+    // preferred, else one filter row per workgroup (tile 1)
+    auto plan_rs_forms = [&](int form, std::string* why) {
+        if (form != 1 && ring_preferred(p, g) && plan_ring(p, g, o, dev, out_final, out, nullptr)) return true;
+        if (form == 2) return plan_ring(p, g, o, dev, out_final, out, why);
+        out.ring_inst = -1;
+        return plan_rowslab(p, g, o, dev, out_final, out, why);
+    };
     if (variant == WGRAD_VARIANT_AUTO) {
         if (dw_shape && dw_filter && !o.group_merge && !o.tile) variant = WGRAD_VARIANT_DEPTHWISE;
-        else if (!o.tile && plan_rowslab(p, g, o, dev, out_final, out, &rs_why)) variant = WGRAD_VARIANT_ROWSLAB;
+        else if (!o.tile && plan_rs_forms(0, &rs_why)) variant = WGRAD_VARIANT_ROWSLAB;
         else variant = WGRAD_VARIANT_MFMA;
     }
     if (variant == WGRAD_VARIANT_DEPTHWISE && !(dw_shape && dw_filter))
@@ -290,12 +384,20 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
 
     char name[256];
     if (variant == WGRAD_VARIANT_ROWSLAB) {
-        if (o.tile) return fail(msg, U, "tile applies to the flat-tile MFMA variant only");
-        if (!plan_rowslab(p, g, o, dev, out_final, out, &rs_why)) return fail(msg, U, "%s", rs_why.c_str());
-        const RowSlabArgs& a = out.rs;
-        const RsInstance& ri = kRsInstances[out.rs_inst];
-        snprintf(name, sizeof name, "wgrad_rowslab_%s_m%dc%dx%d_k%d_slab%dx%d_kouter_spk%d_gm%d", dname, ri.mb, ri.cb,
-                 ri.xf, 16 * ri.nks, a.PR, a.SW, a.S, info.group_merge);
+        if (o.tile > 2)
+            return fail(msg, U, "row-slab variant: tile is 0 (auto), 1 (one filter row per workgroup) or 2 (filter-row ring)");
+        if (!plan_rs_forms(o.tile, &rs_why)) return fail(msg, U, "%s", rs_why.c_str());
+        if (out.ring_inst >= 0) {
+            const RingArgs& a = out.ring;
+            const RingInstance& ri = kRingInstances[out.ring_inst];
+            snprintf(name, sizeof name, "wgrad_ring_%s_m%dc%dx3x3_k%d_w%d_s%dx%d_kouter_spk%d_gm%d", dname, ri.mb, kRingCB,
+                     16 * ri.nks, ri.xwp, (int)g.sh, (int)g.sw, a.S, info.group_merge);
+        } else {
+            const RowSlabArgs& a = out.rs;
+            const RsInstance& ri = kRsInstances[out.rs_inst];
+            snprintf(name, sizeof name, "wgrad_rowslab_%s_m%dc%dx%d_k%d_slab%dx%d_kouter_spk%d_gm%d", dname, ri.mb,
+                     ri.cb, ri.xf, 16 * ri.nks, a.PR, a.SW, a.S, info.group_merge);
+        }
     } else if (variant == WGRAD_VARIANT_DEPTHWISE) {
         if (o.group_merge > 1) return fail(msg, U, "group_merge applies to the MFMA variant only");
         DwArgs& a = out.dwk;

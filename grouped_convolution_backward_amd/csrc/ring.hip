@@ -1,0 +1,317 @@
+// Filter-row ring MFMA kernel for grouped convolution backward-weight on
+// gfx950 (2D, 3x3 filter, dilation 1).
+//
+// The implicit GEMM of the Composable Kernel wgrad page (A = dY rows, B = X
+// gathered per filter tap, reduction over r = (n*Ho + ho)*Wo + wo), tiled so
+// that every input row and every dY row enters a workgroup once:
+//
+// * A workgroup owns one (group block, M block, 32-channel C block) tile and
+//   all nine taps: its output tile is MB x (3*3*32). Wave y (0..2) holds the
+//   MB x (3*32) block of filter row y in registers; a fourth wave issues the
+//   loads.
+// * The reduction runs over whole output rows (n, ho) of the workgroup's
+//   split, one at a time. Output row ho reads input rows ho*sh - ph + y for
+//   y = 0..2, so consecutive output rows of one image share 3 - sh of them.
+//   Input rows live in an LDS ring of 3*nb slots: each output row stages its
+//   dY row and only the input rows the previous output row did not already
+//   stage (all three at an image start or at the start of the split), and
+//   wave y reads the slot of its own window row. Within the row, tap x of
+//   position k is the pixel k + x (w-stride 1), or for w-stride 2 a pixel of
+//   the even or odd half of the row tile, so the three taps are shifted
+//   transposed reads of one slot, as in the row-slab kernel.
+// * Output rows are handed over rps at a time (one workgroup barrier per
+//   step), and loads run nb - 1 steps ahead. An output row issues its dY
+//   loads and one group of loads per newly staged input row, so the count
+//   varies; the waits assume the smallest count (one new row), which waits at
+//   least for every load of the step about to be computed. A last step past
+//   the split's end is padded with zero rows (zero dY, zero new input rows),
+//   which add nothing.
+// * MFMA operands come from ds_read_b64_tr_b16 (rocm-libraries PR 11602).
+//   X fragments are the first operand, so each lane's accumulators are four
+//   consecutive dW columns of one dW row, stored straight from registers:
+//   the three waves' tiles are disjoint, so no cross-wave reduction is
+//   needed. Merged groups (PR 12359) store only their diagonal blocks.
+// * Compared with one filter row per workgroup, per-workgroup traffic into
+//   LDS drops about threefold for the same work.
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+
+namespace wgrad {
+namespace {
+
+using namespace dev;
+
+__device__ __forceinline__ void store_quad(void* out, int mode, int64_t e, const f32x4& v) {
+    if (mode == OUT_BF16) {
+        u32x2 p;
+        p[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        p[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e) = p;
+    } else if (mode == OUT_FP16) {
+        u32x2 p;
+        p[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
+        p[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e) = p;
+    } else {
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(out) + e));
+    }
+}
+
+// s_waitcnt that leaves at most min(later, MAXL) * PER of this wave's
+// vector-memory loads outstanding (immediate operands need a branch)
+template <int MAXL, int PER>
+__device__ __forceinline__ void vm_wait_rows(int later) {
+    if constexpr (MAXL > 0) {
+        if (later >= MAXL) {
+            __builtin_amdgcn_s_waitcnt(kWaitVm<MAXL * PER>);
+            return;
+        }
+        vm_wait_rows<MAXL - 1, PER>(later);
+    } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+    }
+}
+
+template <int MB, int NKS, int XWP, int STRIDE, int NB, int RPS, bool F16>
+__global__ __launch_bounds__(256, 1) void ring_kernel(const RingArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    constexpr int CB = kRingCB;
+    constexpr int FM = MB / 32;
+    constexpr int KS = 16 * NKS;                   // positions per output row (padded)
+    constexpr int ACH = MB / 8, XCH = CB / 8;      // 16-byte chunks per position / pixel
+    constexpr int RA = 64 / ACH, RX = 64 / XCH;    // rows one 1 KB load fills
+    constexpr int NA = KS / RA, NXL = XWP / RX;
+    constexpr int NLMIN = NA + NXL;                // loads per output row: one new input row
+    constexpr int NLMAX = NA + 3 * NXL;            // three new input rows (a fresh window)
+    constexpr int ABUF = KS * MB;                  // elements of one dY buffer
+    constexpr int XROW = XWP * CB;                 // elements of one ring slot
+    constexpr int NBR = NB * RPS;                  // dY buffers (one per output row)
+    constexpr int RS = 3 * NBR;                    // ring slots
+    constexpr int HALF = XWP / 2;                  // w-stride 2: odd input columns start here
+    static_assert(KS % RA == 0 && XWP % RX == 0 && (STRIDE == 1 || HALF % RX == 0), "row geometry");
+    static_assert((NB - 1) * RPS * NLMAX <= 63, "vmcnt range");
+    static_assert(NB >= 2, "dY buffers");
+    static_assert(NKS % 2 == 0, "fragment double buffer restarts at 0 each row");
+    static_assert(MB == 32 || MB == 64, "M block");
+    uint16_t* const sA0 = smem;                    // NBR dY buffers
+    uint16_t* const ring = smem + NBR * ABUF;      // RS slots
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0..2 filter row, 3 loads
+
+    const int L = xcd_logical_id(blockIdx.x, a.total_wg);
+    int t = L % a.tiles;
+    const int z = L / a.tiles;
+    const int cbk = t % a.cblocks;
+    t /= a.cblocks;
+    const int mbk = t % a.mblocks;
+    const int gb = t / a.mblocks;
+    const int m0 = mbk * MB, c0 = cbk * CB;
+    const int r_begin = z * a.rpw;
+    const int cnt = max(0, min(a.NHo, r_begin + a.rpw) - r_begin);
+    const int nsteps = (cnt + RPS - 1) / RPS;
+    const int n0 = (int)magic_div((uint32_t)r_begin, a.mHo);
+
+    // output row j of the split: image n, row ho, and the ring position of
+    // its window's first row (it advances by sh within an image and by 3,
+    // a fresh window, at each image start)
+    auto row_of = [&](int j, int& n, int& ho) {
+        const int r = r_begin + j;
+        n = (int)magic_div((uint32_t)r, a.mHo);
+        ho = r - n * a.Ho;
+        return j * a.sh + (n - n0) * (3 - a.sh);
+    };
+
+    if (wave == 3) {
+        const u32x4 dy_desc = buf_desc(a.dy, a.dy_bytes);
+        const u32x4 x_desc = buf_desc(a.x, a.x_bytes);
+        // lane roles, as in the row-slab kernel: dY chunks of 64-channel rows
+        // are XOR-swizzled by bit 1 of the position; 32-channel pixels are not
+        const int ja = lane / ACH;
+        const int a_chunk = (lane % ACH) ^ (MB == 64 ? 4 * ((ja >> 1) & 1) : 0);
+        const bool a_ok = m0 + a_chunk * 8 < a.Mm;
+        const uint32_t a_lane = (uint32_t)((ja * a.Ktot + gb * a.gkpg + m0 + a_chunk * 8) * 2);
+        const uint32_t a_step = (uint32_t)(RA * a.Ktot * 2);
+        const int jx = lane / XCH;
+        const int x_chan = gb * a.gcpg + c0 + (lane % XCH) * 8;
+        auto issue_row = [&](int j) {
+            int n, ho;
+            const int base = row_of(j, n, ho);
+            const bool real = j < cnt;                 // else a zero row padding the last step
+            uint16_t* sA = sA0 + (j % NBR) * ABUF;
+            const uint32_t abase = a_lane + (uint32_t)((r_begin + j) * a.Wo * a.Ktot * 2);
+#pragma unroll
+            for (int l = 0; l < NA; ++l) {
+                const bool ok = real && a_ok && l * RA + ja < a.Wo;
+                dma_load16(dy_desc, lds_addr(sA + l * RA * MB), ok ? abase + l * a_step : kBufOob);
+            }
+            // the window rows the previous output row did not stage (all three
+            // at a window start); rows outside the image are staged as zeros
+            const int w0 = (j == 0 || ho == 0) ? 0 : 3 - a.sh;
+            for (int w = w0; w < 3; ++w) {
+                const int hi = ho * a.sh - a.ph + w;
+                const bool rok = real && (unsigned)hi < (unsigned)a.Hi;
+                uint16_t* dst = ring + ((base + w) % RS) * XROW;
+                const int pixrow = (n * a.Hi + hi) * a.Wi;
+#pragma unroll
+                for (int l = 0; l < NXL; ++l) {
+                    const int pj = l * RX + jx;
+                    const int off = STRIDE == 1 ? pj : (pj < HALF ? 2 * pj : 2 * (pj - HALF) + 1);
+                    const int col = off - a.pw;
+                    const bool ok = rok && off < a.XW && (unsigned)col < (unsigned)a.Wi;
+                    dma_load16(x_desc, lds_addr(dst + l * RX * CB),
+                               ok ? (uint32_t)(((pixrow + col) * a.Ctot + x_chan) * 2) : kBufOob);
+                }
+            }
+        };
+        auto issue_step = [&](int st) {
+#pragma unroll
+            for (int q = 0; q < RPS; ++q) issue_row(st * RPS + q);
+        };
+        // issue steps 0 .. NB-2, then before barrier s+1 issue step s+NB-1
+        // (into the dY buffers step s-1 left) and wait for step s+1
+#pragma unroll
+        for (int st = 0; st < NB - 1; ++st)
+            if (st < nsteps) issue_step(st);
+        if (nsteps > 0) vm_wait_rows<NB - 2, RPS * NLMIN>(min(nsteps - 1, NB - 2));
+        __builtin_amdgcn_s_barrier();
+        for (int st = 0; st < nsteps; ++st) {
+            if (st + NB - 1 < nsteps) issue_step(st + NB - 1);
+            if (st + 1 < nsteps) vm_wait_rows<NB - 2, RPS * NLMIN>(min(nsteps - 2 - st, NB - 2));
+            __builtin_amdgcn_s_barrier();
+        }
+        return;
+    }
+
+    const int y = wave;
+    // lane geometry of the transposed reads: rows frow (+4), columns fcol..fcol+3
+    const int g16 = lane >> 4;
+    const int frow = (g16 >> 1) * 8 + ((lane & 15) >> 2);
+    const int fcol = (g16 & 1) * 16 + (lane & 3) * 4;
+    // element offset inside a ring slot of the pixel each reduction row of
+    // this lane reads for tap 0; rows past Wo read pixel 0 (their dY is zero)
+    int xaddr[NKS][2];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = ks * 16 + frow + 4 * h;
+            xaddr[ks][h] = (k < a.Wo ? k : 0) * CB + fcol;
+        }
+    const int a_sw = MB == 64 ? ((lane >> 3) & 1) : 0;
+
+    f32x16 acc[FM][3];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int x = 0; x < 3; ++x) acc[i][x] = f32x16{0};
+
+    i16x8 af[2][FM], bf[2][3];
+    auto read_frags = [&](const uint16_t* sA, const uint16_t* sX, int ks, i16x8* fa, i16x8* fb) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[i] = tr_frag(sA + (ks * 16 + frow) * MB + (i ^ a_sw) * 32 + fcol, MB);
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+            const int dx = (STRIDE == 1 ? x : (x & 1) * HALF + (x >> 1)) * CB;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sX + xaddr[ks][0] + dx));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sX + xaddr[ks][1] + dx));
+            fb[x] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+    __builtin_amdgcn_s_barrier();
+    for (int st = 0; st < nsteps; ++st) {
+        // the step's rows: dY buffer and this wave's window row slot
+        const uint16_t* sA[RPS];
+        const uint16_t* sX[RPS];
+#pragma unroll
+        for (int q = 0; q < RPS; ++q) {
+            int n, ho;
+            const int j = st * RPS + q;
+            sA[q] = sA0 + (j % NBR) * ABUF;
+            sX[q] = ring + ((row_of(j, n, ho) + y) % RS) * XROW;
+        }
+        // RPS*NKS k-steps, fragments read one k-step ahead across row ends
+        constexpr int T = RPS * NKS;
+        read_frags(sA[0], sX[0], 0, af[0], bf[0]);
+#pragma unroll
+        for (int k = 0; k < T; ++k) {
+            const int cur = k & 1;
+            __builtin_amdgcn_sched_barrier(0);
+            if (k + 1 < T) read_frags(sA[(k + 1) / NKS], sX[(k + 1) / NKS], (k + 1) % NKS, af[cur ^ 1], bf[cur ^ 1]);
+#pragma unroll
+            for (int x = 0; x < 3; ++x)
+#pragma unroll
+                for (int i2 = 0; i2 < FM; ++i2) mfma_step32<F16>(bf[cur][x], af[cur][i2], acc[i2][x]);
+#pragma unroll
+            for (int m = 0; m < FM * 3; ++m) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // step st is consumed (its dY buffers may be refilled) and step st + 1 has landed
+        lds_barrier();
+    }
+
+    // ---- store this filter row's block: lane holds dW row m0 + i*32 + lane%32
+    // and, per vq, four consecutive channels; with merged groups only the
+    // diagonal blocks. Offsets are relative to the tile's first element.
+    const int64_t tile0 = (a.out_mode == OUT_WORKSPACE ? (int64_t)z * a.slice_elems : 0) +
+                          (int64_t)(gb * a.gkpg) * a.row_len + y * 3 * a.cpg;
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) {
+        const int cg = c0 + 8 * vq + 4 * (lane / 32);
+        const int gj = (int)magic_div((uint32_t)cg, a.mCpg);   // group of these channels (cpg % 4 == 0)
+        const int glo = gj * a.kpg;
+        const int cofs = cg - gj * a.cpg;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int mg = m0 + i * 32 + (lane & 31);
+            if (mg < a.Mm && mg >= glo && mg < glo + a.kpg) {
+#pragma unroll
+                for (int x = 0; x < 3; ++x) {
+                    const f32x16& c = acc[i][x];
+                    store_quad(a.out, a.out_mode, tile0 + (mg * a.row_len + x * a.cpg + cofs),
+                               f32x4{c[4 * vq], c[4 * vq + 1], c[4 * vq + 2], c[4 * vq + 3]});
+                }
+            }
+        }
+    }
+}
+
+template <int I, bool F16>
+int launch_ring_i(const Plan& plan, const RingArgs& a, hipStream_t s) {
+    constexpr RingInstance r = kRingInstances[I];
+    auto k = ring_kernel<r.mb, r.nks, r.xwp, r.stride, r.nb, r.rps, F16>;
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes);
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(k, dim3(a.total_wg), dim3(256), plan.lds_bytes, s, a);
+    return (int)hipGetLastError();
+}
+
+template <bool F16>
+int launch_ring_t(const Plan& plan, const RingArgs& a, hipStream_t s) {
+    static_assert(kNumRingInstances == 6, "dispatch table");
+    switch (plan.ring_inst) {
+        case 0: return launch_ring_i<0, F16>(plan, a, s);
+        case 1: return launch_ring_i<1, F16>(plan, a, s);
+        case 2: return launch_ring_i<2, F16>(plan, a, s);
+        case 3: return launch_ring_i<3, F16>(plan, a, s);
+        case 4: return launch_ring_i<4, F16>(plan, a, s);
+        case 5: return launch_ring_i<5, F16>(plan, a, s);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int launch_ring(const Plan& plan, const RingArgs& a, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return plan.in_f16 ? launch_ring_t<true>(plan, a, s) : launch_ring_t<false>(plan, a, s);
+}
+
+}  // namespace wgrad

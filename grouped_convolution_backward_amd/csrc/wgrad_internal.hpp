@@ -96,6 +96,49 @@ struct RowSlabArgs {
     MagicU32 mSW, mXW, mHo, mDo;
 };
 
+// Filter-row ring kernel (2D, 3x3 filter, dilation 1, h-stride 1 or 2): a
+// workgroup owns one (group block, M block, 32-channel C block) tile and all
+// three filter rows, one MFMA wave per filter row; it walks consecutive
+// output rows of its split, staging each dY row once and each input row once
+// into an LDS ring that the three waves read at their own row offset.
+// Instances fix the M block, the positions per row (16*nks >= Wo), the X row
+// width in pixels and the w-stride; nb dY buffers, loaded nb - 1 rows ahead.
+struct RingInstance {
+    int mb, nks, xwp, stride, nb, rps;
+};
+constexpr RingInstance kRingInstances[] = {
+    {32, 2, 32, 1, 4, 2},    // rows up to 30 wide
+    {64, 2, 32, 1, 3, 2},
+    {32, 4, 64, 1, 4, 1},    // rows up to 62 wide
+    {64, 4, 64, 1, 4, 1},
+    {32, 2, 64, 2, 4, 1},    // w-stride 2, rows up to 31 wide
+    {64, 2, 64, 2, 4, 1},
+};
+constexpr int kNumRingInstances = sizeof(kRingInstances) / sizeof(kRingInstances[0]);
+constexpr int kRingCB = 32;                       // channels per C block
+constexpr int ring_slots(const RingInstance& r) { return 3 * r.nb * r.rps; }
+inline int ring_lds_bytes(const RingInstance& r) {
+    return 2 * (r.nb * r.rps * 16 * r.nks * r.mb + ring_slots(r) * r.xwp * kRingCB);
+}
+
+struct RingArgs {
+    const uint16_t* x;
+    const uint16_t* dy;
+    void* out;
+    int32_t Ktot, Ctot, kpg, cpg, gkpg, gcpg;
+    int32_t Hi, Wi, Ho, Wo;
+    int32_t sh, ph, pw;      // h-stride and left pads (dilations 1, 3x3 filter)
+    int32_t NHo;             // N*Ho output rows
+    int32_t Mm;              // merged M = Gm*kpg
+    int32_t row_len;         // 9*cpg: length of one dW row
+    int32_t mblocks, cblocks, tiles;
+    int32_t XW;              // input columns one output row reads: (Wo-1)*sw + 3
+    int32_t rpw;             // output rows per workgroup (one split)
+    int32_t S, total_wg, out_mode, slice_elems;
+    uint32_t x_bytes, dy_bytes;
+    MagicU32 mHo, mCpg;
+};
+
 // Depthwise (C/G = K/G = 1) channel-vector kernel.
 struct DwArgs {
     const uint16_t* x;
@@ -205,6 +248,8 @@ struct Plan {
     int dw3_ty;                  // filter height of the strip depthwise instance (0 = not used)
     RowSlabArgs rs;
     int rs_inst;                 // index into kRsInstances
+    RingArgs ring;
+    int ring_inst;               // index into kRingInstances, or -1 (row-slab variant: per-filter-row form)
     int lds_bytes;               // dynamic LDS of the main kernel
     ReduceArgs red;
     int dw_tile_y, dw_tile_x;   // depthwise kernel filter instance
@@ -225,6 +270,7 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
 int launch_mfma(const Plan& plan, const MfmaArgs& a, void* stream);
 int launch_depthwise(const Plan& plan, const DwArgs& a, void* stream);
 int launch_rowslab(const Plan& plan, const RowSlabArgs& a, void* stream);
+int launch_ring(const Plan& plan, const RingArgs& a, void* stream);          // ring.hip
 int launch_depthwise2(const Plan& plan, const Dw2Args& a, void* stream);
 int launch_depthwise3(const Plan& plan, const Dw3Args& a, void* stream);
 int launch_reduce(const ReduceArgs& a, int64_t grid, void* stream);

@@ -79,9 +79,12 @@ typedef enum {
     WGRAD_VARIANT_AUTO = 0,
     WGRAD_VARIANT_MFMA = 1,      /* MFMA implicit GEMM over flat K tiles, any shape, optional group merge */
     WGRAD_VARIANT_DEPTHWISE = 2, /* C/G = K/G = 1: channel-vector direct kernel */
-    WGRAD_VARIANT_ROWSLAB = 3,   /* MFMA implicit GEMM over slabs of output rows, one filter row per
-                                    tile, X staged once per row (filter width 1, 3 or 5, w-dilation 1,
-                                    channel runs multiple of 32), optional group merge */
+    WGRAD_VARIANT_ROWSLAB = 3,   /* MFMA implicit GEMM over slabs of output rows, X staged once per
+                                    row (channel runs multiple of 32), optional group merge. Two forms:
+                                    one filter row per workgroup (filter width 1, 3 or 5, w-dilation
+                                    1), or, for 2D 3x3 filters with dilation 1, h-stride <= 3,
+                                    w-stride <= 2 and output rows up to 62 wide, every filter row per
+                                    workgroup with input rows kept in an LDS ring */
     WGRAD_VARIANT_DGRAD = 4      /* backward data (wgrad_dgrad_plan only): MFMA implicit GEMM over
                                     input positions, reduction over (tap, K/G) */
 } wgrad_variant;
@@ -95,7 +98,8 @@ typedef struct {
     int32_t tile;         /* MFMA variant: tile id (see wgrad_plan_info.tile). DEPTHWISE variant:
                              kernel form, 1 = generic filter, 2 = windowed (filter width 3,
                              w-stride 1, w-dilation 1), 3 = strip (3x3, stride 1, dilation 1).
-                             0 = auto */
+                             ROWSLAB variant: form, 1 = one filter row per workgroup, 2 = every
+                             filter row per workgroup (input-row ring). 0 = auto */
 } wgrad_overrides;
 
 /* What a plan decided, for logging and tests. */
@@ -105,7 +109,8 @@ typedef struct {
     int64_t gemm_n;          /* (C/G)*Z*Y*X */
     int64_t gemm_k;          /* N*Do*Ho*Wo */
     int32_t variant;         /* wgrad_variant actually used */
-    int32_t tile;            /* MFMA tile id, depthwise kernel form (1 generic, 2 windowed, 3 strip), or 0 */
+    int32_t tile;            /* MFMA tile id, depthwise kernel form (1 generic, 2 windowed, 3 strip),
+                                2 for the row-slab ring form, or 0 (row-slab, one filter row) */
     int32_t tile_m, tile_n, tile_k;
     int32_t split_k;         /* S */
     int32_t group_merge;     /* Gm */

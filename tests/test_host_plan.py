@@ -399,3 +399,46 @@ def test_dgrad_plan_rejections_and_plan_kinds():
     e = dplan(dict(cfg, N=0))
     assert e.info["grid_main"] == 0
     assert lib.wgrad_dgrad_run(e.handle, None, None, None, None) == gcb.OK
+
+
+def test_ring_form_plans():
+    # the grouped 3x3 workload takes the filter-row ring form: one workgroup
+    # per (group block, M block, 32-channel block) and split, all nine taps
+    c4a = workloads.CONFIGS["c4a"]
+    p = plan(c4a)
+    assert p.info["variant"] == gcb.VARIANT_ROWSLAB and p.info["tile"] == 2
+    assert p.name.startswith("wgrad_ring_bf16_m32c32x3x3") and p.name.endswith("gm4")
+    Gm, S = p.info["group_merge"], p.info["split_k"]
+    assert Gm == 4 and p.info["tile_n"] == 9 * 32
+    assert p.info["grid_main"] == (c4a["G"] // Gm) * S
+    rows = c4a["N"] * p.info["out_len"][0]
+    rpw = -(-rows // S)
+    assert -(-rows // rpw) == S and S <= 256
+    assert p.workspace_bytes == S * c4a["K"] * 9 * (c4a["C"] // c4a["G"]) * 4
+    # the one-filter-row form is still there by request
+    p1 = plan(c4a, variant=gcb.VARIANT_ROWSLAB, tile=1)
+    assert p1.info["tile"] == 0 and p1.name.startswith("wgrad_rowslab_")
+    # dense shapes keep one filter row per workgroup unless asked
+    c2 = workloads.CONFIGS["c2"]
+    assert plan(c2).name.startswith("wgrad_rowslab_")
+    p2 = plan(c2, variant=gcb.VARIANT_ROWSLAB, tile=2)
+    assert p2.name.startswith("wgrad_ring_bf16_m64c32") and p2.info["grid_main"] == 2 * p2.info["split_k"]
+    # stride 2 in w picks a stride-2 row tile; the split never exceeds the rows
+    p3 = plan(workloads.CONFIGS["c3"], variant=gcb.VARIANT_ROWSLAB, tile=2)
+    assert "_s2x2_" in p3.name
+    assert plan(c4a, variant=gcb.VARIANT_ROWSLAB, tile=2, split_k=10 ** 6).info["split_k"] == rows
+
+
+def test_ring_form_rejections():
+    c4a = workloads.CONFIGS["c4a"]
+    ring = dict(variant=gcb.VARIANT_ROWSLAB, tile=2)
+    _expect(gcb.ERR_UNSUPPORTED, workloads.CONFIGS["c4b"], **ring)                  # 1D
+    _expect(gcb.ERR_UNSUPPORTED, workloads.get("pw"), **ring)                       # 1x1 filter
+    _expect(gcb.ERR_UNSUPPORTED, workloads.problem(c4a, dilation=(2, 1)), **ring)   # dilation
+    _expect(gcb.ERR_UNSUPPORTED, workloads.problem(c4a, stride=(1, 3)), **ring)     # w-stride 3
+    _expect(gcb.ERR_UNSUPPORTED, workloads.problem(c4a, stride=(4, 1)), **ring)     # h-stride 4
+    _expect(gcb.ERR_UNSUPPORTED, workloads.problem(c4a, in_len=(28, 100)), **ring)  # rows wider than 62
+    _expect(gcb.ERR_UNSUPPORTED, workloads.CONFIGS["c5"], **ring)                   # 1-channel groups
+    _expect(gcb.ERR_UNSUPPORTED, c4a, variant=gcb.VARIANT_ROWSLAB, tile=3)
+    # where the ring form does not apply, auto falls back to one filter row per workgroup
+    assert plan(workloads.problem(c4a, in_len=(28, 100))).name.startswith("wgrad_rowslab_")
