@@ -7,8 +7,9 @@
 //
 // * A workgroup owns one (group block, M block, 32-channel C block) tile and
 //   all nine taps: its output tile is MB x (3*3*32). Wave y (0..2) holds the
-//   MB x (3*32) block of filter row y in registers; a fourth wave issues the
-//   loads.
+//   MB x (3*32) block of filter row y in registers; two more waves issue the
+//   loads, one the dY rows and one the input rows, each counting only its
+//   own outstanding loads, so more rows can be in flight.
 // * The reduction runs over whole output rows (n, ho) of the workgroup's
 //   split, one at a time. Output row ho reads input rows ho*sh - ph + y for
 //   y = 0..2, so consecutive output rows of one image share 3 - sh of them.
@@ -26,6 +27,14 @@
 //   least for every load of the step about to be computed. A last step past
 //   the split's end is padded with zero rows (zero dY, zero new input rows),
 //   which add nothing.
+// * w-stride 1: a lane's operand for tap x is its tap-0 operand moved x
+//   positions along the reduction: the eight positions a lane holds continue
+//   in the lane 32 above it (and, for the upper half, in the next k-step), so
+//   taps 1 and 2 are built in registers from the tap-0 fragment with one
+//   cross-half lane swap (v_permlane32_swap) and 16-bit funnel shifts,
+//   instead of two more LDS reads each. Past a row's last k-step the missing
+//   positions are zero: they meet only reduction rows past the row's end,
+//   whose dY is zero.
 // * MFMA operands come from ds_read_b64_tr_b16 (rocm-libraries PR 11602).
 //   X fragments are the first operand, so each lane's accumulators are four
 //   consecutive dW columns of one dW row, stored straight from registers:
@@ -41,24 +50,6 @@ namespace wgrad {
 namespace {
 
 using namespace dev;
-
-__device__ __forceinline__ void store_quad(void* out, int mode, int64_t e, const f32x4& v) {
-    if (mode == OUT_BF16) {
-        u32x2 p;
-        p[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        p[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e) = p;
-    } else if (mode == OUT_FP16) {
-        u32x2 p;
-        p[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
-        p[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e) = p;
-    } else {
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(out) + e));
-    }
-}
 
 // s_waitcnt that leaves at most min(later, MAXL) * PER of this wave's
 // vector-memory loads outstanding (immediate operands need a branch)
@@ -76,7 +67,7 @@ __device__ __forceinline__ void vm_wait_rows(int later) {
 }
 
 template <int MB, int NKS, int XWP, int STRIDE, int NB, int RPS, bool F16>
-__global__ __launch_bounds__(256, 1) void ring_kernel(const RingArgs a) {
+__global__ __launch_bounds__(320, 1) void ring_kernel(const RingArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     constexpr int CB = kRingCB;
     constexpr int FM = MB / 32;
@@ -84,15 +75,15 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(const RingArgs a) {
     constexpr int ACH = MB / 8, XCH = CB / 8;      // 16-byte chunks per position / pixel
     constexpr int RA = 64 / ACH, RX = 64 / XCH;    // rows one 1 KB load fills
     constexpr int NA = KS / RA, NXL = XWP / RX;
-    constexpr int NLMIN = NA + NXL;                // loads per output row: one new input row
-    constexpr int NLMAX = NA + 3 * NXL;            // three new input rows (a fresh window)
+    // loads per output row: NA dY loads (one producer), NXL per newly staged
+    // input row (the other): one row, or three at a fresh window
     constexpr int ABUF = KS * MB;                  // elements of one dY buffer
     constexpr int XROW = XWP * CB;                 // elements of one ring slot
     constexpr int NBR = NB * RPS;                  // dY buffers (one per output row)
     constexpr int RS = 3 * NBR;                    // ring slots
     constexpr int HALF = XWP / 2;                  // w-stride 2: odd input columns start here
     static_assert(KS % RA == 0 && XWP % RX == 0 && (STRIDE == 1 || HALF % RX == 0), "row geometry");
-    static_assert((NB - 1) * RPS * NLMAX <= 63, "vmcnt range");
+    static_assert((NB - 1) * RPS * NA <= 63 && (NB - 1) * RPS * 3 * NXL <= 63, "vmcnt range");
     static_assert(NB >= 2, "dY buffers");
     static_assert(NKS % 2 == 0, "fragment double buffer restarts at 0 each row");
     static_assert(MB == 32 || MB == 64, "M block");
@@ -100,7 +91,7 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(const RingArgs a) {
     uint16_t* const ring = smem + NBR * ABUF;      // RS slots
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0..2 filter row, 3 loads
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0..2 filter row, 3 and 4 loads
 
     const int L = xcd_logical_id(blockIdx.x, a.total_wg);
     int t = L % a.tiles;
@@ -125,7 +116,8 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(const RingArgs a) {
         return j * a.sh + (n - n0) * (3 - a.sh);
     };
 
-    if (wave == 3) {
+    if (wave >= 3) {
+        const bool dy_part = wave == 3;            // wave 3 loads dY rows, wave 4 input rows
         const u32x4 dy_desc = buf_desc(a.dy, a.dy_bytes);
         const u32x4 x_desc = buf_desc(a.x, a.x_bytes);
         // lane roles, as in the row-slab kernel: dY chunks of 64-channel rows
@@ -137,16 +129,34 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(const RingArgs a) {
         const uint32_t a_step = (uint32_t)(RA * a.Ktot * 2);
         const int jx = lane / XCH;
         const int x_chan = gb * a.gcpg + c0 + (lane % XCH) * 8;
+        // the per-lane part of every load is the same for all rows: dY byte
+        // offsets within a row (or out of range past Wo), and input-row byte
+        // offsets of this lane's pixels (or out of range outside the row)
+        uint32_t a_off[NA], x_off[NXL];
+#pragma unroll
+        for (int l = 0; l < NA; ++l)
+            a_off[l] = a_ok && l * RA + ja < a.Wo ? a_lane + l * a_step : kBufOob;
+#pragma unroll
+        for (int l = 0; l < NXL; ++l) {
+            const int pj = l * RX + jx;
+            const int off = STRIDE == 1 ? pj : (pj < HALF ? 2 * pj : 2 * (pj - HALF) + 1);
+            const int col = off - a.pw;
+            x_off[l] = off < a.XW && (unsigned)col < (unsigned)a.Wi ? (uint32_t)((col * a.Ctot + x_chan) * 2) : kBufOob;
+        }
+        const uint32_t a_row = (uint32_t)(a.Wo * a.Ktot * 2), x_row = (uint32_t)(a.Wi * a.Ctot * 2);
+        // an out-of-range lane offset stays out of range (>= 2^31) after a row
+        // base below 2 GiB is added, so the row's own check is one select
         auto issue_row = [&](int j) {
             int n, ho;
             const int base = row_of(j, n, ho);
             const bool real = j < cnt;                 // else a zero row padding the last step
-            uint16_t* sA = sA0 + (j % NBR) * ABUF;
-            const uint32_t abase = a_lane + (uint32_t)((r_begin + j) * a.Wo * a.Ktot * 2);
+            if (dy_part) {
+                uint16_t* sA = sA0 + (j % NBR) * ABUF;
+                const uint32_t rb = (uint32_t)(r_begin + j) * a_row;
 #pragma unroll
-            for (int l = 0; l < NA; ++l) {
-                const bool ok = real && a_ok && l * RA + ja < a.Wo;
-                dma_load16(dy_desc, lds_addr(sA + l * RA * MB), ok ? abase + l * a_step : kBufOob);
+                for (int l = 0; l < NA; ++l)
+                    dma_load16(dy_desc, lds_addr(sA + l * RA * MB), real ? rb + a_off[l] : kBufOob);
+                return;
             }
             // the window rows the previous output row did not stage (all three
             // at a window start); rows outside the image are staged as zeros
@@ -155,16 +165,10 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(const RingArgs a) {
                 const int hi = ho * a.sh - a.ph + w;
                 const bool rok = real && (unsigned)hi < (unsigned)a.Hi;
                 uint16_t* dst = ring + ((base + w) % RS) * XROW;
-                const int pixrow = (n * a.Hi + hi) * a.Wi;
+                const uint32_t rb = (uint32_t)(n * a.Hi + hi) * x_row;
 #pragma unroll
-                for (int l = 0; l < NXL; ++l) {
-                    const int pj = l * RX + jx;
-                    const int off = STRIDE == 1 ? pj : (pj < HALF ? 2 * pj : 2 * (pj - HALF) + 1);
-                    const int col = off - a.pw;
-                    const bool ok = rok && off < a.XW && (unsigned)col < (unsigned)a.Wi;
-                    dma_load16(x_desc, lds_addr(dst + l * RX * CB),
-                               ok ? (uint32_t)(((pixrow + col) * a.Ctot + x_chan) * 2) : kBufOob);
-                }
+                for (int l = 0; l < NXL; ++l)
+                    dma_load16(x_desc, lds_addr(dst + l * RX * CB), rok ? rb + x_off[l] : kBufOob);
             }
         };
         auto issue_step = [&](int st) {
@@ -176,11 +180,17 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(const RingArgs a) {
 #pragma unroll
         for (int st = 0; st < NB - 1; ++st)
             if (st < nsteps) issue_step(st);
-        if (nsteps > 0) vm_wait_rows<NB - 2, RPS * NLMIN>(min(nsteps - 1, NB - 2));
+        // each producer waits for its own loads of the step: dY rows are NA
+        // loads each, input rows at least NXL (one new row)
+        auto wait_step = [&](int later) {
+            if (dy_part) vm_wait_rows<NB - 2, RPS * NA>(later);
+            else vm_wait_rows<NB - 2, RPS * NXL>(later);
+        };
+        if (nsteps > 0) wait_step(min(nsteps - 1, NB - 2));
         __builtin_amdgcn_s_barrier();
         for (int st = 0; st < nsteps; ++st) {
             if (st + NB - 1 < nsteps) issue_step(st + NB - 1);
-            if (st + 1 < nsteps) vm_wait_rows<NB - 2, RPS * NLMIN>(min(nsteps - 2 - st, NB - 2));
+            if (st + 1 < nsteps) wait_step(min(nsteps - 2 - st, NB - 2));
             __builtin_amdgcn_s_barrier();
         }
         return;
@@ -192,14 +202,18 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(const RingArgs a) {
     const int frow = (g16 >> 1) * 8 + ((lane & 15) >> 2);
     const int fcol = (g16 & 1) * 16 + (lane & 3) * 4;
     // element offset inside a ring slot of the pixel each reduction row of
-    // this lane reads for tap 0; rows past Wo read pixel 0 (their dY is zero)
+    // this lane reads for tap 0. w-stride 1: every row reads its own pixel
+    // (the row tile is KS pixels wide, so all are in the slot; pixels past the
+    // input row are zeros), which the register shifts rely on. w-stride 2:
+    // rows past Wo read pixel 0 (their dY is zero).
+    static_assert(STRIDE != 1 || XWP == KS, "w-stride 1 row tiles are one pixel per position");
     int xaddr[NKS][2];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int k = ks * 16 + frow + 4 * h;
-            xaddr[ks][h] = (k < a.Wo ? k : 0) * CB + fcol;
+            xaddr[ks][h] = (STRIDE == 1 || k < a.Wo ? k : 0) * CB + fcol;
         }
     const int a_sw = MB == 64 ? ((lane >> 3) & 1) : 0;
 
@@ -235,6 +249,52 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(const RingArgs a) {
         }
         // RPS*NKS k-steps, fragments read one k-step ahead across row ends
         constexpr int T = RPS * NKS;
+        if constexpr (STRIDE == 1) {
+            // tap 0 of k-step t, then taps 1 and 2 of k-step t - 1, whose
+            // shifted operand needs k-step t's tap-0 fragment (same row) or
+            // zeros (t - 1 ends a row); fragments are read two k-steps ahead,
+            // so those of t - 1 .. t + 2 are live
+            i16x8 fa[4][FM], fx[4];
+            auto read_t = [&](int tt, int sl) {
+                const int q = tt / NKS, ks = tt % NKS;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    fa[sl][i] = tr_frag(sA[q] + (ks * 16 + frow) * MB + (i ^ a_sw) * 32 + fcol, MB);
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sX[q] + xaddr[ks][0]));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sX[q] + xaddr[ks][1]));
+                fx[sl] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            auto shifted_taps = [&](int sl, int nsl) {
+                const u32x4 w = __builtin_bit_cast(u32x4, fx[sl]);
+                const uint32_t nw0 = nsl >= 0 ? __builtin_bit_cast(u32x4, fx[nsl])[0] : 0u;
+                // lanes 0..31 continue in lane + 32, lanes 32..63 in the next k-step's lane - 32
+                const auto sw = __builtin_amdgcn_permlane32_swap(w[0], nw0, false, false);
+                const uint32_t ext = lane < 32 ? sw[1] : sw[0];
+                const u32x4 s1 = {__builtin_amdgcn_alignbit(w[1], w[0], 16), __builtin_amdgcn_alignbit(w[2], w[1], 16),
+                                  __builtin_amdgcn_alignbit(w[3], w[2], 16), __builtin_amdgcn_alignbit(ext, w[3], 16)};
+                const u32x4 s2 = {w[1], w[2], w[3], ext};
+#pragma unroll
+                for (int i2 = 0; i2 < FM; ++i2) {
+                    mfma_step32<F16>(__builtin_bit_cast(i16x8, s1), fa[sl][i2], acc[i2][1]);
+                    mfma_step32<F16>(__builtin_bit_cast(i16x8, s2), fa[sl][i2], acc[i2][2]);
+                }
+            };
+            read_t(0, 0);
+            if (T > 1) read_t(1, 1);
+#pragma unroll
+            for (int tt = 0; tt < T; ++tt) {
+                const int c = tt % 4;
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i2 = 0; i2 < FM; ++i2) mfma_step32<F16>(fx[c], fa[c][i2], acc[i2][0]);
+                if (tt > 0) shifted_taps((tt - 1) % 4, tt % NKS ? c : -1);
+                // issued after this k-step's operands are in registers, so the
+                // waits for k-step t never cover the reads of t + 1 and t + 2
+                if (tt + 2 < T) read_t(tt + 2, (tt + 2) % 4);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            shifted_taps((T - 1) % 4, -1);
+        } else {
         read_frags(sA[0], sX[0], 0, af[0], bf[0]);
 #pragma unroll
         for (int k = 0; k < T; ++k) {
@@ -253,6 +313,7 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(const RingArgs a) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        }
         // step st is consumed (its dY buffers may be refilled) and step st + 1 has landed
         lds_barrier();
     }
@@ -262,24 +323,48 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(const RingArgs a) {
     // diagonal blocks. Offsets are relative to the tile's first element.
     const int64_t tile0 = (a.out_mode == OUT_WORKSPACE ? (int64_t)z * a.slice_elems : 0) +
                           (int64_t)(gb * a.gkpg) * a.row_len + y * 3 * a.cpg;
+    auto store_all = [&](auto put) {
 #pragma unroll
-    for (int vq = 0; vq < 4; ++vq) {
-        const int cg = c0 + 8 * vq + 4 * (lane / 32);
-        const int gj = (int)magic_div((uint32_t)cg, a.mCpg);   // group of these channels (cpg % 4 == 0)
-        const int glo = gj * a.kpg;
-        const int cofs = cg - gj * a.cpg;
+        for (int vq = 0; vq < 4; ++vq) {
+            const int cg = c0 + 8 * vq + 4 * (lane / 32);
+            const int gj = (int)magic_div((uint32_t)cg, a.mCpg);   // group of these channels (cpg % 4 == 0)
+            const int glo = gj * a.kpg;
+            const int cofs = cg - gj * a.cpg;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int mg = m0 + i * 32 + (lane & 31);
-            if (mg < a.Mm && mg >= glo && mg < glo + a.kpg) {
+            for (int i = 0; i < FM; ++i) {
+                const int mg = m0 + i * 32 + (lane & 31);
+                if (mg < a.Mm && mg >= glo && mg < glo + a.kpg) {
 #pragma unroll
-                for (int x = 0; x < 3; ++x) {
-                    const f32x16& c = acc[i][x];
-                    store_quad(a.out, a.out_mode, tile0 + (mg * a.row_len + x * a.cpg + cofs),
-                               f32x4{c[4 * vq], c[4 * vq + 1], c[4 * vq + 2], c[4 * vq + 3]});
+                    for (int x = 0; x < 3; ++x) {
+                        const f32x16& c = acc[i][x];
+                        put(mg * a.row_len + x * a.cpg + cofs, f32x4{c[4 * vq], c[4 * vq + 1], c[4 * vq + 2], c[4 * vq + 3]});
+                    }
                 }
             }
         }
+    };
+    // one loop per output type, so that no store carries the type switch
+    if (a.out_mode == OUT_WORKSPACE || a.out_mode == OUT_FP32) {
+        float* o = static_cast<float*>(a.out) + tile0;
+        store_all([&](int e, const f32x4& v) { __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(o + e)); });
+    } else if (a.out_mode == OUT_BF16) {
+        uint16_t* o = static_cast<uint16_t*>(a.out) + tile0;
+        store_all([&](int e, const f32x4& v) {
+            u32x2 p;
+            p[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+            p[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+            *reinterpret_cast<u32x2*>(o + e) = p;
+        });
+    } else {
+        uint16_t* o = static_cast<uint16_t*>(a.out) + tile0;
+        store_all([&](int e, const f32x4& v) {
+            u32x2 p;
+            p[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
+            p[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
+            *reinterpret_cast<u32x2*>(o + e) = p;
+        });
     }
 }
 
@@ -289,7 +374,7 @@ int launch_ring_i(const Plan& plan, const RingArgs& a, hipStream_t s) {
     auto k = ring_kernel<r.mb, r.nks, r.xwp, r.stride, r.nb, r.rps, F16>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes);
     if (e != hipSuccess) return (int)e;
-    hipLaunchKernelGGL(k, dim3(a.total_wg), dim3(256), plan.lds_bytes, s, a);
+    hipLaunchKernelGGL(k, dim3(a.total_wg), dim3(320), plan.lds_bytes, s, a);
     return (int)hipGetLastError();
 }
 

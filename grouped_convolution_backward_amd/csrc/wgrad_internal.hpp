@@ -107,8 +107,8 @@ struct RingInstance {
     int mb, nks, xwp, stride, nb, rps;
 };
 constexpr RingInstance kRingInstances[] = {
-    {32, 2, 32, 1, 4, 2},    // rows up to 30 wide
-    {64, 2, 32, 1, 3, 2},
+    {32, 2, 32, 1, 3, 4},    // rows up to 30 wide
+    {64, 2, 32, 1, 3, 4},
     {32, 4, 64, 1, 4, 1},    // rows up to 62 wide
     {64, 4, 64, 1, 4, 1},
     {32, 2, 64, 2, 4, 1},    // w-stride 2, rows up to 31 wide
