@@ -69,8 +69,8 @@ def algorithmic(cfg, info):
 # the source files each kernel family is built from (besides the shared
 # device helpers and argument headers); a traffic record is valid only for
 # the exact bytes of these files
-_FAMILY_SOURCES = (("wgrad_rowslab", "rowslab.hip"), ("wgrad_mfma", "kernels.hip"), ("wgrad_dw", "depthwise.hip"),
-                   ("dgrad_", "dgrad.hip"))
+_FAMILY_SOURCES = (("wgrad_rowslab", "rowslab.hip"), ("wgrad_ring", "ring.hip"), ("wgrad_mfma", "kernels.hip"),
+                   ("wgrad_dw", "depthwise.hip"), ("dgrad_", "dgrad.hip"))
 _SHARED_SOURCES = ("device_common.hpp", "wgrad_internal.hpp", "dgrad_internal.hpp", "magic.hpp")
 
 
