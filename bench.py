@@ -70,13 +70,13 @@ def algorithmic(cfg, info):
 # device helpers and argument headers); a traffic record is valid only for
 # the exact bytes of these files
 _FAMILY_SOURCES = (("wgrad_rowslab", "rowslab.hip"), ("wgrad_ring", "ring.hip"), ("wgrad_mfma", "kernels.hip"),
-                   ("wgrad_dw", "depthwise.hip"), ("dgrad_", "dgrad.hip"))
+                   ("wgrad_dw", "depthwise.hip"), ("dgrad_ring", "dgrad_ring.hip"), ("dgrad_", "dgrad.hip"))
 _SHARED_SOURCES = ("device_common.hpp", "wgrad_internal.hpp", "dgrad_internal.hpp", "magic.hpp")
 
 
 def kernel_source_hash(plan_name):
     """Hash of the sources the named plan's main kernel is compiled from."""
-    own = [f for pre, f in _FAMILY_SOURCES if plan_name.startswith(pre)]
+    own = [f for pre, f in _FAMILY_SOURCES if plan_name.startswith(pre)][:1]
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "grouped_convolution_backward_amd", "csrc")
     for f in sorted(own + list(_SHARED_SOURCES)):

@@ -68,6 +68,42 @@ struct DgradDwArgs {
     int32_t nch, items;
     uint32_t dy_bytes;
 };
+// Row-ring backward data (2D, 3x3 filter, unit stride and dilation): a
+// workgroup owns one group block and one block of cbd dX channels, keeps that
+// block's weights in LDS for the whole launch, and walks its split of input
+// rows four at a time, one row per MFMA wave. Input rows are numbered
+// "virtually", Hi + 2 per image (the last two are padding rows that are
+// computed but not stored), so that dY row u = v + ph - y of virtual input
+// row v is the same for every image and a window of dY rows can be kept in
+// an LDS ring across the rows of a step and from one step to the next.
+struct DgradRingInstance {
+    int cbd, mt, ch;     // dX channels per block, 32-position M tiles per row, 8-channel dY chunks per pixel
+};
+constexpr DgradRingInstance kDgRingInstances[] = {
+    {32, 1, 4}, {32, 2, 4}, {64, 1, 4}, {64, 2, 4},
+    {32, 1, 8}, {32, 2, 8}, {64, 1, 8}, {64, 2, 8},
+};
+constexpr int kNumDgRingInstances = sizeof(kDgRingInstances) / sizeof(kDgRingInstances[0]);
+constexpr int kDgRingSlots = 10;         // a step's 6-row dY window plus the next step's 4 rows
+constexpr int kDgRingLdsMax = 160 * 1024;
+struct DgradRingArgs {
+    const uint16_t* dy;
+    const uint16_t* w;
+    void* dx;
+    int32_t Ktot, Ctot, kpg, cpg, Gm, gkpg, gcpg;
+    int32_t Hi, Wi, Ho, Wo, ph, pw;
+    int32_t N, VR, NV;             // virtual rows per image (Hi + 2) and in all (N * VR)
+    int32_t cblocks, tiles;        // dX channel blocks per group block; group blocks * cblocks
+    int32_t vpw;                   // virtual rows per workgroup (a multiple of 4)
+    int32_t qp, nxl;               // pixels per ring slot (>= Wi + 2) and 1 KB loads per dY row
+    int32_t total_wg, out_mode;
+    uint32_t dy_bytes, w_bytes;
+    MagicU32 mVR, mkpg, mcpg;
+};
+inline int dg_ring_lds_bytes(const DgradRingInstance& r, int qp) {
+    return 2 * (9 * 8 * r.ch * r.cbd + kDgRingSlots * qp * 8 * r.ch);
+}
+
 // dgrad tiles: id -> (BM, BN); 4 waves each
 struct DgradTile {
     int id, bm, bn;

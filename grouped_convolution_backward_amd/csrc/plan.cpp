@@ -340,6 +340,7 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
     out.prob = p;
     out.in_f16 = p.in_dtype == WGRAD_FP16;
     out.ring_inst = -1;
+    out.dg_ring = -1;
     wgrad_plan_info& info = out.info;
     {
         const int64_t all[3] = {g.Do, g.Ho, g.Wo};
@@ -621,6 +622,66 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
     return WGRAD_OK;
 }
 
+// Row-ring backward data (tile 6): 2D, 3x3 filter, unit stride and
+// dilation, h-pads with pad_lo <= 2 and Ho <= Hi (so the two padding rows
+// after each image read only zero dY rows), rows up to 64 wide, merged runs
+// of 32 or 64 dY channels and a multiple of 32 dX channels, weight chunks
+// inside one group. Returns false with a reason when the shape does not fit.
+bool plan_dgrad_ring(const wgrad_problem& p, const Geo& g, int64_t Gm, const DeviceModel& dev, Plan& out,
+                     std::string* why) {
+    const int64_t cpg = p.C / p.G, kpg = p.K / p.G;
+    auto no = [&](const char* m) { if (why) *why = m; return false; };
+    if (p.ndim != 2 || g.Y != 3 || g.X != 3 || g.sh != 1 || g.sw != 1 || g.dh != 1 || g.dw != 1)
+        return no("row-ring dgrad needs a 2D 3x3 filter with unit stride and dilation");
+    if (g.ph > 2 || g.Ho > g.Hi) return no("row-ring dgrad needs pad_lo <= 2 and pad_lo + pad_hi <= 2 along h");
+    if (g.Wi > 64) return no("row-ring dgrad needs input rows of at most 64 positions");
+    const int64_t gkpg = Gm * kpg, gcpg = Gm * cpg;
+    if (cpg % 8 || p.K % 8 || p.C % 8) return no("row-ring dgrad needs 16-byte channel vectors inside one group");
+    if (gkpg != 32 && gkpg != 64) return no("row-ring dgrad needs 32 or 64 merged output channels per group block");
+    if (gcpg % 32) return no("row-ring dgrad needs a merged input-channel run that is a multiple of 32");
+    const int64_t ndy = p.N * g.Ho * g.Wo * p.K, nw = p.K * 9 * cpg, ndx = p.N * g.Hi * g.Wi * p.C;
+    if (2 * ndy >= (int64_t{1} << 31) || 2 * nw >= (int64_t{1} << 31) || 4 * ndx >= (int64_t{1} << 31))
+        return no("row-ring dgrad needs dY, W and dX below 2 GiB");
+    const int ch = (int)(gkpg / 8), mt = g.Wi <= 32 ? 1 : 2;
+    const int pxl = 64 / ch;
+    const int64_t qp = ceil_div(g.Wi + 2, pxl) * pxl;
+    // 64 dX channels per block when the run allows it and the LDS holds it
+    int inst = -1;
+    for (int cbd : {64, 32}) {
+        if (gcpg % cbd) continue;
+        for (int i = 0; i < kNumDgRingInstances; ++i) {
+            const DgradRingInstance& r = kDgRingInstances[i];
+            if (r.cbd == cbd && r.mt == mt && r.ch == ch && dg_ring_lds_bytes(r, (int)qp) <= kDgRingLdsMax) inst = i;
+        }
+        if (inst >= 0) break;
+    }
+    if (inst < 0) return no("row-ring dgrad: no instance fits the LDS");
+    const DgradRingInstance& ri = kDgRingInstances[inst];
+    const int64_t VR = g.Hi + 2, NV = p.N * VR;
+    const int64_t cblocks = gcpg / ri.cbd, tiles = (p.G / Gm) * cblocks;
+    // four rows per step; as many splits as leave one workgroup per CU
+    const int64_t s0 = std::max<int64_t>(1, (int64_t)dev.num_cus / tiles);
+    const int64_t vpw = 4 * ceil_div(ceil_div(NV, s0), 4);
+    const int64_t S = ceil_div(NV, vpw);
+    if (tiles * S > kMax31) return no("row-ring dgrad grid too large");
+    DgradRingArgs& a = out.dgr;
+    a = DgradRingArgs{};
+    a.Ktot = (int32_t)p.K; a.Ctot = (int32_t)p.C; a.kpg = (int32_t)kpg; a.cpg = (int32_t)cpg;
+    a.Gm = (int32_t)Gm; a.gkpg = (int32_t)gkpg; a.gcpg = (int32_t)gcpg;
+    a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo;
+    a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
+    a.N = (int32_t)p.N; a.VR = (int32_t)VR; a.NV = (int32_t)NV;
+    a.cblocks = (int32_t)cblocks; a.tiles = (int32_t)tiles;
+    a.vpw = (int32_t)vpw;
+    a.qp = (int32_t)qp; a.nxl = (int32_t)(qp / pxl);
+    a.total_wg = (int32_t)(tiles * S);
+    a.out_mode = p.out_dtype == WGRAD_BF16 ? OUT_BF16 : p.out_dtype == WGRAD_FP16 ? OUT_FP16 : OUT_FP32;
+    a.dy_bytes = (uint32_t)(2 * ndy); a.w_bytes = (uint32_t)(2 * nw);
+    a.mVR = make_magic((uint32_t)VR); a.mkpg = make_magic((uint32_t)kpg); a.mcpg = make_magic((uint32_t)cpg);
+    out.dg_ring = inst;
+    return true;
+}
+
 int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceModel& dev, Plan& out,
                      std::string* msg) {
     const int U = WGRAD_ERR_UNSUPPORTED;
@@ -654,6 +715,7 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
                     kDgDwLdsMax / 32);
     if (dw_cb && (dw_tile || (o.tile == 0 && o.group_merge <= 1))) {
         out = Plan{};
+        out.dg_ring = -1;
         out.op = OP_DGRAD;
         out.prob = p;
         out.in_f16 = p.in_dtype == WGRAD_FP16;
@@ -736,6 +798,39 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
         while (Gm * 2 <= 8 && p.G % (Gm * 2) == 0 && (Gm * cpg < 32 || Gm * kpg < 32)) Gm *= 2;
     }
     const int64_t gkpg = Gm * kpg, gcpg = Gm * cpg;
+    // row-ring form (tile 6), automatic where it applies
+    if (o.tile == 6 || o.tile == 0) {
+        Plan rp{};
+        std::string why;
+        if (p.N > 0 && plan_dgrad_ring(p, g, Gm, dev, rp, &why)) {
+            out = Plan{};
+            out.op = OP_DGRAD;
+            out.prob = p;
+            out.in_f16 = p.in_dtype == WGRAD_FP16;
+            out.variant = WGRAD_VARIANT_DGRAD;
+            out.dg_ring = rp.dg_ring;
+            out.dgr = rp.dgr;
+            const DgradRingInstance& ri = kDgRingInstances[out.dg_ring];
+            wgrad_plan_info& info = out.info;
+            {
+                const int64_t all[3] = {g.Do, g.Ho, g.Wo};
+                for (int i = 0; i < 3; ++i) info.out_len[i] = i < p.ndim ? all[3 - p.ndim + i] : 0;
+            }
+            info.gemm_m = M; info.gemm_n = cpg; info.gemm_k = kpg * taps;
+            info.variant = WGRAD_VARIANT_DGRAD;
+            info.tile = 6;
+            info.tile_m = 32 * ri.mt; info.tile_n = ri.cbd; info.tile_k = 16;
+            info.split_k = 1; info.group_merge = (int32_t)Gm; info.vector_width = 8;
+            info.grid_main = out.dgr.total_wg;
+            info.num_cus = dev.num_cus;
+            char name[160];
+            snprintf(name, sizeof name, "dgrad_ring_%s_m%dx32_n%d_k%d_v%d_gm%lld", out.in_f16 ? "fp16" : "bf16", ri.mt,
+                     ri.cbd, 8 * ri.ch, out.dgr.vpw, (long long)Gm);
+            out.name = name;
+            return WGRAD_OK;
+        }
+        if (o.tile == 6) return fail(msg, U, "%s", p.N > 0 ? why.c_str() : "row-ring dgrad needs N > 0");
+    }
     int V = 8;
     while (V > 1 && (kpg % V || cpg % V || p.K % V || p.C % V)) V >>= 1;
     int tile_id = o.tile;
@@ -765,6 +860,7 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
         return fail(msg, U, "the dgrad kernel needs dY and W below 2 GiB each");
     if (total > kMax31 || Mq > kMax31) return fail(msg, U, "grid too large");
     out = Plan{};
+    out.dg_ring = -1;
     out.op = OP_DGRAD;
     out.prob = p;
     out.in_f16 = p.in_dtype == WGRAD_FP16;

@@ -257,6 +257,8 @@ struct Plan {
     int dg_bn, dg_v, dg_bk;      // dgrad tile width, load vector width, channels per reduction chunk
     DgradDwArgs dgdw;
     int dg_dw;                   // 1: the depthwise dgrad kernel
+    DgradRingArgs dgr;
+    int dg_ring;                 // index into kDgRingInstances, or -1
     std::string name;
 };
 
@@ -276,5 +278,6 @@ int launch_depthwise3(const Plan& plan, const Dw3Args& a, void* stream);
 int launch_reduce(const ReduceArgs& a, int64_t grid, void* stream);
 int launch_dgrad(const Plan& plan, const DgradArgs& a, void* stream);   // dgrad.hip
 int launch_dgrad_dw(const Plan& plan, const DgradDwArgs& a, void* stream);
+int launch_dgrad_ring(const Plan& plan, const DgradRingArgs& a, void* stream);   // dgrad_ring.hip
 
 }  // namespace wgrad

@@ -202,8 +202,12 @@ int wgrad_run_stage(const wgrad_plan_t* plan, int stage, const void* x, const vo
  * (positions x channels) tiles; 4 = the depthwise direct kernel (C/G = K/G
  * = 1, C % 8 == 0, at most 2048 taps), which auto picks for such shapes, in
  * its row-walking form for 2D 3x3 filters with unit stride and dilation; 5 =
- * the depthwise kernel's per-tap form for any depthwise shape. Anything else
- * is WGRAD_ERR_UNSUPPORTED. wgrad_plan_query reports
+ * the depthwise kernel's per-tap form for any depthwise shape; 6 = the
+ * row-ring MFMA kernel (2D 3x3 filter, unit stride and dilation, h pads at
+ * most 2 in all, input rows of at most 64 positions, C/G, C and K multiples
+ * of 8, Gm*K/G of 32 or 64 and Gm*C/G a multiple of 32), which keeps a group
+ * block's weights in LDS and stages each dY row once per workgroup; auto
+ * picks it wherever it applies. Anything else is WGRAD_ERR_UNSUPPORTED. wgrad_plan_query reports
  * variant DGRAD, gemm_m/n/k as above and workspace_bytes 0.
  * The plan is released with wgrad_plan_destroy; wgrad_run and
  * wgrad_run_stage reject it (and wgrad_dgrad_run rejects backward-weight

@@ -224,3 +224,37 @@ def test_dgrad_empty_batch():
     w = torch.zeros(p.w_shape(), dtype=torch.bfloat16, device="cuda")
     p.run(e, w, e)
     torch.cuda.synchronize()
+
+
+# row-ring form (tile 6): images crossing step boundaries, one-row and
+# narrow images, every pad the form takes, 32- and 64-channel dY runs, one
+# to three dX channel blocks, merged groups, fp16 in and fp32 out
+RING = [
+    (2, 1, 3, 64, 64, (13, 56), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+    (2, 1, 2, 96, 32, (9, 30), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+    (2, 16, 3, 8, 8, (7, 28), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+    (2, 4, 2, 16, 16, (6, 40), (3, 3), (1, 1), (0, 2), (2, 0), (1, 1), "bf16", None),
+    (2, 1, 2, 64, 32, (5, 17), (3, 3), (1, 1), (2, 0), (0, 2), (1, 1), "bf16", None),
+    (2, 1, 2, 32, 64, (4, 64), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "fp16", "fp32"),
+    (2, 1, 5, 32, 64, (1, 20), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+    (2, 2, 3, 64, 32, (9, 3), (3, 3), (1, 1), (0, 0), (0, 0), (1, 1), "fp16", None),
+]
+
+
+@pytest.mark.parametrize("i", range(len(RING)))
+def test_dgrad_ring_form(i):
+    cfg = prob(*RING[i], name=f"ring{i}")
+    dyb, wb = draw(cfg, "int", (1100 + i, 1200 + i))
+    _, bits, p = run_dgrad(cfg, dyb, wb, tile=6)
+    assert p.info["tile"] == 6 and p.name.startswith("dgrad_ring_"), p.name
+    dx64, _ = oracle.dgrad(cfg, dyb, wb)
+    check_exact(cfg, bits, dx64)
+    # the flat MFMA kernel gives the same (exact) bits
+    _, bits1, _ = run_dgrad(cfg, dyb, wb, tile=1)
+    assert np.array_equal(bits, bits1)
+    dyb, wb = draw(cfg, "uniform", (1300 + i, 1400 + i))
+    vals, bits, _ = run_dgrad(cfg, dyb, wb, tile=6)
+    dx64, ab64 = oracle.dgrad(cfg, dyb, wb)
+    check_tol(cfg, vals, dx64, ab64)
+    _, bits2, _ = run_dgrad(cfg, dyb, wb, tile=6)
+    assert np.array_equal(bits, bits2)

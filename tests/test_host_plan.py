@@ -316,7 +316,7 @@ def dplan(cfg, **kw):
 def test_dgrad_plans_sizes_and_tiles():
     import oracle
     cfg = workloads.CONFIGS["c2"]
-    p = dplan(cfg)
+    p = dplan(cfg, tile=2)                    # the flat MFMA kernel (auto takes the row ring)
     info = p.info
     assert info["variant"] == gcb.VARIANT_DGRAD
     assert info["gemm_m"] == 32 * 56 * 56 and info["gemm_n"] == 64 and info["gemm_k"] == 64 * 9
@@ -334,10 +334,11 @@ def test_dgrad_plans_sizes_and_tiles():
     assert p.info["out_len"] == oracle.out_len(g)
     # explicit tiles; 128-wide channel tiles for wide groups
     wide = dict(cfg, C=256)
+    wide = dict(cfg, C=256, pad_lo=(2, 1), pad_hi=(2, 1))   # out of the row ring's reach
     assert dplan(wide).info["tile_n"] == 128
     assert dplan(wide, tile=2).info["tile_n"] == 64
     # small groups merge until both merged runs reach 32 channels
-    p = dplan(workloads.CONFIGS["c4a"])
+    p = dplan(workloads.CONFIGS["c4a"], tile=1)
     assert p.info["group_merge"] == 4 and p.info["tile_n"] == 32 and p.name.endswith("gm4")
     assert p.info["grid_main"] == ((32 * 28 * 28 + 127) // 128) * 8
     assert dplan(workloads.CONFIGS["c4a"], group_merge=8).info["group_merge"] == 8
@@ -442,3 +443,23 @@ def test_ring_form_rejections():
     _expect(gcb.ERR_UNSUPPORTED, c4a, variant=gcb.VARIANT_ROWSLAB, tile=3)
     # where the ring form does not apply, auto falls back to one filter row per workgroup
     assert plan(workloads.problem(c4a, in_len=(28, 100))).name.startswith("wgrad_rowslab_")
+
+
+def test_dgrad_ring_form_plans():
+    def dplan(cfg, **kw):
+        return gcb.DgradPlan(cfg, hip_device=-1, **kw)
+    # the dense and grouped 3x3 unit-stride workloads take the row-ring form
+    p = dplan(workloads.CONFIGS["c2"])
+    assert p.info["tile"] == 6 and p.name.startswith("dgrad_ring_bf16_m2x32_n64_k64")
+    rows = 32 * (56 + 2)
+    vpw = int(p.name.split("_v")[1].split("_")[0])
+    assert vpw % 4 == 0 and p.info["grid_main"] == -(-rows // vpw) and p.info["grid_main"] <= 256
+    p = dplan(workloads.CONFIGS["c4a"])
+    assert p.info["tile"] == 6 and p.info["group_merge"] == 4 and p.name.endswith("gm4")
+    # shapes it does not take fall back to the flat MFMA kernel, or fail when asked for
+    for bad in (workloads.problem("c2", pad_lo=(2, 1), pad_hi=(2, 1)),     # Ho > Hi
+                workloads.problem("c2", in_len=(56, 70)),                  # rows wider than 64
+                workloads.CONFIGS["c3"], workloads.CONFIGS["c1"]):
+        assert dplan(bad).info["tile"] in (1, 2, 3)
+        with pytest.raises(gcb.WgradError):
+            dplan(bad, tile=6)
