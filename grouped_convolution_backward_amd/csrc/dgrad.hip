@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     // workgroup and kept incrementally (the scalar unit is shared by every
     // wave of the CU): a new k-chunk adds to k0 and kw, a new tap adjusts the
     // output offsets (od, oh, ow), the dY tap offset and the weight tap offset.
-    int cur = 0, cur_kc = 0, cur_iz = 0, cur_iy = 0, cur_ix = 0;
+    int cur = 0, cur_kc = 0, cur_iy = 0, cur_ix = 0;   // the depth tap is the outermost: no counter
     int k0 = 0, kw = 0;                                     // k0 * taps * cpg
     int od = od0, oh = oh0, ow = ow0;
     uint32_t tapoff = ((uint32_t)(od0 * a.Ho + oh0) * a.Wo + ow0) * (uint32_t)a.Ktot;
@@ -225,7 +225,6 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
         oh = oh0;
         tapoff += (uint32_t)(ny - 1) * ost_h;
         wt -= (ny - 1) * wst_y;
-        ++cur_iz;
         od -= a.zdo;
         tapoff -= ost_d;
         wt += wst_z;

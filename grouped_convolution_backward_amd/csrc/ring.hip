@@ -37,9 +37,12 @@
 //   whose dY is zero.
 // * MFMA operands come from ds_read_b64_tr_b16 (rocm-libraries PR 11602).
 //   X fragments are the first operand, so each lane's accumulators are four
-//   consecutive dW columns of one dW row, stored straight from registers:
-//   the three waves' tiles are disjoint, so no cross-wave reduction is
-//   needed. Merged groups (PR 12359) store only their diagonal blocks.
+//   consecutive dW columns of one dW row. The three waves' tiles are
+//   disjoint (no cross-wave reduction); they are gathered in LDS and stored
+//   as whole 32-channel runs of one tap (rows of a tile are a dW row apart,
+//   so stores straight from registers would write 32-byte pieces of 32
+//   scattered lines per instruction). Merged groups (PR 12359) store only
+//   their diagonal blocks.
 // * Compared with one filter row per workgroup, per-workgroup traffic into
 //   LDS drops about threefold for the same work.
 #include <hip/hip_runtime.h>
@@ -318,33 +321,64 @@ __global__ __launch_bounds__(320, 1) void ring_kernel(const RingArgs a) {
         lds_barrier();
     }
 
-    // ---- store this filter row's block: lane holds dW row m0 + i*32 + lane%32
-    // and, per vq, four consecutive channels; with merged groups only the
-    // diagonal blocks. Offsets are relative to the tile's first element.
+    // ---- the three waves' blocks meet in LDS as one fp32 tile [m][tap][c]
+    // (the staging buffers are free: every wave is past the last step), and
+    // are stored from there as whole 128-byte runs of 32 channels of one tap,
+    // so each store instruction writes eight full lines
+    float* const red = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int x = 0; x < 3; ++x)
+#pragma unroll
+            for (int vq = 0; vq < 4; ++vq) {
+                const f32x16& c = acc[i][x];
+                *reinterpret_cast<f32x4*>(red + (i * 32 + (lane & 31)) * kRingTilePitch + (y * 3 + x) * CB + 8 * vq +
+                                          4 * (lane >> 5)) = f32x4{c[4 * vq], c[4 * vq + 1], c[4 * vq + 2], c[4 * vq + 3]};
+            }
+    // the load waves have ended; this barrier joins the three MFMA waves
+    lds_barrier();
+    // element it = row * RUNS + run of the tile (run = tap * CB/4 + chunk, a
+    // 4-channel chunk) goes to thread it % 192, so eight consecutive lanes
+    // store one tap's 32 channels (a whole 128-byte line) of one row. A
+    // thread's runs repeat every PER passes; with merged groups only the
+    // diagonal blocks are stored. Offsets are relative to the slice start.
+    constexpr int NTH = 3 * 64, RUNS = 9 * (CB / 4), PER = 3, ITER = MB * RUNS / NTH;
+    constexpr int RSTEP = PER * NTH / RUNS;        // tile rows advanced every PER passes
+    static_assert((MB * RUNS) % NTH == 0 && ITER % PER == 0 && (PER * NTH) % RUNS == 0, "store passes");
+    const int tid = threadIdx.x;
+    int lrow[PER], lcol[PER], glo[PER];
+    int64_t goff[PER];
+#pragma unroll
+    for (int ph = 0; ph < PER; ++ph) {
+        const int it = tid + ph * NTH;
+        const int run = it % RUNS, tap = run / (CB / 4), c4 = (run % (CB / 4)) * 4;
+        const int cg = c0 + c4;
+        const int gj = (int)magic_div((uint32_t)cg, a.mCpg);   // group of these channels (cpg % 4 == 0)
+        lrow[ph] = it / RUNS;
+        lcol[ph] = tap * CB + c4;
+        glo[ph] = gj * a.kpg;
+        goff[ph] = tap * a.cpg + (cg - gj * a.cpg);
+    }
     const int64_t tile0 = (a.out_mode == OUT_WORKSPACE ? (int64_t)z * a.slice_elems : 0) +
-                          (int64_t)(gb * a.gkpg) * a.row_len + y * 3 * a.cpg;
+                          (int64_t)(gb * a.gkpg) * a.row_len;
     auto store_all = [&](auto put) {
 #pragma unroll
-        for (int vq = 0; vq < 4; ++vq) {
-            const int cg = c0 + 8 * vq + 4 * (lane / 32);
-            const int gj = (int)magic_div((uint32_t)cg, a.mCpg);   // group of these channels (cpg % 4 == 0)
-            const int glo = gj * a.kpg;
-            const int cofs = cg - gj * a.cpg;
+        for (int u = 0; u < ITER / PER; ++u)
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int mg = m0 + i * 32 + (lane & 31);
-                if (mg < a.Mm && mg >= glo && mg < glo + a.kpg) {
-#pragma unroll
-                    for (int x = 0; x < 3; ++x) {
-                        const f32x16& c = acc[i][x];
-                        put(mg * a.row_len + x * a.cpg + cofs, f32x4{c[4 * vq], c[4 * vq + 1], c[4 * vq + 2], c[4 * vq + 3]});
-                    }
-                }
+            for (int ph = 0; ph < PER; ++ph) {
+                const int row = lrow[ph] + u * RSTEP;
+                const int mg = m0 + row;
+                if (mg < a.Mm && mg >= glo[ph] && mg < glo[ph] + a.kpg)
+                    put(mg * a.row_len + goff[ph],
+                        *reinterpret_cast<const f32x4*>(red + row * kRingTilePitch + lcol[ph]));
             }
-        }
     };
     // one loop per output type, so that no store carries the type switch
-    if (a.out_mode == OUT_WORKSPACE || a.out_mode == OUT_FP32) {
+    if (a.out_mode == OUT_WORKSPACE) {
+        float* o = static_cast<float*>(a.out) + tile0;
+        store_all([&](int e, const f32x4& v) { store_partial4(o + e, v); });
+    } else if (a.out_mode == OUT_FP32) {
         float* o = static_cast<float*>(a.out) + tile0;
         store_all([&](int e, const f32x4& v) { __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(o + e)); });
     } else if (a.out_mode == OUT_BF16) {

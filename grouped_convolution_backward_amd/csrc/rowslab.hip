@@ -59,6 +59,8 @@ __device__ __forceinline__ void store4(void* out, int mode, int64_t e, const f32
         p[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e) = p;
+    } else if (mode == OUT_WORKSPACE) {
+        store_partial4(static_cast<float*>(out) + e, v);
     } else {
         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(out) + e));
     }

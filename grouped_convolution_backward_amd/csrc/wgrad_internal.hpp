@@ -117,8 +117,13 @@ constexpr RingInstance kRingInstances[] = {
 constexpr int kNumRingInstances = sizeof(kRingInstances) / sizeof(kRingInstances[0]);
 constexpr int kRingCB = 32;                       // channels per C block
 constexpr int ring_slots(const RingInstance& r) { return 3 * r.nb * r.rps; }
+// the epilogue's fp32 tile: mb rows of 9 taps x 32 channels, pitch padded
+// by 4 floats so that 16 consecutive rows start on distinct bank quads
+constexpr int kRingTilePitch = 9 * kRingCB + 4;
 inline int ring_lds_bytes(const RingInstance& r) {
-    return 2 * (r.nb * r.rps * 16 * r.nks * r.mb + ring_slots(r) * r.xwp * kRingCB);
+    const int stage = 2 * (r.nb * r.rps * 16 * r.nks * r.mb + ring_slots(r) * r.xwp * kRingCB);
+    const int tile = 4 * r.mb * kRingTilePitch;
+    return stage > tile ? stage : tile;
 }
 
 struct RingArgs {
