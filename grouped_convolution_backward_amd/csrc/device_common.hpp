@@ -36,22 +36,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// Stores of fp32 split-K partials, which the reduce kernel reads next. They
-// are device-scope stores (sc1): on the dense split-K shapes this shortened
-// the time between the end of the main kernel and the reduce kernel's work
-// by about 1 us against plain or nontemporal stores, consistent with the
-// partials not being left in this XCD's L2 for the end-of-kernel writeback.
-__device__ __forceinline__ void store_partial(float* p, float v) {
-    asm volatile("global_store_dword %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
-}
-__device__ __forceinline__ void store_partial4(float* p, const f32x4& v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
-}
-
 __device__ __forceinline__ void store_out(void* out, int mode, int64_t e, float v) {
-    if (mode == OUT_WORKSPACE) {
-        store_partial(static_cast<float*>(out) + e, v);
-    } else if (mode == OUT_BF16) {
+    if (mode == OUT_BF16) {
         static_cast<uint16_t*>(out)[e] = f32_to_bf16(v);
     } else if (mode == OUT_FP16) {
         static_cast<_Float16*>(out)[e] = (_Float16)v;
@@ -105,6 +91,18 @@ constexpr uint32_t kBufOob = 0x80000000u;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
     // word 3 = 0x00020000: 32-bit data format for untyped loads on gfx9-family parts
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Stores of fp32 split-K partials, which the reduce kernel reads next, into
+// one workspace slice (a buffer of at most 2 GiB; e is the element offset in
+// it). They are device-scope stores (cache policy SC1): on the dense split-K
+// shapes this shortened the time between the end of the main kernel and the
+// reduce kernel's work by about 1 us against plain or nontemporal stores,
+// consistent with the partials not being left in this XCD's L2 for the
+// end-of-kernel writeback. A buffer-store builtin, not inline assembly, so
+// that the compiler sees the store and guards its data registers.
+constexpr int kCpolSc1 = 16;
+__device__ __forceinline__ void store_partial4(__amdgpu_buffer_rsrc_t r, int64_t e, const f32x4& v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)(e * 4), 0, kCpolSc1);
 }
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));

@@ -143,6 +143,7 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
     }
     if (tiles * S > kMax31 || S > 65535) return no("row-slab grid too large");
     const int64_t ndw = p.K * g.Z * g.Y * g.X * cpg;
+    if (S > 1 && 4 * ndw >= (int64_t{1} << 31)) return no("row-slab partials need a dW below 2 GiB of fp32");
     RowSlabArgs& a = out.rs;
     a = RowSlabArgs{};
     a.Ktot = (int32_t)p.K; a.Ctot = (int32_t)p.C; a.kpg = (int32_t)kpg; a.cpg = (int32_t)cpg;
@@ -222,6 +223,7 @@ bool plan_ring(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o, c
     if (NHo) S = ceil_div(NHo, rpw);
     if (tiles * S > kMax31 || S > 65535) return no("filter-row ring grid too large");
     const int64_t ndw = p.K * 9 * cpg;
+    if (S > 1 && 4 * ndw >= (int64_t{1} << 31)) return no("filter-row ring partials need a dW below 2 GiB of fp32");
     RingArgs& a = out.ring;
     a = RingArgs{};
     a.Ktot = (int32_t)p.K; a.Ctot = (int32_t)p.C; a.kpg = (int32_t)kpg; a.cpg = (int32_t)cpg;

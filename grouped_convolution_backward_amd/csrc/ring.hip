@@ -360,8 +360,7 @@ __global__ __launch_bounds__(320, 1) void ring_kernel(const RingArgs a) {
         glo[ph] = gj * a.kpg;
         goff[ph] = tap * a.cpg + (cg - gj * a.cpg);
     }
-    const int64_t tile0 = (a.out_mode == OUT_WORKSPACE ? (int64_t)z * a.slice_elems : 0) +
-                          (int64_t)(gb * a.gkpg) * a.row_len;
+    const int64_t tile0 = (int64_t)(gb * a.gkpg) * a.row_len;   // within dW or a workspace slice
     auto store_all = [&](auto put) {
 #pragma unroll
         for (int u = 0; u < ITER / PER; ++u)
@@ -376,8 +375,9 @@ __global__ __launch_bounds__(320, 1) void ring_kernel(const RingArgs a) {
     };
     // one loop per output type, so that no store carries the type switch
     if (a.out_mode == OUT_WORKSPACE) {
-        float* o = static_cast<float*>(a.out) + tile0;
-        store_all([&](int e, const f32x4& v) { store_partial4(o + e, v); });
+        const __amdgpu_buffer_rsrc_t ws = buf_rsrc(static_cast<float*>(a.out) + (int64_t)z * a.slice_elems,
+                                                   4u * (uint32_t)a.slice_elems);
+        store_all([&](int e, const f32x4& v) { store_partial4(ws, tile0 + e, v); });
     } else if (a.out_mode == OUT_FP32) {
         float* o = static_cast<float*>(a.out) + tile0;
         store_all([&](int e, const f32x4& v) { __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(o + e)); });

@@ -59,8 +59,6 @@ __device__ __forceinline__ void store4(void* out, int mode, int64_t e, const f32
         p[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e) = p;
-    } else if (mode == OUT_WORKSPACE) {
-        store_partial4(static_cast<float*>(out) + e, v);
     } else {
         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(out) + e));
     }
@@ -311,7 +309,9 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
     lds_barrier();
     float* red = reinterpret_cast<float*>(smem);
     const int mbase = gb * a.gkpg;
-    const int64_t zoff = a.out_mode == OUT_WORKSPACE ? (int64_t)z * a.slice_elems : 0;
+    // this workgroup's workspace slice (partials only)
+    const __amdgpu_buffer_rsrc_t ws = buf_rsrc(static_cast<float*>(a.out) + (int64_t)z * a.slice_elems,
+                                               4u * (uint32_t)a.slice_elems);
 #pragma unroll
     for (int x = 0; x < XF; ++x) {
 #pragma unroll
@@ -347,7 +347,10 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
                                *reinterpret_cast<const f32x4*>(red + 2 * TILE + o)) +
                               *reinterpret_cast<const f32x4*>(red + 3 * TILE + o);
             const int mg = m0 + row;
-            if (mg < a.Mm && mg >= glo && mg < ghi) store4(a.out, a.out_mode, zoff + e0 + (int64_t)mg * a.row_len, sum);
+            if (mg < a.Mm && mg >= glo && mg < ghi) {
+                if (a.out_mode == OUT_WORKSPACE) store_partial4(ws, e0 + (int64_t)mg * a.row_len, sum);
+                else store4(a.out, a.out_mode, e0 + (int64_t)mg * a.row_len, sum);
+            }
         }
         lds_barrier();
     }
