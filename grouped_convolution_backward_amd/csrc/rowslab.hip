@@ -305,54 +305,71 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
         lds_barrier();
     }
 
-    // ---- sum the four stream tiles in LDS (fixed order) and store, one tap at a time
+    // ---- sum the four stream tiles in LDS (fixed order) and store, as many
+    // taps per pass as the slab buffers hold (two on the 3-tap 64x64 shapes:
+    // one barrier pair less than a tap at a time)
+    constexpr int TPP0 = (4 * NB * BUF * 2) / (4 * TILE * 4);
+    constexpr int TPP = TPP0 < 1 ? 1 : TPP0 > XF ? XF : TPP0;   // taps per pass
+    static_assert(TPP == 1 || TPP * 4 * TILE * 4 <= 4 * NB * BUF * 2, "pass tiles fit the slab buffers");
     lds_barrier();
     float* red = reinterpret_cast<float*>(smem);
     const int mbase = gb * a.gkpg;
     // this workgroup's workspace slice (partials only)
     const __amdgpu_buffer_rsrc_t ws = buf_rsrc(static_cast<float*>(a.out) + (int64_t)z * a.slice_elems,
                                                4u * (uint32_t)a.slice_elems);
+    // thread t sums the float4 at row t/(CB/4) + u*(NT/(CB/4)), columns
+    // (t % (CB/4))*4 .. +3 of a tap's tile, for u = 0, 1, ...
+    constexpr int TPR = CB / 4;                     // threads per tile row
+    constexpr int RPI = NT / TPR;                   // rows per pass
+    static_assert(MB % RPI == 0, "reduction passes");
+    static_assert(NT % TPR == 0, "consumer threads cover whole rows");
+    const int col = (threadIdx.x % TPR) * 4;
+    const int cg = c0 + col;
+    const int gj = cg / a.cpg;                      // group of this column
+    const int glo = gj * a.kpg, ghi = glo + a.kpg;  // its rows (the diagonal block)
 #pragma unroll
-    for (int x = 0; x < XF; ++x) {
+    for (int x0 = 0; x0 < XF; x0 += TPP) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int tp = 0; tp < TPP; ++tp) {
+            const int x = x0 + tp;
+            if (x >= XF) break;
 #pragma unroll
-            for (int fc = 0; fc < FCW; ++fc)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int vq = 0; vq < 4; ++vq) {
-                    const int row = i * 32 + (lane & 31);
-                    const int col = (half * FCW + fc) * 32 + 8 * vq + 4 * (lane / 32);
-                    const f32x16& c = acc[i][x * FCW + fc];
-                    *reinterpret_cast<f32x4*>(red + pair * TILE + row * RP + col) =
-                        f32x4{c[4 * vq], c[4 * vq + 1], c[4 * vq + 2], c[4 * vq + 3]};
-                }
-        lds_barrier();
-        // thread t sums the float4 at row t/(CB/4) + u*(NT/(CB/4)), columns
-        // (t % (CB/4))*4 .. +3 of this tap's tile, for u = 0, 1, ...
-        constexpr int TPR = CB / 4;                 // threads per tile row
-        constexpr int RPI = NT / TPR;               // rows per pass
-        static_assert(MB % RPI == 0, "reduction passes");
-        const int col = (threadIdx.x % TPR) * 4;
-        const int cg = c0 + col;
-        static_assert(NT % TPR == 0, "consumer threads cover whole rows");
-        const int gj = cg / a.cpg;                  // group of this column
-        const int glo = gj * a.kpg, ghi = glo + a.kpg;   // its rows (the diagonal block)
-        const int64_t e0 = (int64_t)mbase * a.row_len + (y * XF + x) * a.cpg + (cg - gj * a.cpg);
+                for (int fc = 0; fc < FCW; ++fc)
 #pragma unroll
-        for (int u = 0; u < MB / RPI; ++u) {
-            const int row = threadIdx.x / TPR + u * RPI;
-            const int o = row * RP + col;
-            const f32x4 sum = ((*reinterpret_cast<const f32x4*>(red + o) +
-                                *reinterpret_cast<const f32x4*>(red + TILE + o)) +
-                               *reinterpret_cast<const f32x4*>(red + 2 * TILE + o)) +
-                              *reinterpret_cast<const f32x4*>(red + 3 * TILE + o);
-            const int mg = m0 + row;
-            if (mg < a.Mm && mg >= glo && mg < ghi) {
-                if (a.out_mode == OUT_WORKSPACE) store_partial4(ws, e0 + (int64_t)mg * a.row_len, sum);
-                else store4(a.out, a.out_mode, e0 + (int64_t)mg * a.row_len, sum);
-            }
+                    for (int vq = 0; vq < 4; ++vq) {
+                        const int row = i * 32 + (lane & 31);
+                        const int cc = (half * FCW + fc) * 32 + 8 * vq + 4 * (lane / 32);
+                        const f32x16& c = acc[i][x * FCW + fc];
+                        *reinterpret_cast<f32x4*>(red + (tp * 4 + pair) * TILE + row * RP + cc) =
+                            f32x4{c[4 * vq], c[4 * vq + 1], c[4 * vq + 2], c[4 * vq + 3]};
+                    }
         }
         lds_barrier();
+#pragma unroll
+        for (int tp = 0; tp < TPP; ++tp) {
+            const int x = x0 + tp;
+            if (x >= XF) break;
+            const float* rt = red + tp * 4 * TILE;
+            const int64_t e0 = (int64_t)mbase * a.row_len + (y * XF + x) * a.cpg + (cg - gj * a.cpg);
+#pragma unroll
+            for (int u = 0; u < MB / RPI; ++u) {
+                const int row = threadIdx.x / TPR + u * RPI;
+                const int o = row * RP + col;
+                const f32x4 sum = ((*reinterpret_cast<const f32x4*>(rt + o) +
+                                    *reinterpret_cast<const f32x4*>(rt + TILE + o)) +
+                                   *reinterpret_cast<const f32x4*>(rt + 2 * TILE + o)) +
+                                  *reinterpret_cast<const f32x4*>(rt + 3 * TILE + o);
+                const int mg = m0 + row;
+                if (mg < a.Mm && mg >= glo && mg < ghi) {
+                    if (a.out_mode == OUT_WORKSPACE) store_partial4(ws, e0 + (int64_t)mg * a.row_len, sum);
+                    else store4(a.out, a.out_mode, e0 + (int64_t)mg * a.row_len, sum);
+                }
+            }
+        }
+        // the next pass overwrites the tiles
+        if (x0 + TPP < XF) lds_barrier();
     }
 }
 
