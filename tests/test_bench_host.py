@@ -1,0 +1,82 @@
+"""Host-side parts of bench.py: the one-GPU guard, the algorithmic work of
+the headline workload, the kernel-source hashing that keys the committed
+traffic records, and the rule that a traffic record counts only for the
+plan and sources it was taken on. No GPU is touched."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
+
+
+def test_algorithmic_work_of_the_dense_workload():
+    # 2*G*(K/G)*(C/G)*Y*X*N*Ho*Wo and |X| + |dY| + |dW| for N=32 56x56 C=K=64 3x3
+    cfg = workloads.get("c2")
+    flops, nbytes = bench.algorithmic(cfg, {"gemm_k": 32 * 56 * 56})
+    assert flops == 2 * 64 * 64 * 9 * 32 * 56 * 56 == 7_398_752_256
+    assert nbytes == 12_845_056 + 12_845_056 + 73_728
+
+
+def test_algorithmic_bytes_count_fp32_output():
+    cfg = dict(workloads.get("c1"), out_dtype="fp32")
+    _, nbytes = bench.algorithmic(cfg, {"gemm_k": 64})
+    assert nbytes == 2 * (8 * 8 * 16) + 2 * (64 * 32) + 4 * 32 * 9 * 16
+
+
+@pytest.mark.parametrize("plan,own", [
+    ("wgrad_rowslab_bf16_m64c64x3_k32_slab1x32_kouter_spk82_gm1", "rowslab.hip"),
+    ("wgrad_ring_bf16_m32c32x3x3_k32_w32_s1x1_kouter_spk32_gm4", "ring.hip"),
+    ("dgrad_ring_bf16_m2x32_n64_k64_v8_gm1", "dgrad_ring.hip"),
+    ("dgrad_mfma_fp16_t2_128x64x32_v8_kouterB_gm1", "dgrad.hip"),
+])
+def test_source_hash_follows_the_kernel_family(plan, own, tmp_path, monkeypatch):
+    """The hash changes with the family's own source and with the shared
+    headers, and not with another family's source."""
+    csrc = tmp_path / "grouped_convolution_backward_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    names = {f for _, f in bench._FAMILY_SOURCES} | set(bench._SHARED_SOURCES)
+    for f in names:
+        (csrc / f).write_text(f"// {f}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash(plan)
+    other = next(f for f in sorted(names - {own} - set(bench._SHARED_SOURCES)))
+    (csrc / other).write_text("// changed\n")
+    assert bench.kernel_source_hash(plan) == h0
+    (csrc / own).write_text("// changed\n")
+    h1 = bench.kernel_source_hash(plan)
+    assert h1 != h0
+    (csrc / "device_common.hpp").write_text("// changed\n")
+    assert bench.kernel_source_hash(plan) != h1
+
+
+def test_traffic_record_needs_same_plan_and_sources(tmp_path, monkeypatch):
+    plan = "wgrad_rowslab_bf16_m64c64x3_k32_slab1x32_kouter_spk82_gm1"
+    (tmp_path / "profiles").mkdir()
+    csrc = tmp_path / "grouped_convolution_backward_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for f in {f for _, f in bench._FAMILY_SOURCES} | set(bench._SHARED_SOURCES):
+        (csrc / f).write_text(f"// {f}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    rec = {"c2": {"kernel": plan, "source_hash": bench.kernel_source_hash(plan), "bytes_per_launch": 123}}
+    (tmp_path / "profiles" / "traffic.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("c2", plan) == 123
+    assert bench.measured_traffic("c2", plan.replace("spk82", "spk41")) is None
+    assert bench.measured_traffic("c3", plan) is None
+    (csrc / "rowslab.hip").write_text("// edited kernel\n")
+    assert bench.measured_traffic("c2", plan) is None
