@@ -284,7 +284,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--configs", default="c1,c2,c3,c4a,c4b,c5,pw,c3d,dgrad:c2,dgrad:c3,dgrad:c4a,dgrad:c5,dgrad:c3d",
                     help="workload names; dgrad:<name> times backward data of that workload")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (for profilers)")
