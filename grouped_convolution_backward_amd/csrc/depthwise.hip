@@ -240,10 +240,24 @@ __global__ __launch_bounds__(64 * kDw3Waves, 1) void dw3_kernel(const Dw3Args a)
     const __amdgpu_buffer_rsrc_t x_rs = buf_rsrc(a.x, a.x_bytes);
     const __amdgpu_buffer_rsrc_t dy_rs = buf_rsrc(a.dy, a.dy_bytes);
     const int sub = lane / cl, nsub = 64 / cl;
-    // worker w = (wave, sub) * S + z: consecutive items go to the same wave
-    // slot of consecutive workgroups (one XCD), and idle workers spread evenly
-    const int wid = (wave * nsub + sub) * a.S + z;
-    const int nworkers = kDw3Waves * nsub * a.S;
+    // Item order. When every XCD holds whole splits (the same number for each
+    // channel block), XCD x takes items [x*items/8, (x+1)*items/8): the
+    // strips there are mostly neighbours of each other, so the input columns
+    // two strips share come from HBM once and from this XCD's L2 after (with
+    // one range per XCD the neighbours on two XCDs are 7 pairs, against one
+    // pair in four strips when items go round-robin over the XCDs). Within an
+    // XCD, and otherwise over the whole grid, worker (wave, sub, z) takes
+    // items rank, rank + workers, ... with rank = (wave, sub) * (splits) + z:
+    // consecutive items go to the same wave slot of consecutive workgroups,
+    // and idle workers spread evenly.
+    const int xq = a.total_wg >> 3;
+    const bool xmajor = (a.total_wg & 7) == 0 && xq % a.cblocks == 0;
+    const int zpx = xmajor ? xq / a.cblocks : a.S;  // splits per XCD (or all of them)
+    const int zx = z / zpx, zl = z - zx * zpx;
+    const int wid = (wave * nsub + sub) * zpx + zl;
+    const int nworkers = kDw3Waves * nsub * zpx;
+    const int it_begin = xmajor ? (int)((int64_t)a.items * zx / 8) : 0;
+    const int it_end = xmajor ? (int)((int64_t)a.items * (zx + 1) / 8) : a.items;
 
     float acc[T][CH];
 #pragma unroll
@@ -321,7 +335,7 @@ __global__ __launch_bounds__(64 * kDw3Waves, 1) void dw3_kernel(const Dw3Args a)
         }
     };
 
-    for (int it = wid; it < a.items; it += nworkers) {
+    for (int it = it_begin + wid; it < it_end; it += nworkers) {
         const int strip = it / a.nch, c = it - strip * a.nch;
         const int n = strip / a.nseg;
         const int wo0 = (strip - n * a.nseg) * kUnit;
