@@ -503,7 +503,8 @@ __global__ __launch_bounds__(256) void dgrad_dw_kernel(const DgradDwArgs a) {
 // from registers. The block's weights sit in LDS as fp32 [tap][channel].
 // Chunks are numbered strip-fastest with aligned row ranges, so neighbouring
 // strips read their shared columns at the same time (one HBM fetch, one L2
-// hit).
+// hit); odd chunks walk upward, so neighbouring chunks meet at their shared
+// halo rows at the same time too.
 __device__ __forceinline__ void widen4(const u32x2& v, float* f, bool f16) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -579,54 +580,68 @@ __global__ __launch_bounds__(256) void dgrad_dw_ring_kernel(const DgradDwArgs a)
 #pragma unroll
         for (int jj = 0; jj < COLS; ++jj) dst[jj] = buf_load8(dy_rs, rok && col_ok[jj] ? base + jj * colstep : kBufOob);
     };
-    u32x2 ring[SLOTS][COLS];
-    // the row entering at step i is dY row r0 + i + ph and lives in slot i % 5;
-    // steps -2 and -1 hold the two rows above the first
-    load_row(r0 + a.ph - 2, ring[3]);
-    load_row(r0 + a.ph - 1, ring[4]);
-    load_row(r0 + a.ph, ring[0]);
-    load_row(r0 + a.ph + 1, ring[1]);
+    // The walk runs down the chunk's input rows (even chunks) or up (odd
+    // chunks), so the two chunks on either side of a chunk boundary read the
+    // halo dY rows they share at the same moment (both at their start, or
+    // both at their end) and the second reader finds them in L2. dY rows are
+    // numbered along the walk: row(k) = r0 + ph - 2 + k going down,
+    // r1 - 1 + ph - k going up. Step i computes input row r0 + i (down) or
+    // r1 - 1 - i (up) from rows k = i, i + 1, i + 2: filter row y takes
+    // k = i + 2 - y going down, k = i + y going up. Row k lives in register
+    // slot (k + 3) % 5; four rows are loaded before the first step and one
+    // per step, two steps ahead.
     const int nsteps = r1 - r0;
     const int64_t pix0 = ((int64_t)n * a.Hi) * a.Wi;
-    auto step = [&](int i, auto rot) {
-        constexpr int R = decltype(rot)::value;   // i % 5
-        // the prefetch is issued on every step, past the chunk's end too
-        // (rows below are in bounds or read as zeros), so no branch sits
-        // between a load and its use and the waits stay exact
-        load_row(r0 + i + 2 + a.ph, ring[(R + 2) % SLOTS]);   // two steps ahead
-        if (i >= nsteps) return;
-        float acc[S][CH];
+    auto walk = [&](auto up_tag) {
+        constexpr bool UP = decltype(up_tag)::value;
+        auto row_k = [&](int k) { return UP ? r1 - 1 + a.ph - k : r0 + a.ph - 2 + k; };
+        u32x2 ring[SLOTS][COLS];
 #pragma unroll
-        for (int j = 0; j < S; ++j)
+        for (int k = 0; k < 4; ++k) load_row(row_k(k), ring[(k + 3) % SLOTS]);
+        auto step = [&](int i, auto rot) {
+            constexpr int R = decltype(rot)::value;   // i % 5
+            // the prefetch is issued on every step, past the chunk's end too
+            // (rows outside dY read as zeros), so no branch sits between a
+            // load and its use and the waits stay exact
+            load_row(row_k(i + 4), ring[(R + 2) % SLOTS]);
+            if (i >= nsteps) return;
+            float acc[S][CH];
 #pragma unroll
-            for (int k = 0; k < CH; ++k) acc[j][k] = 0.f;
+            for (int j = 0; j < S; ++j)
 #pragma unroll
-        for (int y = 0; y < 3; ++y) {
-            const u32x2* row = ring[(R - y + SLOTS) % SLOTS];
-            float f[COLS][CH];
+                for (int k = 0; k < CH; ++k) acc[j][k] = 0.f;
 #pragma unroll
-            for (int jj = 0; jj < COLS; ++jj) widen4(row[jj], f[jj], F16);
+            for (int y = 0; y < 3; ++y) {
+                const u32x2* row = ring[UP ? (R + y + 3) % SLOTS : (R - y + SLOTS) % SLOTS];
+                float f[COLS][CH];
 #pragma unroll
-            for (int x = 0; x < XF; ++x) {
-                const f32x4 wv = *reinterpret_cast<const f32x4*>(wl + (y * 3 + x) * a.cb);
+                for (int jj = 0; jj < COLS; ++jj) widen4(row[jj], f[jj], F16);
 #pragma unroll
-                for (int j = 0; j < S; ++j)
+                for (int x = 0; x < XF; ++x) {
+                    const f32x4 wv = *reinterpret_cast<const f32x4*>(wl + (y * 3 + x) * a.cb);
 #pragma unroll
-                    for (int k = 0; k < CH; ++k) acc[j][k] = __builtin_fmaf(f[j + XF - 1 - x][k], wv[k], acc[j][k]);
+                    for (int j = 0; j < S; ++j)
+#pragma unroll
+                        for (int k = 0; k < CH; ++k) acc[j][k] = __builtin_fmaf(f[j + XF - 1 - x][k], wv[k], acc[j][k]);
+                }
             }
-        }
-        const int64_t pix = pix0 + (int64_t)(r0 + i) * a.Wi;
+            const int64_t pix = pix0 + (int64_t)(UP ? r1 - 1 - i : r0 + i) * a.Wi;
 #pragma unroll
-        for (int j = 0; j < S; ++j)
-            if (w0 + j < a.Wi) store4v(a.dx, a.out_mode, (pix + w0 + j) * a.C + c, acc[j]);
+            for (int j = 0; j < S; ++j)
+                if (w0 + j < a.Wi) store4v(a.dx, a.out_mode, (pix + w0 + j) * a.C + c, acc[j]);
+        };
+        for (int i = 0; i < nsteps; i += SLOTS) {
+            step(i, std::integral_constant<int, 0>{});
+            step(i + 1, std::integral_constant<int, 1>{});
+            step(i + 2, std::integral_constant<int, 2>{});
+            step(i + 3, std::integral_constant<int, 3>{});
+            step(i + 4, std::integral_constant<int, 4>{});
+        }
     };
-    for (int i = 0; i < nsteps; i += SLOTS) {
-        step(i, std::integral_constant<int, 0>{});
-        step(i + 1, std::integral_constant<int, 1>{});
-        step(i + 2, std::integral_constant<int, 2>{});
-        step(i + 3, std::integral_constant<int, 3>{});
-        step(i + 4, std::integral_constant<int, 4>{});
-    }
+    if (chunk & 1)
+        walk(std::true_type{});
+    else
+        walk(std::false_type{});
 }
 
 }  // namespace
