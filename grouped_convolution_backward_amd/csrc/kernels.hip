@@ -208,9 +208,10 @@ __global__ __launch_bounds__(256) void mfma_kernel(const MfmaArgs a) {
 }
 
 // dW[e] = round(sum_z ws[z][e]) in fp32, in one fixed order: z-lane l of a
-// workgroup sums slices l, l+ZL, l+2ZL, ... in ascending order, then the ZL
-// lane sums are added in ascending l. The order depends only on (S, ZL), so
-// a plan always produces the same bits. Splitting the slices over ZL lanes
+// workgroup sums slices l, l+ZL, l+2ZL, ... (in groups of four into four
+// running sums, the rest into the first, the four added in a fixed order),
+// then the ZL lane sums are combined by a fixed binary tree. The order
+// depends only on (S, ZL), so a plan always produces the same bits. Splitting the slices over ZL lanes
 // keeps the grid wide when dW is small and S is large.
 __global__ __launch_bounds__(256) void reduce_kernel(const ReduceArgs a) {
     __shared__ f32x4 part[256];
