@@ -380,6 +380,21 @@ def test_depthwise_strip_split_sweep(split_k):
     check_exact(cfg, bits.reshape(-1), dw64)
 
 
+@pytest.mark.parametrize("split_k", [12, 16, 40])
+def test_depthwise_strip_xcd_item_order(split_k):
+    # 2 x 7 strips of 30 rows: with 2 channel blocks, 16 and 40 splits give
+    # every XCD whole splits (items taken XCD by XCD, item counts that 8 does
+    # not divide); 12 splits do not (24 workgroups, 3 per XCD), the items go
+    # round-robin over all workers
+    cfg = workloads.problem("c5", N=2, in_len=(30, 26), out_len=(30, 26))
+    cfg["name"] = f"strip_xcd{split_k}"
+    xb, dyb = workloads.inputs(cfg, "int")
+    _, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_DEPTHWISE, tile=3, split_k=split_k)
+    assert "dwstrip" in p.name and p.info["split_k"] == split_k
+    dw64, _ = oracle_ref(cfg, xb, dyb)
+    check_exact(cfg, bits.reshape(-1), dw64)
+
+
 @pytest.mark.parametrize("form", [1, 2, 3])
 def test_depthwise_forms_agree_bitwise(form):
     # the three depthwise kernel forms on one shape, integer inputs: each is
