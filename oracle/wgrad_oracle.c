@@ -25,7 +25,7 @@
  * deterministic. Alongside dW it returns sum |dY*X| per element, which
  * scales the acceptance bound.
  *
- * Readings where the pages are silent (each listed in the design doc):
+ * Readings where the pages are silent:
  *   - C and K are totals; cpg = C/G and kpg = K/G must be whole.
  *   - Ho = floor((Hi + pl + ph - d*(Y-1) - 1)/s) + 1; only the left pad
  *     enters the input index, the right pad only sizes Ho.
