@@ -86,6 +86,7 @@ def _load():
         lib.oracle_widen.argtypes = [u16p, ctypes.c_int64, ctypes.c_int64, f64p]
         lib.oracle_widen.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_last_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -167,7 +168,13 @@ def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def max_threads() -> int:
+    """Threads a call with nthreads=0 uses (OpenMP's default team size)."""
     return int(_load().oracle_max_threads())
+
+
+def last_threads() -> int:
+    """Threads the last wgrad / wgrad_sampled / dgrad loop actually ran on."""
+    return int(_load().oracle_last_threads())
 
 
 # --- fp64 -> 16-bit rounding (round to nearest, ties to even) -------------

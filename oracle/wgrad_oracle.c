@@ -9,8 +9,9 @@
  * backward_weight_kernel.hpp": the NWGC/GKXC/NWGK, NHWGC/GKYXC/NHWGK and
  * NDHWGC/GKZYXC/NDHWGK argument constructors fix the layouts and the
  * per-group base offsets group_stride_a = K, group_stride_b = C,
- * group_stride_c = K*C*prod(filter); the operator() comment
- * "conv_bwd_weight = Out * In = Weight" fixes the operands). With per-group
+ * group_stride_c = K*C*prod(filter); the comment in operator() fixes the
+ * operands: the weight gradient is formed from the output gradient and the
+ * input). With per-group
  * channel counts cpg = C/G and kpg = K/G:
  *
  *   dW[g,k,z,y,x,c] = sum_{n<N} sum_{do<Do} sum_{ho<Ho} sum_{wo<Wo}
@@ -37,6 +38,35 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
+
+/* Threads of the last parallel loop (for tests). Each call sets its thread
+ * count with a num_threads clause on its own loop, never through the global
+ * OpenMP setting, so one call's request does not leak into the next. */
+static int g_last_threads = 1;
+
+static int pick_threads(int nthreads)
+{
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/* Called from each iteration of a parallel loop: every thread of the team
+ * records the team size (the same value), so it is set even when some
+ * threads get no iteration. */
+static void note_threads(void)
+{
+#ifdef _OPENMP
+    const int n = omp_get_num_threads();
+#pragma omp atomic write
+    g_last_threads = n;
+#else
+    g_last_threads = 1;
+#endif
+}
 
 /* Mirrors the fields of the problem; every field is int64 so that the
  * Python side can fill it with a flat array. */
@@ -181,11 +211,13 @@ int oracle_wgrad(const oracle_problem* p, const uint16_t* x, const uint16_t* dy,
     if (!xs || !dys) { free(xs); free(dys); return -1; }
     const int64_t Z = g.f[0], Y = g.f[1], X = g.f[2];
     const int64_t per_k = Z * Y * X * cpg;
+    const int nt = pick_threads(nthreads);
+    (void)nt;
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
 #endif
     for (int64_t kt = 0; kt < p->K; ++kt) {
+        note_threads();
         const int64_t gi = kt / kpg;
         for (int64_t z = 0; z < Z; ++z)
             for (int64_t y = 0; y < Y; ++y)
@@ -222,11 +254,13 @@ int oracle_wgrad_sampled(const oracle_problem* p, const uint16_t* x, const uint1
     double* xs = widen_all(x, nx, p->in_dtype);
     double* dys = widen_all(dy, ndy, p->in_dtype);
     if (!xs || !dys) { free(xs); free(dys); return -1; }
+    const int nt = pick_threads(nthreads);
+    (void)nt;
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
 #endif
     for (int64_t i = 0; i < nidx; ++i) {
+        note_threads();
         int64_t e = idx[i];
         int64_t c = e % cpg;
         int64_t t = e / cpg;
@@ -274,11 +308,13 @@ int oracle_dgrad(const oracle_problem* p, const uint16_t* dy, const uint16_t* w,
     double* ws = widen_all(w, nw, p->in_dtype);
     if (!dys || !ws) { free(dys); free(ws); return -1; }
     const int64_t rows = p->N * Di * Hi * Wi;
+    const int nt = pick_threads(nthreads);
+    (void)nt;
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 16)
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nt)
 #endif
     for (int64_t r = 0; r < rows; ++r) {
+        note_threads();
         int64_t t = r;
         const int64_t wi = t % Wi;  t /= Wi;
         const int64_t hi = t % Hi;  t /= Hi;
@@ -327,6 +363,12 @@ int oracle_widen(const uint16_t* src, int64_t n, int64_t dtype, double* out)
     for (int64_t i = 0; i < n; ++i)
         out[i] = dtype == ORC_FP16 ? widen_fp16(src[i]) : widen_bf16(src[i]);
     return 0;
+}
+
+/* Threads the last oracle_wgrad / oracle_wgrad_sampled / oracle_dgrad loop ran on. */
+int oracle_last_threads(void)
+{
+    return g_last_threads;
 }
 
 int oracle_max_threads(void)

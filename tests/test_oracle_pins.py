@@ -530,11 +530,68 @@ def test_invalid_problems_rejected():
 
 
 def test_multithreaded_is_bitwise_deterministic():
+    """One thread and every core give the same bits (each element is one
+    ascending sum whatever thread computes it), and a one-thread call does not
+    leave later calls on one thread."""
     cfg = workloads.CONFIGS["c4b"]
     xb, dyb = workloads.inputs(cfg)
     a, _ = oracle.wgrad(cfg, xb, dyb, nthreads=1)
+    assert oracle.last_threads() == 1
     b, _ = oracle.wgrad(cfg, xb, dyb, nthreads=0)
+    assert oracle.last_threads() == oracle.max_threads()
+    if (os.cpu_count() or 1) > 1:
+        assert oracle.max_threads() > 1, "a one-thread call lowered the default team size"
     assert np.array_equal(a, b)
+    i = np.arange(0, a.size, 7, dtype=np.int64)
+    c, _ = oracle.wgrad_sampled(cfg, xb, dyb, i, nthreads=3)
+    assert oracle.last_threads() == 3
+    assert np.array_equal(c, a.reshape(-1)[i])
+
+
+def test_violations_comparator():
+    """The acceptance comparator itself: an error exactly at the bound passes,
+    a few ulps above it fails, on either side of the reference; NaN and
+    infinities on the GPU side always fail; a NaN reference cannot pass."""
+    for out_dtype in ("bf16", "fp16", "fp32"):
+        ref = np.array([0.0, 3.0, -7.5, 1024.0, -0.25])
+        ab = np.array([0.0, 5.0, 12.0, 2048.0, 0.5])
+        b = oracle.bound(ab, out_dtype)
+        # an error exactly equal to the bound passes (reference 0: the
+        # error is the GPU value itself, with no rounding in between)
+        z = np.zeros_like(ref)
+        assert not oracle.violations(b, z, ab, out_dtype).any()
+        assert not oracle.violations(-b, z, ab, out_dtype).any()
+        assert not oracle.violations(ref.copy(), ref, ab, out_dtype).any()
+        # three ulps past the bound fails
+        over = np.nextafter(np.nextafter(np.nextafter(b, np.inf), np.inf), np.inf)
+        assert oracle.violations(over, z, ab, out_dtype).all()
+        assert oracle.violations(-over, z, ab, out_dtype).all()
+        # nonzero reference: the farthest fp64 value whose error is still
+        # within the bound passes, and the value three ulps beyond it fails
+        for sgn in (1.0, -1.0):
+            edge = ref + sgn * b
+            while np.any(np.abs(edge - ref) > b):
+                edge = np.where(np.abs(edge - ref) > b, np.nextafter(edge, ref), edge)
+            assert not oracle.violations(edge, ref, ab, out_dtype).any()
+            far = edge
+            for _ in range(3):
+                far = np.nextafter(far, sgn * np.inf)
+            far = np.where(np.abs(far - ref) > b, far, ref + sgn * 2 * b)
+            assert oracle.violations(far, ref, ab, out_dtype).all()
+        # non-finite GPU values
+        for bad in (np.nan, np.inf, -np.inf):
+            v = oracle.violations(np.full(ref.shape, bad), ref, ab, out_dtype)
+            assert v.all(), (out_dtype, bad)
+        # one bad element among good ones is flagged alone
+        g = ref.copy()
+        g[2] = np.nan
+        assert list(np.nonzero(oracle.violations(g, ref, ab, out_dtype))[0]) == [2]
+        # a NaN reference never passes
+        assert oracle.violations(ref, np.full(ref.shape, np.nan), ab, out_dtype).all()
+    # the bound scales with sum|dY*X|, not with |dW|: a cancelling sum
+    # (ref 0, sum of magnitudes 256) tolerates 2 in bf16 and flags 2.01
+    assert not oracle.violations(np.array([2.0]), np.array([0.0]), np.array([256.0]), "bf16").any()
+    assert oracle.violations(np.array([2.01]), np.array([0.0]), np.array([256.0]), "bf16").all()
 
 
 def test_bound_formula():
