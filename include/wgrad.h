@@ -4,8 +4,9 @@
  *
  * Operation (Composable Kernel page "grouped_convolution_backward_weight_
  * kernel.hpp": the 1D NWGC/GKXC/NWGK, 2D NHWGC/GKYXC/NHWGK and 3D
- * NDHWGC/GKZYXC/NDHWGK argument constructors, their group strides, and
- * operator()'s "Out * In = Weight"), written here for 3D:
+ * NDHWGC/GKZYXC/NDHWGK argument constructors, their group strides, and the
+ * comment in operator() that the kernel forms the weight gradient from the
+ * output gradient and the input), written here for 3D:
  *
  *   dW[g,k,z,y,x,c] = sum_{n,do,ho,wo} [0<=di<Di, 0<=hi<Hi, 0<=wi<Wi]
  *                       dY[n,do,ho,wo,g,k] * X[n,di,hi,wi,g,c]
@@ -126,7 +127,16 @@ typedef struct wgrad_plan_s wgrad_plan_t;
 
 /*
  * Validate a problem and choose kernels, split-K degree S and merge degree
- * Gm (host only, no device work). hip_device >= 0 sizes the plan for that
+ * Gm (host only, no device work).
+ * Source: the support check is the Composable Kernel page's
+ * IsSupportedArgument (a yes/no answer with a logged reason for each
+ * unsupported case), here a status code with a reason string; the choice of
+ * S and Gm follows rocm-libraries PR 12359 ("rocke/wgrad: add group merging
+ * (Gm) for depthwise grouped conv"): its commit list sizes split-K from the
+ * grid including groups, in waves, clamps it to the grid limit and then
+ * snaps it to a multiple of the XCD count; its merge-degree follow-up
+ * ("What changed") takes the largest admissible Gm.
+ * hip_device >= 0 sizes the plan for that
  * device (it must be gfx950); -1 sizes it for an MI355X (256 CUs, 8 XCDs)
  * without touching the HIP runtime, for host-side tests.
  * Returns WGRAD_ERR_INVALID_ARG for: C or K not a multiple of G, a
@@ -141,12 +151,21 @@ int wgrad_plan(const wgrad_problem* problem, const wgrad_overrides* overrides,
 
 /* Bytes of device workspace wgrad_run needs: 0 when S = 1, otherwise
  * S * K * Y * X * (C/G) * 4 (fp32 partials of the unmerged dW, so the size
- * does not depend on Gm). */
+ * does not depend on Gm).
+ * Source: rocm-libraries PR 12359's merge-degree follow-up, "What changed":
+ * the two-stage workspace is sized for the unmerged dW, since merging
+ * changes how many workgroups write dW and not how large dW is.
+ * Host only; a NULL plan gives 0. */
 size_t wgrad_workspace_bytes(const wgrad_plan_t* plan);
 
 /*
  * Enqueue dW = wgrad(X, dY) on stream (a hipStream_t; NULL = the null
- * stream) and return without synchronising. dW is overwritten (no
+ * stream) and return without synchronising.
+ * Source: the deterministic two-stage split-K epilogue that rocm-libraries
+ * PR 11602 leaves the output type to ("Technical Details") and that PR
+ * 12359 routes merged groups through (its commit list: merging and split-K
+ * compose only via the two-stage workspace store, where the off-diagonal
+ * group pairs are masked; packed atomics stay rejected). dW is overwritten (no
  * accumulation, no pre-zeroing needed). With S > 1 it runs two kernels: fp32
  * partials into ws, then a reduce/convert kernel that sums the S slices in
  * one fixed order and rounds to the out dtype (round to nearest even); no
@@ -161,7 +180,8 @@ int wgrad_run(const wgrad_plan_t* plan, const void* x, const void* dy, void* dw,
               void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The two launches of wgrad_run, enqueued one at a time: stage 1 is the main
+ * The two launches of wgrad_run, enqueued one at a time (the two stages of
+ * the split-K epilogue cited at wgrad_run): stage 1 is the main
  * kernel (with S > 1 it writes the fp32 partials into ws), stage 2 the
  * reduce/convert kernel (a no-op when S = 1). Running stage 1 then stage 2
  * on one stream equals wgrad_run; a caller may enqueue other work between
@@ -226,21 +246,30 @@ int wgrad_dgrad_plan(const wgrad_problem* problem, const wgrad_overrides* overri
  */
 int wgrad_dgrad_run(const wgrad_plan_t* plan, const void* dy, const void* w, void* dx, void* stream);
 
-/* Fill *info with the plan's decisions. */
+/* Fill *info with the plan's decisions (host only): the kernel family, tile,
+ * S and Gm chosen as described at wgrad_plan. Errors: WGRAD_ERR_INVALID_ARG
+ * for a NULL plan or info. */
 int wgrad_plan_query(const wgrad_plan_t* plan, wgrad_plan_info* info);
 
 /* Kernel name with its flags (tile, atom, "kouter", "spk<S>", "gm<Gm>"),
- * valid until the plan is destroyed. */
+ * valid until the plan is destroyed; "" for a NULL plan. The flags follow
+ * the pages' kernel names: rocm-libraries PR 11602, "Technical Details"
+ * (the "kouter" flag for the K-outer LDS tile, before "spk*"), and PR 12359,
+ * "Technical Details" (the gm{N} tag, so that merge degrees never share a
+ * name). The string is owned by the plan. */
 const char* wgrad_plan_describe(const wgrad_plan_t* plan);
 
 /* Release a plan (NULL is allowed). A plan is immutable after creation and
- * may be used from several threads at once. */
+ * may be used from several threads at once. Host memory only. */
 void wgrad_plan_destroy(wgrad_plan_t* plan);
 
-/* Reason for the calling thread's last failed call ("" if none). */
+/* Reason for the calling thread's last failed call ("" if none), in the
+ * manner of the rocke validators in rocm-libraries PR 11602 (its commit
+ * list: a bad spec returns a reason string instead of being skipped
+ * silently). Owned by the library, valid until the thread's next call. */
 const char* wgrad_last_error(void);
 
-/* Library version, "major.minor.patch". */
+/* Library version, "major.minor.patch" (plumbing; no page defines it). */
 const char* wgrad_version(void);
 
 #ifdef __cplusplus
