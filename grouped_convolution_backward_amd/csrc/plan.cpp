@@ -21,6 +21,12 @@ namespace {
 
 constexpr int64_t kMax31 = (int64_t{1} << 31) - 1;
 
+// a*b for non-negative a and b, saturated at INT64_MAX instead of wrapping
+inline int64_t smul(int64_t a, int64_t b) {
+    int64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+
 int fail(std::string* msg, int code, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
 int fail(std::string* msg, int code, const char* fmt, ...) {
     char buf[512];
@@ -43,6 +49,11 @@ struct Geo {
     int64_t Hi, Wi, Y, X, sh, sw, dh, dw, ph, pw, Ho, Wo;
     int64_t Di, Z, sd, dd, pd, Do;
 };
+
+// elements of X and dY (the problem has passed check_problem, so both fit in
+// 31 bits and these products in int64)
+inline int64_t in_elems(const wgrad_problem& p, const Geo& g) { return p.N * g.Di * g.Hi * g.Wi * p.C; }
+inline int64_t dy_elems(const wgrad_problem& p, const Geo& g) { return p.N * g.Do * g.Ho * g.Wo * p.K; }
 
 // Split-K degree in the manner of a groups-aware occupancy target: enough
 // workgroups for `target` per CU across the whole grid, clamped to the number
@@ -76,7 +87,7 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
     auto no = [&](const char* m) { if (why) *why = m; return false; };
     if (g.X != 1 && g.X != 3 && g.X != 5) return no("row-slab needs a filter width of 1, 3 or 5");
     if (g.dw != 1) return no("row-slab needs a filter dilation of 1 along w");
-    if (2 * p.N * g.Hi * g.Wi * p.C >= (int64_t{1} << 31) || 2 * p.N * g.Ho * g.Wo * p.K >= (int64_t{1} << 31))
+    if (2 * in_elems(p, g) >= (int64_t{1} << 31) || 2 * dy_elems(p, g) >= (int64_t{1} << 31))
         return no("row-slab needs X and dY below 2 GiB");
     int64_t Gm = o.group_merge;
     if (!Gm) {
@@ -187,7 +198,7 @@ bool plan_ring(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o, c
     if (p.ndim != 2) return no("filter-row ring form needs a 2D problem");
     if (g.Y != 3 || g.X != 3 || g.dh != 1 || g.dw != 1) return no("filter-row ring form needs a 3x3 filter with dilation 1");
     if (g.sh > 3 || g.sw > 2) return no("filter-row ring form needs an h-stride of at most 3 and a w-stride of 1 or 2");
-    if (2 * p.N * g.Hi * g.Wi * p.C >= (int64_t{1} << 31) || 2 * p.N * g.Ho * g.Wo * p.K >= (int64_t{1} << 31))
+    if (2 * in_elems(p, g) >= (int64_t{1} << 31) || 2 * dy_elems(p, g) >= (int64_t{1} << 31))
         return no("filter-row ring form needs X and dY below 2 GiB");
     int64_t Gm = o.group_merge;
     if (!Gm) {
@@ -277,10 +288,17 @@ int check_problem(const wgrad_problem& p, Geo& g, std::string* msg) {
     if (p.C % p.G || p.K % p.G)
         return fail(msg, E, "C (%lld) and K (%lld) must be multiples of G (%lld)", (long long)p.C,
                     (long long)p.K, (long long)p.G);
+    // every field is bounded before any product of fields is formed, and the
+    // products below saturate, so no int64 arithmetic here can wrap
+    if (p.G > kMax31 || p.C > kMax31 || p.K > kMax31 || p.N > kMax31)
+        return fail(msg, E, "G, N, C and K must fit in 31 bits");
     for (int i = 0; i < p.ndim; ++i) {
         if (p.in_len[i] < 1 || p.filt_len[i] < 1 || p.stride[i] < 1 || p.dilation[i] < 1)
             return fail(msg, E, "lengths, strides and dilations must be >= 1 (axis %d)", i);
         if (p.pad_lo[i] < 0 || p.pad_hi[i] < 0) return fail(msg, E, "pads must be >= 0 (axis %d)", i);
+        if (p.in_len[i] > kMax31 || p.filt_len[i] > kMax31 || p.stride[i] > kMax31 || p.dilation[i] > kMax31 ||
+            p.pad_lo[i] > kMax31 || p.pad_hi[i] > kMax31)
+            return fail(msg, E, "lengths, strides, dilations and pads must fit in 31 bits (axis %d)", i);
     }
     // axes outermost first; the problem's ndim axes are the last ones of (d, h, w)
     int64_t len[3], fl[3], st[3], dl[3], pl[3], ol[3];
@@ -306,14 +324,15 @@ int check_problem(const wgrad_problem& p, Geo& g, std::string* msg) {
     g.dd = dl[0];  g.dh = dl[1];  g.dw = dl[2];
     g.pd = pl[0];  g.ph = pl[1];  g.pw = pl[2];
     g.Do = ol[0];  g.Ho = ol[1];  g.Wo = ol[2];
-    const int64_t cpg = p.C / p.G, kpg = p.K / p.G;
-    const int64_t R = p.N * g.Do * g.Ho * g.Wo;
-    const int64_t nx = p.N * g.Di * g.Hi * g.Wi * p.C;
-    const int64_t ndy = R * p.K;
-    const int64_t ndw = p.K * g.Z * g.Y * g.X * cpg;
-    if (nx > kMax31 || ndy > kMax31 || ndw > kMax31 || R > kMax31 || g.Hi > kMax31 || g.Wi > kMax31)
+    const int64_t cpg = p.C / p.G;
+    const int64_t R = smul(smul(smul(p.N, g.Do), g.Ho), g.Wo);
+    const int64_t nx = smul(smul(smul(smul(p.N, g.Di), g.Hi), g.Wi), p.C);
+    const int64_t ndy = smul(R, p.K);
+    const int64_t ndw = smul(smul(smul(smul(p.K, g.Z), g.Y), g.X), cpg);
+    if (nx > kMax31 || ndy > kMax31 || ndw > kMax31 || R > kMax31)
         return fail(msg, E, "tensor element offsets must fit in 31 bits");
-    // index arithmetic on the padded input also stays in 31 bits
+    // index arithmetic on the padded input also stays in 31 bits (every
+    // factor is below 2^31 here, so these products fit in int64)
     if ((g.Do * g.sd + g.Z * g.dd) > kMax31 || (g.Ho * g.sh + g.Y * g.dh) > kMax31 ||
         (g.Wo * g.sw + g.X * g.dw) > kMax31)
         return fail(msg, E, "spatial index range must fit in 31 bits");

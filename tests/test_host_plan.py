@@ -309,6 +309,31 @@ def test_3d_invalid_problems_rejected():
     _expect(gcb.ERR_INVALID_ARG, dict(prob3(1, 1, 8, 8, (4, 4, 4), (1, 1, 1)), ndim=4))
 
 
+def test_size_products_cannot_wrap():
+    # lengths and strides of 2^20 on three axes: X would hold 2^64 elements,
+    # which wraps int64 to a small number if the product is formed unchecked
+    big = prob3(1, 1, 16, 16, (2 ** 20,) * 3, (1, 1, 1), stride=(2 ** 20,) * 3)
+    assert "31 bits" in _expect(gcb.ERR_INVALID_ARG, big)
+    # single fields beyond 31 bits are rejected before any product
+    assert "31 bits" in _expect(gcb.ERR_INVALID_ARG, prob3(1, 1, 16, 16, (4, 4, 2 ** 40), (1, 1, 1)))
+    assert "31 bits" in _expect(gcb.ERR_INVALID_ARG, prob3(1, 1, 16, 16, (4, 4, 4), (1, 1, 1),
+                                                         pad=(0, 0, 2 ** 62)))
+    assert "31 bits" in _expect(gcb.ERR_INVALID_ARG, prob3(1, 2 ** 33, 16, 16, (4, 4, 4), (1, 1, 1)))
+
+
+def test_row_slab_forms_reject_inputs_of_2_gib():
+    # 3D: X of 4096*64*64*64 bf16 elements is exactly 2 GiB, which the
+    # row-slab kernels' 32-bit byte offsets cannot address; the depth axis
+    # counts toward that size
+    cfg = prob3(1, 1, 64, 64, (4096, 64, 64), (3, 3, 3), pad=(1, 1, 1))
+    p = plan(cfg)
+    assert p.info["variant"] != gcb.VARIANT_ROWSLAB, p.name
+    assert "2 GiB" in _expect(gcb.ERR_UNSUPPORTED, cfg, variant=gcb.VARIANT_ROWSLAB)
+    # one depth slice less fits and takes the row-slab kernel
+    small = prob3(1, 1, 64, 64, (4095, 64, 64), (3, 3, 3), pad=(1, 1, 1))
+    assert plan(small).info["variant"] == gcb.VARIANT_ROWSLAB
+
+
 def dplan(cfg, **kw):
     return gcb.DgradPlan(cfg, hip_device=-1, **kw)
 
@@ -463,3 +488,23 @@ def test_dgrad_ring_form_plans():
         assert dplan(bad).info["tile"] in (1, 2, 3)
         with pytest.raises(gcb.WgradError):
             dplan(bad, tile=6)
+
+
+def test_build_guard_rejects_scratch_in_counted_load_kernels():
+    """build.py fails the build when a kernel in a source file that issues
+    counted direct-to-LDS loads uses scratch memory or a dynamic stack: its
+    exact vmcnt waits would then be short."""
+    from grouped_convolution_backward_amd import build as b
+    for f in ("rowslab.hip", "ring.hip", "dgrad_ring.hip"):
+        assert b.uses_counted_lds_loads(f), f
+    assert not b.uses_counted_lds_loads("plan.cpp")
+
+    def remarks(name, scratch, dyn):
+        return (f"x.hip:1:1: remark: Function Name: {name} [-Rpass-analysis=kernel-resource-usage]\n"
+                f"x.hip:1:1: remark:     VGPRs: 90 [-Rpass-analysis=kernel-resource-usage]\n"
+                f"x.hip:1:1: remark:     ScratchSize [bytes/lane]: {scratch} [-Rpass-analysis=kernel-resource-usage]\n"
+                f"x.hip:1:1: remark:     Dynamic Stack: {dyn} [-Rpass-analysis=kernel-resource-usage]\n")
+    clean = remarks("k0", 0, "False") + remarks("k1", 0, "False")
+    assert b.scratch_violations(clean) == []
+    assert b.scratch_violations(clean + remarks("k2", 16, "False")) == [("k2", 16, "False")]
+    assert b.scratch_violations(remarks("k3", 0, "True") + clean) == [("k3", 0, "True")]
