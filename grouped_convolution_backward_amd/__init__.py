@@ -5,7 +5,8 @@ A thin ctypes binding over libwgrad.so, whose C ABI is include/wgrad.h. The
 functions keep the ABI's names (``wgrad_plan``, ``wgrad_run``,
 ``wgrad_workspace_bytes``, ``wgrad_plan_query``, ``wgrad_plan_describe``,
 ``wgrad_plan_destroy``, ``wgrad_last_error``, ``wgrad_dgrad_plan``,
-``wgrad_dgrad_run``); this module only marshals arguments. Every step of the computation runs in the HIP kernels; there is
+``wgrad_dgrad_run``, ``wgrad_run_noalloc``); this module only marshals
+arguments. Every step of the computation runs in the HIP kernels; there is
 no CPU or PyTorch fallback, and loading fails loudly if the library has not
 been built (``python -m grouped_convolution_backward_amd.build``).
 
@@ -25,6 +26,7 @@ BF16, FP16, FP32 = 0, 1, 2
 DTYPES = {"bf16": BF16, "fp16": FP16, "fp32": FP32}
 VARIANT_AUTO, VARIANT_MFMA, VARIANT_DEPTHWISE, VARIANT_ROWSLAB, VARIANT_DGRAD = 0, 1, 2, 3, 4
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+NOALLOC_SCRATCH_BYTES = 16 << 20   # WGRAD_NOALLOC_SCRATCH_BYTES
 
 
 class WgradError(RuntimeError):
@@ -63,7 +65,7 @@ class wgrad_plan_info(ctypes.Structure):
 # every symbol include/wgrad.h declares
 EXPORTS = ("wgrad_plan", "wgrad_workspace_bytes", "wgrad_run", "wgrad_run_stage", "wgrad_plan_query",
            "wgrad_plan_describe", "wgrad_plan_destroy", "wgrad_last_error", "wgrad_version",
-           "wgrad_dgrad_plan", "wgrad_dgrad_run")
+           "wgrad_dgrad_plan", "wgrad_dgrad_run", "wgrad_run_noalloc")
 
 _lib = None
 
@@ -108,6 +110,8 @@ def load_library():
     lib.wgrad_dgrad_plan.restype = ctypes.c_int
     lib.wgrad_dgrad_run.argtypes = [vp, vp, vp, vp, vp]
     lib.wgrad_dgrad_run.restype = ctypes.c_int
+    lib.wgrad_run_noalloc.argtypes = [vp, vp, vp, vp, vp]
+    lib.wgrad_run_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -182,6 +186,12 @@ def wgrad_run_stage(plan: "Plan", stage: int, x, dy, dw, ws=None, stream=None) -
     plan.run(x, dy, dw, ws, stream, stage=stage)
 
 
+def wgrad_run_noalloc(plan: "Plan", x, dy, dw, stream=None) -> None:
+    """wgrad_run with the library's per-GPU scratch as the split-K workspace
+    (no caller workspace, no device allocation)."""
+    plan.run_noalloc(x, dy, dw, stream)
+
+
 def wgrad_dgrad_plan(problem: dict, variant: int = 0, tile: int = 0, split_k: int = 0, group_merge: int = 0,
                      hip_device: int | None = None) -> "DgradPlan":
     """Create a backward-data plan (same problem dict; in_dtype is dY's and
@@ -239,8 +249,7 @@ class Plan:
         p = self.problem
         return (p["K"], *tuple(p["filt_len"])[: p["ndim"]], p["C"] // p["G"])
 
-    def run(self, x, dy, dw, ws=None, stream=None, stage=0):
-        """stage 0 = the whole path (wgrad_run); 1 or 2 = wgrad_run_stage."""
+    def _check_io(self, x, dy, dw):
         import torch
         p = self.problem
         in_t = torch.bfloat16 if p["in_dtype"] == "bf16" else torch.float16
@@ -250,20 +259,37 @@ class Plan:
             if not t.is_cuda or t.dtype != dt or not t.is_contiguous() or t.numel() != _prod(shape):
                 raise ValueError(f"{name}: need a contiguous {dt} GPU tensor with {_prod(shape)} elements "
                                  f"(got {t.dtype}, {tuple(t.shape)}, cuda={t.is_cuda})")
+
+    @staticmethod
+    def _stream_ptr(stream):
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return sp or None
+
+    def run(self, x, dy, dw, ws=None, stream=None, stage=0):
+        """stage 0 = the whole path (wgrad_run); 1 or 2 = wgrad_run_stage."""
+        self._check_io(x, dy, dw)
         ws_ptr, ws_n = None, 0
         if self.workspace_bytes:
             if ws is None or not ws.is_cuda or ws.numel() * ws.element_size() < self.workspace_bytes:
                 raise ValueError(f"workspace of {self.workspace_bytes} bytes required")
             ws_ptr, ws_n = ws.data_ptr(), ws.numel() * ws.element_size()
-        if stream is None:
-            stream = torch.cuda.current_stream()
-        sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
         lib = load_library()
-        args = (x.data_ptr() or None, dy.data_ptr() or None, dw.data_ptr(), ws_ptr, ws_n, sp or None)
+        args = (x.data_ptr() or None, dy.data_ptr() or None, dw.data_ptr(), ws_ptr, ws_n, self._stream_ptr(stream))
         if stage:
             _check(lib.wgrad_run_stage(self.handle, int(stage), *args))
         else:
             _check(lib.wgrad_run(self.handle, *args))
+
+    def run_noalloc(self, x, dy, dw, stream=None):
+        """wgrad_run_noalloc: the split-K partials go to the library's
+        per-GPU scratch; plans whose workspace exceeds NOALLOC_SCRATCH_BYTES
+        are rejected (WgradError, ERR_INVALID_ARG)."""
+        self._check_io(x, dy, dw)
+        _check(load_library().wgrad_run_noalloc(self.handle, x.data_ptr() or None, dy.data_ptr() or None,
+                                                dw.data_ptr(), self._stream_ptr(stream)))
 
     def new_workspace(self, device=None):
         import torch

@@ -123,9 +123,8 @@ size_t wgrad_workspace_bytes(const wgrad_plan_t* plan) {
 
 namespace {
 
-int run_stages(const wgrad_plan_t* plan, int first, int last, const void* x, const void* dy, void* dw,
-               void* ws, size_t ws_bytes, void* stream) {
-    g_last_error.clear();
+// Checks of a backward-weight run's plan and tensor pointers.
+int check_run_args(const wgrad_plan_t* plan, const void* x, const void* dy, const void* dw) {
     if (!plan) return set_error(WGRAD_ERR_INVALID_ARG, "plan is NULL");
     const wgrad::Plan& P = plan->plan;
     if (P.op != wgrad::OP_WGRAD) return set_error(WGRAD_ERR_INVALID_ARG, "not a backward-weight plan");
@@ -134,6 +133,14 @@ int run_stages(const wgrad_plan_t* plan, int first, int last, const void* x, con
     if (!empty_in && (!x || !dy)) return set_error(WGRAD_ERR_INVALID_ARG, "x and dy must not be NULL");
     if ((x && !aligned16(x)) || (dy && !aligned16(dy)) || !aligned16(dw))
         return set_error(WGRAD_ERR_INVALID_ARG, "x, dy and dw must be 16-byte aligned");
+    return WGRAD_OK;
+}
+
+int run_stages(const wgrad_plan_t* plan, int first, int last, const void* x, const void* dy, void* dw,
+               void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (int rc = check_run_args(plan, x, dy, dw)) return rc;
+    const wgrad::Plan& P = plan->plan;
     const size_t need = static_cast<size_t>(P.info.workspace_bytes);
     if (need) {
         if (!ws) return set_error(WGRAD_ERR_INVALID_ARG, "workspace is NULL but the plan needs " + std::to_string(need) + " bytes");
@@ -209,6 +216,27 @@ int wgrad_run_stage(const wgrad_plan_t* plan, int stage, const void* x, const vo
                     size_t ws_bytes, void* stream) {
     if (stage != 1 && stage != 2) return set_error(WGRAD_ERR_INVALID_ARG, "stage must be 1 or 2");
     return run_stages(plan, stage, stage, x, dy, dw, ws, ws_bytes, stream);
+}
+
+int wgrad_run_noalloc(const wgrad_plan_t* plan, const void* x, const void* dy, void* dw, void* stream) {
+    g_last_error.clear();
+    if (int rc = check_run_args(plan, x, dy, dw)) return rc;
+    const size_t need = static_cast<size_t>(plan->plan.info.workspace_bytes);
+    if (need > static_cast<size_t>(WGRAD_NOALLOC_SCRATCH_BYTES))
+        return set_error(WGRAD_ERR_INVALID_ARG,
+                         "the plan's split-K workspace of " + std::to_string(need) +
+                             " bytes exceeds the library scratch of " +
+                             std::to_string(static_cast<size_t>(WGRAD_NOALLOC_SCRATCH_BYTES)) +
+                             " bytes; use wgrad_run with a caller workspace or a plan with a smaller split_k");
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (need) {
+        const int e = wgrad::scratch_workspace(stream, &ws, &ws_bytes);
+        if (e != hipSuccess)
+            return set_error(WGRAD_ERR_HIP, std::string("library scratch on this device: ") +
+                                                hipGetErrorString((hipError_t)e));
+    }
+    return run_stages(plan, 1, 2, x, dy, dw, ws, ws_bytes, stream);
 }
 
 int wgrad_plan_query(const wgrad_plan_t* plan, wgrad_plan_info* info) {

@@ -284,5 +284,9 @@ int launch_reduce(const ReduceArgs& a, int64_t grid, void* stream);
 int launch_dgrad(const Plan& plan, const DgradArgs& a, void* stream);   // dgrad.hip
 int launch_dgrad_dw(const Plan& plan, const DgradDwArgs& a, void* stream);
 int launch_dgrad_ring(const Plan& plan, const DgradRingArgs& a, void* stream);   // dgrad_ring.hip
+// Device address and size of the library's split-K scratch array on the
+// stream's GPU (noalloc.hip); resolved once per device. Returns a hipError_t
+// value (0 = success).
+int scratch_workspace(void* stream, void** ptr, size_t* bytes);
 
 }  // namespace wgrad

@@ -193,6 +193,31 @@ int wgrad_run(const wgrad_plan_t* plan, const void* x, const void* dy, void* dw,
 int wgrad_run_stage(const wgrad_plan_t* plan, int stage, const void* x, const void* dy, void* dw,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* Size of the library-owned split-K scratch that wgrad_run_noalloc uses on
+ * each GPU (16 MiB). */
+#define WGRAD_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * wgrad_run without a caller workspace and without any device allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The split-K partials go to a scratch array the library holds on each GPU
+ * it runs on, WGRAD_NOALLOC_SCRATCH_BYTES in size, from the first use until
+ * the process ends. Plans whose wgrad_workspace_bytes exceeds that size are
+ * rejected with WGRAD_ERR_INVALID_ARG before anything is enqueued (plan with
+ * a smaller split_k override, or use wgrad_run). The scratch needs no
+ * clearing: the main kernel writes every partial the reduce kernel reads.
+ * The first call on a GPU looks up the array's device address (no
+ * allocation); make one call before capturing a graph.
+ * The GPU is the stream's (the current device for the NULL stream). Every
+ * call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (different streams, or graphs
+ * replayed concurrently) race and give wrong results. Arguments, results
+ * and the other errors are those of wgrad_run; plans with S = 1 never touch
+ * the array.
+ */
+int wgrad_run_noalloc(const wgrad_plan_t* plan, const void* x, const void* dy, void* dw, void* stream);
+
 /*
  * Backward data of the same convolution (rocm-libraries PR 11602, "add
  * transpose load for bwd weight and bwd data": its dgrad part, which reads

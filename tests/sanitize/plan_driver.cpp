@@ -117,9 +117,28 @@ int main() {
             expect(wgrad_run_stage(plan, 2, fake_x, fake_dy, fake_dw, fake_ws, ws, nullptr) ==
                        (info.split_k > 1 ? WGRAD_ERR_HIP : WGRAD_OK),
                    "stage 2", line);
+            // the library-scratch variant: a workspace beyond the scratch is
+            // rejected before any device call; otherwise the stubbed device
+            // lookup (or launch) fails
+            const int before_na = stub_launch_count();
+            const int na = wgrad_run_noalloc(plan, fake_x, fake_dy, fake_dw, nullptr);
+            if (ws > WGRAD_NOALLOC_SCRATCH_BYTES) {
+                expect(na == WGRAD_ERR_INVALID_ARG, "oversized workspace accepted by the no-allocation run", line);
+                expect(stub_launch_count() == before_na, "oversized no-allocation run launched", line);
+            } else {
+                expect(na == WGRAD_ERR_HIP, "no-allocation run without a device", line);
+            }
+            expect(wgrad_run_noalloc(plan, fake_x, fake_dy, nullptr, nullptr) == WGRAD_ERR_INVALID_ARG,
+                   "no-allocation run accepted a NULL dw", line);
+            expect(wgrad_run_noalloc(plan, fake_x, fake_dy, odd, nullptr) == WGRAD_ERR_INVALID_ARG,
+                   "no-allocation run accepted a misaligned dw", line);
+            expect(stub_launch_count() == before_na + (ws > WGRAD_NOALLOC_SCRATCH_BYTES || ws ? 0 : 1),
+                   "a rejected no-allocation run launched", line);
         } else {
             expect(wgrad_run(plan, fake_x, fake_dy, fake_dw, fake_ws, ws, nullptr) == WGRAD_ERR_INVALID_ARG,
                    "wgrad run accepted a dgrad plan", line);
+            expect(wgrad_run_noalloc(plan, fake_x, fake_dy, fake_dw, nullptr) == WGRAD_ERR_INVALID_ARG,
+                   "no-allocation run accepted a dgrad plan", line);
             if (info.grid_main > 0) {   // an empty dX (N = 0) needs no pointers
                 expect(wgrad_dgrad_run(plan, fake_dy, fake_x, nullptr, nullptr) == WGRAD_ERR_INVALID_ARG,
                        "NULL dx accepted", line);
