@@ -26,8 +26,27 @@ and WRITE_SIZE runs, each scaled by what the counter reads for a plain
 device copy of known size (--copy-calibration), when they were taken on the
 current kernel sources.
 
+Per configuration, beside the graph-replayed steady state (us_per_step):
+* "iters": 10 warmup calls, then 50 timed calls of the whole path, each
+  bracketed by HIP events on the launch stream, with a 512 MiB fill kernel
+  between calls (outside the events) so that no call finds its inputs or
+  workspace in the L2 or the 256 MB MALL; median and min in us;
+* "hot": the same 50 events-bracketed calls with no fill in between (inputs
+  and workspace warm in the caches), labelled as such;
+* MFMA counters of the main kernel from the committed rocprofv3 record
+  profiles/mfma_counters.json, when it was taken on the same plan and
+  kernel sources (else null);
+* "cpu_oracle_s": the CPU oracle's wall time for the full dW of that
+  configuration on this host, with its thread count.
+
 cpu_baseline: the CPU oracle (fp64 direct loop, OpenMP) over the full
 headline dW, timed on this host.
+
+Roofline bound: the dense configurations (the dense split-K shape and the
+strided fp16 shape, and the 3D dense shape) are judged on MFMA throughput,
+the others on HBM bandwidth where their arithmetic intensity puts them;
+the headline roofline block also carries the HBM fraction of the same
+kernel and the MFMA and HBM fractions of the whole step.
 """
 
 from __future__ import annotations
@@ -49,6 +68,17 @@ METRIC = "wgrad TFLOP/s (GB/s for depthwise) and % of roofline, 1 MI355X"
 HEADLINE = "c2"
 ROTATE_BYTES = 600 * 2 ** 20
 GRAPH_MIN_LAUNCHES = 64
+FLUSH_BYTES = 512 * 2 ** 20
+ITER_WARMUP, ITER_TIMED = 10, 50
+# workloads judged on MFMA throughput whatever their exact arithmetic
+# intensity (the dense contractions); the others by intensity
+DENSE = ("c2", "c3", "c3d")
+
+
+def judged_bound(name, flops, nbytes):
+    if name.split(":")[-1] in DENSE:
+        return "mfma"
+    return "mfma" if flops / PEAK_MFMA_16 >= nbytes / PEAK_HBM else "hbm"
 
 
 def algorithmic(cfg, info):
@@ -99,6 +129,63 @@ def measured_traffic(workload, plan_name):
         return e["bytes_per_launch"]
     except (OSError, KeyError, ValueError):
         return None
+
+
+def measured_mfma(workload, plan_name):
+    """MFMA counters of the workload's main kernel from the committed
+    rocprofv3 record (profiles/mfma_counters.json), if taken on the same
+    plan built from the current sources of its kernel (else None)."""
+    path = os.path.join(ROOT, "profiles", "mfma_counters.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        e = t[workload]
+        if e.get("kernel") != plan_name or e.get("source_hash") != kernel_source_hash(plan_name):
+            return None
+        return {k: e[k] for k in ("mfma_insts", "useful_frac", "mfma_busy_cycles", "busy_frac_of_simd_cycles",
+                                  "launch_us") if k in e}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+class Timer:
+    """Events-bracketed calls on the current stream: 'flushed' with a large
+    fill kernel before each call (outside the events), or 'hot'."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        # GPU spin used to let the host queue a batch of calls ahead of the GPU
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record(s)
+        torch.cuda._sleep(1_000_000)
+        e1.record(s)
+        torch.cuda.synchronize()
+        self.spin_per_ms = 1_000_000 / max(1e-3, e0.elapsed_time(e1))
+
+    def calls(self, fn, n, flush):
+        torch = self.torch
+        s = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(self.spin_per_ms * 20))      # about 20 ms for the host to run ahead
+        for i in range(n):
+            if flush:
+                self.flush_buf.fill_(float(i & 7))
+            ev[i][0].record(s)
+            fn(i)
+            ev[i][1].record(s)
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+        return {"median_us": round(_median(us), 3), "min_us": round(min(us), 3), "n": n}
 
 
 class Case:
@@ -196,10 +283,19 @@ class Case:
             out.append(e0.elapsed_time(e1) * 1e-3 / (reps * glen))
         return out[0], out[1]
 
-    def row(self, sec_per_step, t_main, t_red):
+    def iteration_stats(self, timer):
+        """Median and min of 50 events-bracketed calls of the whole path,
+        flushed between calls and hot."""
+        for i in range(ITER_WARMUP):
+            self.step(i)
+        flushed = timer.calls(lambda i: self.step(i), ITER_TIMED, flush=True)
+        hot = timer.calls(lambda i: self.step(0), ITER_TIMED, flush=False)
+        return flushed, hot
+
+    def row(self, sec_per_step, t_main, t_red, flushed=None, hot=None):
         flops, nbytes = self.flops, self.bytes
         floor = max(flops / PEAK_MFMA_16, nbytes / PEAK_HBM)
-        return {
+        r = {
             "kernel": self.plan.name,
             "us_per_step": round(sec_per_step * 1e6, 3),
             "tflops": round(flops / sec_per_step / 1e12, 3),
@@ -207,14 +303,23 @@ class Case:
             "frac_mfma_peak": round(flops / sec_per_step / PEAK_MFMA_16, 4),
             "frac_hbm_peak": round(nbytes / sec_per_step / PEAK_HBM, 4),
             "frac_attainable": round(floor / sec_per_step, 4),
-            "bound": "mfma" if flops / PEAK_MFMA_16 >= nbytes / PEAK_HBM else "hbm",
+            "bound": judged_bound(self.name, flops, nbytes),
             "main_kernel_us": round(t_main * 1e6, 3),
             "reduce_kernel_us": round(t_red * 1e6, 3),
+            "main_kernel_frac_mfma_peak": round(flops / t_main / PEAK_MFMA_16, 4) if t_main else None,
+            "main_kernel_frac_hbm_peak": round(nbytes / t_main / PEAK_HBM, 4) if t_main else None,
             "split_k": self.plan.info["split_k"],
             "group_merge": self.plan.info["group_merge"],
             "input_sets": self.nsets,
             "hbm_bytes_measured": measured_traffic(self.name, self.plan.name),
+            "mfma_counters": measured_mfma(self.name, self.plan.name),
         }
+        if flushed is not None:
+            r["iters"] = dict(flushed, flush="512 MiB fill between calls, outside the events",
+                              tflops_at_median=round(flops / flushed["median_us"] / 1e6, 3),
+                              frac_attainable_at_median=round(floor / (flushed["median_us"] * 1e-6), 4))
+            r["hot"] = dict(hot, note="no flush between calls: inputs and workspace warm in L2/MALL")
+        return r
 
 
 class DgradCase(Case):
@@ -264,19 +369,32 @@ class DgradCase(Case):
         return e0.elapsed_time(e1) * 1e-3 / (reps * glen), 0.0
 
 
-def cpu_baseline(workloads, cfg):
+def oracle_time(workloads, cfg, dgrad=False):
+    """Wall time of the CPU oracle over the full output of one configuration
+    (the same seeded inputs as the GPU), with the threads it ran on."""
     import oracle
-    x_bits, dy_bits = workloads.inputs(cfg)
-    threads = oracle.max_threads()
-    t0 = time.perf_counter()
-    dw, _ = oracle.wgrad(cfg, x_bits, dy_bits)
+    if dgrad:
+        s0, s1 = cfg["seeds"]
+        dy_bits = workloads.draw(workloads.dy_shape(cfg), cfg["in_dtype"], cfg["dist"], s0 + 100)
+        w_bits = workloads.draw(oracle.dw_shape(cfg), cfg["in_dtype"], cfg["dist"], s1 + 100)
+        t0 = time.perf_counter()
+        out, _ = oracle.dgrad(cfg, dy_bits, w_bits)
+    else:
+        x_bits, dy_bits = workloads.inputs(cfg)
+        t0 = time.perf_counter()
+        out, _ = oracle.wgrad(cfg, x_bits, dy_bits)
     dt = time.perf_counter() - t0
+    return dt, oracle.last_threads(), out.size
+
+
+def cpu_baseline(workloads, cfg):
+    dt, threads, n = oracle_time(workloads, cfg)
     G = cfg["G"]
     taps = math.prod(cfg["filt_len"][: cfg["ndim"]])
     R = cfg["N"] * math.prod(cfg["out_len"][: cfg["ndim"]])
     flops = 2 * G * (cfg["K"] // G) * (cfg["C"] // G) * taps * R
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"full dW of the headline workload ({dw.size} elements, {flops/2:.3g} MACs) in "
+            "sample": f"full dW of the headline workload ({n} elements, {flops/2:.3g} MACs) in "
                       f"{dt:.2f} s, fp64, {threads} OpenMP threads"}
 
 
@@ -301,6 +419,7 @@ def main():
     import workloads
 
     torch.cuda.init()
+    timer = Timer(torch)
     if args.copy_calibration:
         src = torch.ones(128 * 2 ** 20, dtype=torch.bfloat16, device="cuda")   # 256 MiB
         dst = torch.empty_like(src)
@@ -321,7 +440,14 @@ def main():
             case = Case(torch, gcb, workloads, name, workloads.get(name))
         sec = case.time_steps(args.steps, args.warmup, use_graphs=not args.eager)
         t_main, t_red = case.kernel_times()
-        per[name] = case.row(sec, t_main, t_red)
+        flushed, hot = (None, None) if args.eager else case.iteration_stats(timer)
+        per[name] = case.row(sec, t_main, t_red, flushed, hot)
+        if not args.no_cpu_baseline and not args.eager:
+            base = name.split(":", 1)[-1]
+            dt, th, _ = oracle_time(workloads, workloads.get(base), dgrad=name.startswith("dgrad:"))
+            per[name]["cpu_oracle_s"] = round(dt, 3)
+            per[name]["cpu_oracle_threads"] = th
+            per[name]["gpu_speedup_vs_cpu_oracle"] = round(dt / sec, 1)
         print(f"[bench] {name}: {per[name]}", file=sys.stderr, flush=True)
         if name == HEADLINE:
             head = (case, sec, t_main)
@@ -349,10 +475,19 @@ def main():
         achieved, peak, unit = flops / t_main / 1e12, PEAK_MFMA_16 / 1e12, "TFLOP/s"
     else:
         achieved, peak, unit = nbytes / t_main / 1e9, PEAK_HBM / 1e9, "GB/s"
+    # contract fields first (dominant kernel: the main kernel), then the
+    # secondary fractions: the same kernel against the other peak, and the
+    # whole step (main + reduce + launch gaps) against both
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4),
             "traffic": measured_traffic(HEADLINE, case.plan.name),
-            "kernel": case.plan.name, "kernel_us": round(t_main * 1e6, 3)}
+            "kernel": case.plan.name, "kernel_us": round(t_main * 1e6, 3),
+            "kernel_frac_mfma": round(flops / t_main / PEAK_MFMA_16, 4),
+            "kernel_frac_hbm": round(nbytes / t_main / PEAK_HBM, 4),
+            "step_us": round(sec * 1e6, 3),
+            "step_frac_mfma": round(flops / sec / PEAK_MFMA_16, 4),
+            "step_frac_hbm": round(nbytes / sec / PEAK_HBM, 4),
+            "mfma_counters": hb.get("mfma_counters")}
     out = {
         "metric": METRIC,
         "value": round(flops / sec / 1e12, 3),

@@ -80,3 +80,39 @@ def test_traffic_record_needs_same_plan_and_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("c3", plan) is None
     (csrc / "rowslab.hip").write_text("// edited kernel\n")
     assert bench.measured_traffic("c2", plan) is None
+
+
+def test_mfma_counter_record_needs_same_plan_and_sources(tmp_path, monkeypatch):
+    plan = "wgrad_rowslab_bf16_m64c64x3_k32_slab1x32_kouter_spk82_gm1"
+    (tmp_path / "profiles").mkdir()
+    csrc = tmp_path / "grouped_convolution_backward_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for f in {f for _, f in bench._FAMILY_SOURCES} | set(bench._SHARED_SOURCES):
+        (csrc / f).write_text(f"// {f}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    rec = {"c2": {"kernel": plan, "source_hash": bench.kernel_source_hash(plan), "mfma_insts": 258048,
+                  "useful_frac": 0.875, "busy_frac_of_simd_cycles": 0.24, "other": 1}}
+    (tmp_path / "profiles" / "mfma_counters.json").write_text(json.dumps(rec))
+    got = bench.measured_mfma("c2", plan)
+    assert got == {"mfma_insts": 258048, "useful_frac": 0.875, "busy_frac_of_simd_cycles": 0.24}
+    assert bench.measured_mfma("c2", plan.replace("spk82", "spk41")) is None
+    (csrc / "rowslab.hip").write_text("// edited kernel\n")
+    assert bench.measured_mfma("c2", plan) is None
+
+
+def test_dense_workloads_are_judged_on_mfma():
+    # the dense split-K shape sits just under the ridge (HBM floor 3.22 us,
+    # MFMA floor 2.96 us) but is a dense contraction: judged on MFMA
+    cfg = workloads.get("c2")
+    flops, nbytes = bench.algorithmic(cfg, {"gemm_k": 32 * 56 * 56})
+    assert flops / bench.PEAK_MFMA_16 < nbytes / bench.PEAK_HBM
+    assert bench.judged_bound("c2", flops, nbytes) == "mfma"
+    assert bench.judged_bound("dgrad:c3", flops, nbytes) == "mfma"
+    cfg5 = workloads.get("c5")
+    f5, b5 = bench.algorithmic(cfg5, {"gemm_k": 16 * 56 * 56})
+    assert bench.judged_bound("c5", f5, b5) == "hbm"
+
+
+def test_median_of_even_and_odd_counts():
+    assert bench._median([3.0, 1.0, 2.0]) == 2.0
+    assert bench._median([4.0, 1.0, 3.0, 2.0]) == 2.5
