@@ -148,6 +148,208 @@ def measured_mfma(workload, plan_name):
         return None
 
 
+# plan-name prefix -> the main kernel's function (longer prefixes first)
+_KERNEL_FN = (("wgrad_rowslab_", "rowslab_kernel"), ("wgrad_ring_", "ring_kernel"), ("wgrad_mfma_", "mfma_kernel"),
+              ("wgrad_dwstrip_", "dw3_kernel"), ("wgrad_dwwin_", "dw2_kernel"), ("wgrad_dw_", "dw_kernel"),
+              ("dgrad_ring_", "dgrad_ring_kernel"), ("dgrad_dwring_", "dgrad_dw_ring_kernel"),
+              ("dgrad_dw_", "dgrad_dw_kernel"), ("dgrad_mfma_", "dgrad_kernel"))
+COPY_BYTES = 256 * 2 ** 20   # --copy-calibration: torch.neg over this many bytes, read and written
+
+
+def kernel_fn(plan_name):
+    for pre, fn in _KERNEL_FN:
+        if plan_name.startswith(pre):
+            return fn
+    raise ValueError(plan_name)
+
+
+def _kernel_parts(name):
+    """(function, template arguments) of a demangled kernel name."""
+    import re
+    name = name.replace("(anonymous namespace)", "")
+    cut = min([i for i in (name.find("<"), name.find("(")) if i >= 0] or [len(name)])
+    fn = re.split(r"[\s:]+", name[:cut].strip())[-1]
+    targs = ""
+    if "<" in name:
+        depth, start = 0, name.index("<")
+        for i in range(start, len(name)):
+            depth += name[i] == "<"
+            depth -= name[i] == ">"
+            if depth == 0:
+                targs = name[start:i + 1]
+                break
+    return fn, targs
+
+
+def _targs_match(plan_name, targs):
+    """Row-slab and ring kernels: the template arguments start with the M
+    block, C block and (row slab) filter width the plan name states."""
+    import re
+    m = re.search(r"_m(\d+)c(\d+)x(\d+)", plan_name)
+    if not m or not plan_name.startswith(("wgrad_rowslab_", "wgrad_ring_")):
+        return True
+    want = [m.group(1)] if plan_name.startswith("wgrad_ring_") else [m.group(1), m.group(2), m.group(3)]
+    got = [x.strip() for x in targs.strip("<>").split(",")]
+    return got[:len(want)] == want
+
+
+def summarize_trace(path, names):
+    """Markdown table of the main and reduce kernels of each workload from a
+    rocprofv3 kernel-trace CSV: dispatches matched by kernel function and
+    workgroup count (from the host plans), with their count and mean,
+    median and min duration."""
+    import csv
+    import grouped_convolution_backward_amd as gcb
+    import workloads
+    disp = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            gx = int(r.get("Grid_Size_X") or r.get("Grid_Size"))
+            wx = int(r.get("Workgroup_Size_X") or r.get("Workgroup_Size"))
+            fn, targs = _kernel_parts(r["Kernel_Name"])
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            disp.append((fn, targs, gx // max(1, wx), (t1 - t0) / 1e3, t0, t1))
+    lines = ["| workload | plan | kernel | workgroups | dispatches | mean us | median us | min us |",
+             "|---|---|---|---|---|---|---|---|"]
+    for name in names:
+        dgrad = name.startswith("dgrad:")
+        cfg = workloads.get(name.split(":", 1)[-1])
+        plan = (gcb.DgradPlan if dgrad else gcb.Plan)(cfg, hip_device=-1)
+        fn = kernel_fn(plan.name)
+        main = [d for d in disp if d[0] == fn and d[2] == plan.info["grid_main"] and _targs_match(plan.name, d[1])]
+        parts = [(fn, plan.info["grid_main"], main)]
+        if plan.info["split_k"] > 1 and not dgrad and main:
+            # the reduce launches of this workload: inside the time span of its main launches
+            lo, hi = min(d[4] for d in main), max(d[5] for d in main)
+            red = [d for d in disp if d[0] == "reduce_kernel" and d[2] == plan.info["grid_reduce"] and lo <= d[4] <= hi]
+            parts.append(("reduce_kernel", plan.info["grid_reduce"], red))
+        for fn, wgs, sel in parts:
+            if not sel:
+                lines.append(f"| {name} | `{plan.name}` | `{fn}` | {wgs} | 0 | | | |")
+                continue
+            t = sorted(d[3] for d in sel)
+            targs = sorted({d[1] for d in sel})
+            lines.append(f"| {name} | `{plan.name}` | `{fn}{targs[0] if len(targs) == 1 else ''}` | {wgs} | {len(t)} | "
+                         f"{sum(t) / len(t):.2f} | {t[len(t) // 2]:.2f} | {t[0]:.2f} |")
+    return "\n".join(lines)
+
+
+def read_counter_csv(path):
+    """Dispatches of a rocprofv3 counter-collection CSV: a list of
+    {"kernel", "wgs", "counters": {name: value}} in dispatch order (one row
+    per dispatch and counter in the file)."""
+    import csv
+    rows = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            grid = int(r.get("Grid_Size") or r.get("Grid_Size_X"))
+            wgsz = int(r.get("Workgroup_Size") or r.get("Workgroup_Size_X"))
+            d = rows.setdefault(int(r["Dispatch_Id"]), {
+                "kernel": r["Kernel_Name"], "wgs": grid // max(1, wgsz), "counters": {},
+                "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) if r.get("End_Timestamp") else 0})
+            name = r["Counter_Name"]
+            d["counters"][name] = d["counters"].get(name, 0.0) + float(r["Counter_Value"])
+    return [rows[k] for k in sorted(rows)]
+
+
+def _calls(dispatches, fn, wgs, plan_name=""):
+    out = []
+    for d in dispatches:
+        kfn, targs = _kernel_parts(d["kernel"])
+        if kfn == fn and d["wgs"] == wgs and _targs_match(plan_name, targs):
+            out.append(d)
+    return out
+
+
+def ingest_counters(pairs, out_dir=None):
+    """Build profiles/traffic.json and profiles/mfma_counters.json from
+    rocprofv3 counter CSVs: pairs of (workload, csv path). Each workload's
+    main-kernel dispatches are found by kernel function and workgroup count
+    (from the host plan) and averaged. FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) are scaled by what they read for the copy-calibration kernel
+    (torch neg over COPY_BYTES) in the same file; MFMA counters are kept as
+    read, with the useful fraction 2*M*N*R / (MOPS * 512) and the busy
+    fraction MFMA-busy cycles / (4 SIMDs * CU-busy cycles)."""
+    import grouped_convolution_backward_amd as gcb
+    import workloads
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    traffic, mfma = {}, {}
+    for workload, path in pairs:
+        disp = read_counter_csv(path)
+        dgrad = workload.startswith("dgrad:")
+        cfg = workloads.get(workload.split(":", 1)[-1])
+        plan = (gcb.DgradPlan if dgrad else gcb.Plan)(cfg, hip_device=-1)
+        fn = kernel_fn(plan.name)
+        calls = _calls(disp, fn, plan.info["grid_main"], plan.name)
+        if not calls:
+            raise ValueError(f"{workload}: no {fn} dispatch with {plan.info['grid_main']} workgroups in {path}")
+        avg = {}
+        for d in calls:
+            for k, v in d["counters"].items():
+                avg[k] = avg.get(k, 0.0) + v / len(calls)
+        base = {"kernel": plan.name, "source_hash": kernel_source_hash(plan.name), "kernel_fn": fn,
+                "dispatches": len(calls)}
+        if "FETCH_SIZE" in avg or "WRITE_SIZE" in avg:
+            rec = dict(base)
+            for cname, key in (("FETCH_SIZE", "fetch_bytes"), ("WRITE_SIZE", "write_bytes")):
+                if cname not in avg:
+                    continue
+                cal = [d["counters"][cname] for d in disp if "neg" in d["kernel"] and cname in d["counters"]]
+                if not cal:
+                    raise ValueError(f"{path}: no copy-calibration dispatch for {cname}")
+                scale = COPY_BYTES / (_median(cal) * 1024.0)
+                rec[key] = int(round(avg[cname] * 1024.0 * scale))
+                rec[key.replace("bytes", "scale")] = round(scale, 4)
+            prev = traffic.get(workload, {})
+            prev.update(rec)
+            traffic[workload] = prev
+        if "SQ_INSTS_MFMA" in avg:
+            flops, _ = algorithmic(cfg, gcb.Plan(cfg, hip_device=-1).info)
+            mops = avg.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + avg.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
+            rec = dict(base, mfma_insts=int(round(avg["SQ_INSTS_MFMA"])),
+                       mfma_busy_cycles=int(round(avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0))))
+            if mops:
+                rec["useful_frac"] = round(flops / (mops * 512.0), 4)
+            if avg.get("SQ_BUSY_CU_CYCLES"):
+                # both counters are sums over the chip; a CU has 4 SIMDs
+                rec["cu_busy_cycles"] = int(round(avg["SQ_BUSY_CU_CYCLES"]))
+                rec["busy_frac_of_simd_cycles"] = round(
+                    avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4 * avg["SQ_BUSY_CU_CYCLES"]), 4)
+            ns = sorted(d["ns"] for d in calls if d["ns"])
+            if ns:
+                rec["launch_us"] = round(ns[len(ns) // 2] / 1e3, 2)
+            mfma[workload] = rec
+    for fname, recs, about in (
+            ("traffic.json", traffic,
+             "HBM bytes per launch of each workload's main kernel: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
+             "dispatch, one counter per run), each scaled by what it reads for a plain device copy of known size "
+             "(torch neg over 256 MiB) in the same run; source_hash: kernel sources the counters were taken on"),
+            ("mfma_counters.json", mfma,
+             "MFMA counters of each dense workload's main kernel from one rocprofv3 --pmc run, averaged over its "
+             "dispatches: instruction count, MFMA-busy cycles summed over SIMDs, useful fraction 2*M*N*R / "
+             "(MOPS * 512), busy fraction MFMA-busy cycles / (4 SIMDs * CU-busy cycles, SQ_BUSY_CU_CYCLES), launch_us the "
+             "median dispatch duration under the counter run")):
+        if not recs:
+            continue
+        path = os.path.join(out_dir, fname)
+        try:
+            with open(path) as f:
+                old = json.load(f)
+        except (OSError, ValueError):
+            old = {}
+        old["_about"] = about
+        for k, v in recs.items():
+            merged = dict(old.get(k, {})) if old.get(k, {}).get("source_hash") == v["source_hash"] and \
+                old.get(k, {}).get("kernel") == v["kernel"] else {}
+            merged.update(v)
+            if "fetch_bytes" in merged and "write_bytes" in merged:
+                merged["bytes_per_launch"] = merged["fetch_bytes"] + merged["write_bytes"]
+            old[k] = merged
+        with open(path, "w") as f:
+            json.dump(old, f, indent=1, sort_keys=True)
+    return traffic, mfma
+
+
 def _median(v):
     v = sorted(v)
     n = len(v)
@@ -410,7 +612,20 @@ def main():
     ap.add_argument("--sweep-merge", action="store_true", help="also time the depthwise shape over Gm and S")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy (torch neg), the reference for HBM byte counters")
+    ap.add_argument("--ingest-counters", nargs="+", metavar="WORKLOAD=CSV",
+                    help="host only: write profiles/traffic.json and profiles/mfma_counters.json from rocprofv3 "
+                         "counter CSVs of eager bench runs, then exit")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="host only: print the per-workload kernel table of a rocprofv3 kernel-trace CSV, then exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, [n for n in args.configs.split(",") if n]
+                              if HEADLINE in args.configs.split(",") else [HEADLINE] + args.configs.split(",")))
+        return
+    if args.ingest_counters:
+        traffic, mfma = ingest_counters([tuple(x.split("=", 1)) for x in args.ingest_counters])
+        print(json.dumps({"traffic": traffic, "mfma": mfma}, indent=1))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)

@@ -116,3 +116,58 @@ def test_dense_workloads_are_judged_on_mfma():
 def test_median_of_even_and_odd_counts():
     assert bench._median([3.0, 1.0, 2.0]) == 2.0
     assert bench._median([4.0, 1.0, 3.0, 2.0]) == 2.5
+
+
+def _counter_csv(path, dispatches):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Correlation_Id", "Dispatch_Id", "Agent_Id", "Grid_Size", "Kernel_Name", "Workgroup_Size",
+                    "Counter_Name", "Counter_Value"])
+        for i, (kernel, wgs, wg_size, counters) in enumerate(dispatches):
+            for name, val in counters.items():
+                w.writerow([i + 1, i + 1, 1, wgs * wg_size, kernel, wg_size, name, val])
+
+
+def test_counter_ingestion_finds_main_kernels_and_scales_by_the_copy(tmp_path, monkeypatch):
+    """traffic.json and mfma_counters.json from rocprofv3 counter CSVs: the
+    main kernel is found by function and workgroup count (a dgrad kernel of
+    a similar name and a dispatch of another grid are ignored), FETCH_SIZE is
+    scaled by what it reads for the 256 MiB copy, MFMA fractions follow from
+    the counts."""
+    import grouped_convolution_backward_amd as gcb
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", ROOT)
+    p2 = gcb.Plan(workloads.get("c2"), hip_device=-1)
+    p4 = gcb.Plan(workloads.get("c4a"), hip_device=-1)
+    g2, g4 = p2.info["grid_main"], p4.info["grid_main"]
+    assert bench.kernel_fn(p2.name) == "rowslab_kernel" and bench.kernel_fn(p4.name) == "ring_kernel"
+    rs = "void wgrad::(anonymous namespace)::rowslab_kernel<64, 64, 3>(wgrad::RowSlabArgs)"
+    ring = "void wgrad::(anonymous namespace)::ring_kernel<32, 2>(wgrad::RingArgs)"
+    dring = "void wgrad::(anonymous namespace)::dgrad_ring_kernel<1>(wgrad::DgradRingArgs)"
+    neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>(int)"
+    # FETCH_SIZE reads half the true bytes here: the copy of 256 MiB reads 131072 KiB
+    fetch = tmp_path / "fetch.csv"
+    _counter_csv(fetch, [(neg, 4096, 256, {"FETCH_SIZE": 131072.0}),
+                         (rs, g2, 768, {"FETCH_SIZE": 13000.0}), (rs, g2, 768, {"FETCH_SIZE": 15000.0}),
+                         (rs, g2 + 8, 768, {"FETCH_SIZE": 99999.0}),
+                         (dring, g4, 320, {"FETCH_SIZE": 77777.0}), (ring, g4, 320, {"FETCH_SIZE": 12000.0})])
+    write = tmp_path / "write.csv"
+    _counter_csv(write, [(neg, 4096, 256, {"WRITE_SIZE": 262144.0}), (rs, g2, 768, {"WRITE_SIZE": 11808.0}),
+                         (ring, g4, 320, {"WRITE_SIZE": 2304.0})])
+    flops2, _ = bench.algorithmic(workloads.get("c2"), p2.info)
+    mf = tmp_path / "mfma.csv"
+    _counter_csv(mf, [(rs, g2, 768, {"SQ_INSTS_MFMA": 258048.0, "SQ_INSTS_VALU_MFMA_MOPS_BF16": flops2 / 512 / 0.875,
+                                    "SQ_VALU_MFMA_BUSY_CYCLES": 8257536.0, "SQ_BUSY_CU_CYCLES": 7805507.0})])
+    traffic, mfma = bench.ingest_counters([("c2", str(fetch)), ("c4a", str(fetch)), ("c2", str(write)),
+                                           ("c4a", str(write)), ("c2", str(mf))], out_dir=str(tmp_path / "profiles"))
+    t = json.loads((tmp_path / "profiles" / "traffic.json").read_text())
+    assert t["c2"]["fetch_bytes"] == 14000 * 1024 * 2 and t["c2"]["write_bytes"] == 11808 * 1024
+    assert t["c2"]["bytes_per_launch"] == t["c2"]["fetch_bytes"] + t["c2"]["write_bytes"]
+    assert t["c4a"]["fetch_bytes"] == 12000 * 1024 * 2
+    assert t["c2"]["source_hash"] == bench.kernel_source_hash(p2.name) and t["c2"]["kernel"] == p2.name
+    m = json.loads((tmp_path / "profiles" / "mfma_counters.json").read_text())["c2"]
+    assert m["mfma_insts"] == 258048 and m["useful_frac"] == 0.875
+    assert m["busy_frac_of_simd_cycles"] == round(8257536.0 / (4 * 7805507.0), 4)
+    with pytest.raises(ValueError):
+        bench.ingest_counters([("c3", str(fetch))], out_dir=str(tmp_path / "profiles"))
