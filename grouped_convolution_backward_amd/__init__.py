@@ -65,7 +65,7 @@ class wgrad_plan_info(ctypes.Structure):
 # every symbol include/wgrad.h declares
 EXPORTS = ("wgrad_plan", "wgrad_workspace_bytes", "wgrad_run", "wgrad_run_stage", "wgrad_plan_query",
            "wgrad_plan_describe", "wgrad_plan_destroy", "wgrad_last_error", "wgrad_version",
-           "wgrad_dgrad_plan", "wgrad_dgrad_run", "wgrad_run_noalloc")
+           "wgrad_dgrad_plan", "wgrad_dgrad_run", "wgrad_run_noalloc", "wgrad_probe_transpose_read")
 
 _lib = None
 
@@ -112,6 +112,8 @@ def load_library():
     lib.wgrad_dgrad_run.restype = ctypes.c_int
     lib.wgrad_run_noalloc.argtypes = [vp, vp, vp, vp, vp]
     lib.wgrad_run_noalloc.restype = ctypes.c_int
+    lib.wgrad_probe_transpose_read.argtypes = [vp, vp]
+    lib.wgrad_probe_transpose_read.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -190,6 +192,15 @@ def wgrad_run_noalloc(plan: "Plan", x, dy, dw, stream=None) -> None:
     """wgrad_run with the library's per-GPU scratch as the split-K workspace
     (no caller workspace, no device allocation)."""
     plan.run_noalloc(x, dy, dw, stream)
+
+
+def wgrad_probe_transpose_read(out, stream=None) -> None:
+    """Enqueue the transposed-LDS-read lane-map self-test into out, a
+    contiguous int16 GPU tensor of 512 elements."""
+    import torch
+    if not out.is_cuda or out.dtype != torch.int16 or not out.is_contiguous() or out.numel() != 512:
+        raise ValueError("out: need a contiguous int16 GPU tensor of 512 elements")
+    _check(load_library().wgrad_probe_transpose_read(out.data_ptr(), Plan._stream_ptr(stream)))
 
 
 def wgrad_dgrad_plan(problem: dict, variant: int = 0, tile: int = 0, split_k: int = 0, group_merge: int = 0,

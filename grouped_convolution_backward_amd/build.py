@@ -22,7 +22,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["kernels.hip", "rowslab.hip", "ring.hip", "depthwise.hip", "dgrad.hip", "dgrad_ring.hip", "noalloc.hip",
-           "plan.cpp", "abi.cpp"]
+           "probe.hip", "plan.cpp", "abi.cpp"]
 
 # Packed fp32 instructions are kept out of every code object.
 COMMON = ["-O3", "-fPIC", "-std=c++17", "--offload-arch=gfx950", "-mcode-object-version=5", "-I", INCLUDE,

@@ -254,6 +254,16 @@ void wgrad_plan_destroy(wgrad_plan_t* plan) { delete plan; }
 
 const char* wgrad_last_error(void) { return g_last_error.c_str(); }
 
-const char* wgrad_version(void) { return "0.1.0"; }
+const char* wgrad_version(void) { return "0.2.0"; }
+
+int wgrad_probe_transpose_read(void* out, void* stream) {
+    g_last_error.clear();
+    if (!out) return set_error(WGRAD_ERR_INVALID_ARG, "out must not be NULL");
+    if (!aligned16(out)) return set_error(WGRAD_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    const int e = wgrad::launch_tr_probe(static_cast<uint16_t*>(out), stream);
+    if (e != hipSuccess)
+        return set_error(WGRAD_ERR_HIP, std::string("probe kernel launch: ") + hipGetErrorString((hipError_t)e));
+    return WGRAD_OK;
+}
 
 }  // extern "C"

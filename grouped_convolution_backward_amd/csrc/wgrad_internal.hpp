@@ -288,5 +288,8 @@ int launch_dgrad_ring(const Plan& plan, const DgradRingArgs& a, void* stream);  
 // stream's GPU (noalloc.hip); resolved once per device. Returns a hipError_t
 // value (0 = success).
 int scratch_workspace(void* stream, void** ptr, size_t* bytes);
+// One wave's transposed-LDS-read fragment, 64 lanes x 8 values, into out
+// (probe.hip). Returns a hipError_t value.
+int launch_tr_probe(uint16_t* out, void* stream);
 
 }  // namespace wgrad

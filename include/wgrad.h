@@ -297,6 +297,21 @@ const char* wgrad_last_error(void);
 /* Library version, "major.minor.patch" (plumbing; no page defines it). */
 const char* wgrad_version(void);
 
+/*
+ * Self-test of the hardware lane map of the CDNA4 transposed LDS read
+ * (ds_read_b64_tr_b16) that every MFMA kernel here builds its operand
+ * fragments with (rocm-libraries PR 11602, "Technical Details": the K-outer
+ * tile read with ds_read_tr16_b64; its gfx1250 follow-up notes that a
+ * per-lane hardware probe settles such a map in one run). One wave fills a
+ * 16 x 64 tile of 16-bit codes (row << 8 | column) in LDS and reads one
+ * 32x32x16 operand fragment the way the kernels do; out (a device buffer of
+ * 512 uint16, 16-byte aligned) receives lane l's eight values at
+ * [8*l, 8*l + 8). The map the kernels assume: value e of lane l is the code
+ * of row 8*(l/32) + e, column l % 32. Enqueued on stream; no synchronisation.
+ * Errors: WGRAD_ERR_INVALID_ARG (NULL or misaligned out), WGRAD_ERR_HIP.
+ */
+int wgrad_probe_transpose_read(void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
