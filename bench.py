@@ -11,11 +11,21 @@ its TFLOP/s over exactly K timed steps. Every other configuration is timed
 the same way and reported under "per_config"; "dgrad:<name>" rows time
 backward data (dX from dY and W) of that workload's convolution.
 
+Before the first timed workload the headline's step graph is replayed,
+untimed, for 0.3 s so that the GPU clocks are at their loaded steady state;
+every workload then does its W warmup steps and K timed steps as below.
+
+The K timed steps: captured in a HIP graph (cycling through the input
+copies), replayed once untimed, then replayed with HIP events recorded on
+the replay stream around exactly K steps, behind a short GPU spin so that
+the host's graph submission is not on the clock; torch.cuda.synchronize()
+on both sides.
+
 Honest memory: each configuration cycles through enough copies of its inputs
 (> 512 MB in total) that no step finds its inputs in the 256 MB MALL left
 behind by the previous steps. Steps are replayed from HIP graphs (captured
 through torch, at least 64 steps per graph) so that neither the host's
-launch rate nor a graph replay's own start-up sets the time.
+launch rate nor a graph replay's own start-up sets the time (see below).
 
 Dominant-kernel roofline: the per-launch duration of the main kernel comes
 from HIP events recorded on the launch stream around replays of a graph that
@@ -68,6 +78,7 @@ METRIC = "wgrad TFLOP/s (GB/s for depthwise) and % of roofline, 1 MI355X"
 HEADLINE = "c2"
 ROTATE_BYTES = 600 * 2 ** 20
 GRAPH_MIN_LAUNCHES = 64
+MAX_GRAPH = 512           # steps per captured graph in the timed region
 FLUSH_BYTES = 512 * 2 ** 20
 ITER_WARMUP, ITER_TIMED = 10, 50
 # workloads judged on MFMA throughput whatever their exact arithmetic
@@ -373,12 +384,17 @@ class Timer:
         torch.cuda.synchronize()
         self.spin_per_ms = 1_000_000 / max(1e-3, e0.elapsed_time(e1))
 
+    def spin(self, ms):
+        """Keep the GPU busy for about ms milliseconds (lets the host queue
+        work behind it)."""
+        self.torch.cuda._sleep(int(self.spin_per_ms * ms))
+
     def calls(self, fn, n, flush):
         torch = self.torch
         s = torch.cuda.current_stream()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         torch.cuda.synchronize()
-        torch.cuda._sleep(int(self.spin_per_ms * 20))      # about 20 ms for the host to run ahead
+        self.spin(20.0)      # for the host to run ahead
         for i in range(n):
             if flush:
                 self.flush_buf.fill_(float(i & 7))
@@ -430,13 +446,21 @@ class Case:
         # enough launches per graph that the replay's own cost is spread thin
         return self.nsets * max(1, math.ceil(GRAPH_MIN_LAUNCHES / self.nsets))
 
-    def time_steps(self, steps, warmup, use_graphs=True):
+    def time_steps(self, steps, warmup, use_graphs=True, timer=None):
+        """Seconds per step over exactly `steps` steps after `warmup` untimed
+        ones. With graphs: the steps are captured (one graph of up to
+        MAX_GRAPH steps, cycling through the input sets, replayed as often as
+        needed plus a tail graph), replayed once untimed (upload), then timed
+        by HIP events on the replay stream, recorded behind a GPU spin so that
+        the host's graph submission is not on the clock; synchronized on both
+        sides. Without graphs (for profilers): host wall clock around eager
+        launches."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
         if use_graphs:
-            glen = self.graph_len()
+            glen = min(steps, MAX_GRAPH)
             full = self.capture(glen)
             rem = steps % glen
             tail = self.capture(rem) if rem else None
@@ -444,19 +468,23 @@ class Case:
             if tail is not None:
                 tail.replay()
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
+            s = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if timer is not None:
+                timer.spin(5.0)
+            e0.record(s)
             for _ in range(steps // glen):
                 full.replay()
             if tail is not None:
                 tail.replay()
+            e1.record(s)
             torch.cuda.synchronize()
-            t1 = time.perf_counter()
-        else:
-            t0 = time.perf_counter()
-            for i in range(steps):
-                self.step(i)
-            torch.cuda.synchronize()
-            t1 = time.perf_counter()
+            return e0.elapsed_time(e1) * 1e-3 / steps
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
         return (t1 - t0) / steps
 
     def kernel_times(self, reps=4):
@@ -571,6 +599,24 @@ class DgradCase(Case):
         return e0.elapsed_time(e1) * 1e-3 / (reps * glen), 0.0
 
 
+SETTLE_S = 0.3
+
+
+def settle_clocks(torch, gcb, workloads):
+    """Untimed: replay the headline workload's step graph for SETTLE_S
+    seconds so that the GPU clocks reach their loaded steady state before
+    the first timed workload (with a handful of warmup steps the first
+    workload of a run otherwise reads up to 10 % slower)."""
+    case = Case(torch, gcb, workloads, HEADLINE, workloads.get(HEADLINE))
+    g = case.capture(case.graph_len())
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        g.replay()
+        torch.cuda.synchronize()
+    del g, case
+    torch.cuda.empty_cache()
+
+
 def oracle_time(workloads, cfg, dgrad=False):
     """Wall time of the CPU oracle over the full output of one configuration
     (the same seeded inputs as the GPU), with the threads it ran on."""
@@ -646,6 +692,8 @@ def main():
     names = [n for n in args.configs.split(",") if n]
     if HEADLINE not in names:
         names.insert(0, HEADLINE)
+    if not args.eager:
+        settle_clocks(torch, gcb, workloads)
     per = {}
     head = None
     for name in names:
@@ -653,7 +701,7 @@ def main():
             case = DgradCase(torch, gcb, workloads, name, workloads.get(name.split(":", 1)[1]))
         else:
             case = Case(torch, gcb, workloads, name, workloads.get(name))
-        sec = case.time_steps(args.steps, args.warmup, use_graphs=not args.eager)
+        sec = case.time_steps(args.steps, args.warmup, use_graphs=not args.eager, timer=timer)
         t_main, t_red = case.kernel_times()
         flushed, hot = (None, None) if args.eager else case.iteration_stats(timer)
         per[name] = case.row(sec, t_main, t_red, flushed, hot)
