@@ -11,21 +11,18 @@ its TFLOP/s over exactly K timed steps. Every other configuration is timed
 the same way and reported under "per_config"; "dgrad:<name>" rows time
 backward data (dX from dY and W) of that workload's convolution.
 
-Before the first timed workload the headline's step graph is replayed,
-untimed, for 0.3 s so that the GPU clocks are at their loaded steady state;
-every workload then does its W warmup steps and K timed steps as below.
-
-The K timed steps: captured in a HIP graph (cycling through the input
-copies), replayed once untimed, then replayed with HIP events recorded on
-the replay stream around exactly K steps, behind a short GPU spin so that
-the host's graph submission is not on the clock; torch.cuda.synchronize()
-on both sides.
+Every workload does its W warmup steps, then its K timed steps: captured in
+HIP graphs (up to 512 steps per graph, cycling through the input copies),
+replayed untimed for 0.3 s (graph upload, and the GPU clocks back at their
+loaded state after the host has built the workload's inputs), then replayed
+with HIP events recorded on the replay stream around exactly K steps, behind
+a short GPU spin so that the host's graph submission is not on the clock;
+torch.cuda.synchronize() on both sides. Neither the host's launch rate nor
+a graph replay's own start-up sets the time.
 
 Honest memory: each configuration cycles through enough copies of its inputs
 (> 512 MB in total) that no step finds its inputs in the 256 MB MALL left
-behind by the previous steps. Steps are replayed from HIP graphs (captured
-through torch, at least 64 steps per graph) so that neither the host's
-launch rate nor a graph replay's own start-up sets the time (see below).
+behind by the previous steps.
 
 Dominant-kernel roofline: the per-launch duration of the main kernel comes
 from HIP events recorded on the launch stream around replays of a graph that
@@ -450,11 +447,12 @@ class Case:
         """Seconds per step over exactly `steps` steps after `warmup` untimed
         ones. With graphs: the steps are captured (one graph of up to
         MAX_GRAPH steps, cycling through the input sets, replayed as often as
-        needed plus a tail graph), replayed once untimed (upload), then timed
-        by HIP events on the replay stream, recorded behind a GPU spin so that
-        the host's graph submission is not on the clock; synchronized on both
-        sides. Without graphs (for profilers): host wall clock around eager
-        launches."""
+        needed plus a tail graph), replayed untimed for SETTLE_S seconds (graph
+        upload, and the GPU clocks back at their loaded state after the host
+        work of building this workload's inputs), then timed by HIP events on
+        the replay stream, recorded behind a GPU spin so that the host's graph
+        submission is not on the clock; synchronized on both sides. Without
+        graphs (for profilers): host wall clock around eager launches."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
@@ -464,10 +462,14 @@ class Case:
             full = self.capture(glen)
             rem = steps % glen
             tail = self.capture(rem) if rem else None
-            full.replay()                      # untimed: graph upload
-            if tail is not None:
-                tail.replay()
-            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            while True:                        # untimed: upload, settle
+                full.replay()
+                if tail is not None:
+                    tail.replay()
+                torch.cuda.synchronize()
+                if time.perf_counter() - t0 >= SETTLE_S:
+                    break
             s = torch.cuda.current_stream()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             if timer is not None:
@@ -599,22 +601,7 @@ class DgradCase(Case):
         return e0.elapsed_time(e1) * 1e-3 / (reps * glen), 0.0
 
 
-SETTLE_S = 0.3
-
-
-def settle_clocks(torch, gcb, workloads):
-    """Untimed: replay the headline workload's step graph for SETTLE_S
-    seconds so that the GPU clocks reach their loaded steady state before
-    the first timed workload (with a handful of warmup steps the first
-    workload of a run otherwise reads up to 10 % slower)."""
-    case = Case(torch, gcb, workloads, HEADLINE, workloads.get(HEADLINE))
-    g = case.capture(case.graph_len())
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < SETTLE_S:
-        g.replay()
-        torch.cuda.synchronize()
-    del g, case
-    torch.cuda.empty_cache()
+SETTLE_S = 0.3   # untimed replays before each workload's timed steps
 
 
 def oracle_time(workloads, cfg, dgrad=False):
@@ -692,8 +679,6 @@ def main():
     names = [n for n in args.configs.split(",") if n]
     if HEADLINE not in names:
         names.insert(0, HEADLINE)
-    if not args.eager:
-        settle_clocks(torch, gcb, workloads)
     per = {}
     head = None
     for name in names:
