@@ -173,7 +173,7 @@ def test_merge_with_single_merged_group():
     check_exact(cfg, bits.reshape(-1), dw64)
 
 
-@pytest.mark.parametrize("split_k", [1, 3, 8])
+@pytest.mark.parametrize("split_k", [1, 4, 8])
 def test_depthwise_kernel_split_sweep(split_k):
     cfg = workloads.problem("c5", N=2, in_len=(17, 23), out_len=(17, 23))
     xb, dyb = workloads.inputs(cfg, "int")
@@ -261,6 +261,10 @@ ROWSLAB_CASES = [
     ("c4b", dict(N=2, in_len=(300,), out_len=(300,))),           # 1D, row segments with a tail
     ("c2", dict(N=1, C=128, K=64, in_len=(10, 200), out_len=(10, 200))),   # wide rows: segments
     ("c2", dict(N=2, pad_lo=(0, 0), pad_hi=(2, 2))),             # asymmetric pad
+    # stride 2 with more M blocks: ragged (136 = 2*64 + 8), whole (256), grouped (G = 2, 192 rows each)
+    ("c3", dict(N=1, K=136, in_len=(20, 30), out_len=(10, 15))),
+    ("c3", dict(N=2, C=64, K=256, in_dtype="bf16", out_dtype="fp32", dist="uniform")),
+    ("c3", dict(N=1, G=2, C=128, K=384, in_len=(30, 30), out_len=(15, 15))),
 ]
 
 
