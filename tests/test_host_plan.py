@@ -508,3 +508,26 @@ def test_build_guard_rejects_scratch_in_counted_load_kernels():
     assert b.scratch_violations(clean) == []
     assert b.scratch_violations(clean + remarks("k2", 16, "False")) == [("k2", 16, "False")]
     assert b.scratch_violations(remarks("k3", 0, "True") + clean) == [("k3", 0, "True")]
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without libwgrad.so the package raises instead of computing anything
+    another way: a fresh interpreter whose package copy has no library."""
+    import shutil
+    import sys
+    pkg = os.path.dirname(gcb.__file__)
+    dst = tmp_path / "grouped_convolution_backward_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    root = os.path.dirname(pkg)
+    code = ("import grouped_convolution_backward_amd as g, workloads\n"
+            "try:\n"
+            "    g.Plan(workloads.get('c2'), hip_device=-1)\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('no error')\n")
+    env = dict(os.environ, PYTHONPATH=os.pathsep.join([str(tmp_path), root]))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=str(tmp_path),
+                         timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert "raised:" in out.stdout and "is not built" in out.stdout, out.stdout
