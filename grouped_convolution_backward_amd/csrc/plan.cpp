@@ -145,9 +145,11 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
         S = ceil_div(nslabs, spw);
     } else {
         // one workgroup per CU (the kernel's LDS allows no more): as many
-        // splits as fit beside the tiles, each a multiple of four slabs so the
-        // four slab streams of a workgroup get equal counts, then as few
-        // splits as those slab counts need, which keeps the workspace small
+        // splits as fit beside the tiles, each sized to a multiple of four
+        // slabs (the kernel's four slab streams), then as few splits as those
+        // slab counts need, which keeps the workspace small. The kernel
+        // deals the slabs out interleaved (split z takes z, z + S, ...), so
+        // splits differ by at most one slab.
         const int64_t smax = std::max<int64_t>(1, (int64_t)dev.num_cus / tiles);
         spw = 4 * ceil_div(ceil_div(nslabs, smax), 4);
         S = ceil_div(nslabs, spw);

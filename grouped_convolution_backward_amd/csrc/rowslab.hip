@@ -25,6 +25,9 @@
 //   16-byte chunks are XOR-swizzled by bit 1 of the row (64-channel rows), so
 //   the four rows a 16-lane group reads land on all banks; the loads apply
 //   the swizzle by choosing which source chunk each lane fetches.
+// * Split z of S takes slabs z, z + S, z + 2S, ...: at any moment the splits
+//   read neighbouring slabs, which measured faster per step than one
+//   contiguous range per split.
 // * The workgroup runs four slab streams; stream p takes every fourth slab of
 //   the workgroup's split into its own nb LDS buffers. A stream's MFMA waves
 //   (two, each holding 32 of 64 channels, or one for 32-channel blocks) hold
@@ -113,8 +116,9 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
     const int mbk = t % a.mblocks;
     const int gb = t / a.mblocks;
     const int m0 = mbk * MB, c0 = cbk * CB;
-    const int s_begin = z * a.spw;
-    const int s_end = min(a.nslabs, s_begin + a.spw);
+    // slabs of this split, interleaved with the other splits: z, z + S,
+    // z + 2S, ... (at any moment the splits read neighbouring slabs)
+    const int nmine = z < a.nslabs ? (a.nslabs - z + a.S - 1) / a.S : 0;
     const int fz = y / a.Yf, fy = y - fz * a.Yf;
     const int doff = fz * a.dd - a.pd, hoff = fy * a.dh - a.ph;
     const int kreal = a.PR * a.SW;
@@ -187,20 +191,21 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
     // loads of one slab this wave issues (compile-time per half)
     constexpr int NLW0 = (NL + WPS - 1) / WPS, NLW1 = NL / WPS;
 
-    // this stream's slabs: s_begin + pair + 4*i, i < cnt. Every wave of the
-    // workgroup passes the same cnt_max + 1 barriers.
-    const int cnt = s_begin + pair < s_end ? (s_end - s_begin - pair + 3) / 4 : 0;
-    const int cnt_max = s_end > s_begin ? (s_end - s_begin + 3) / 4 : 0;
+    // this stream's slabs: the split's slabs pair + 4*i, i < cnt. Every wave
+    // of the workgroup passes the same cnt_max + 1 barriers.
+    const int cnt = nmine > pair ? (nmine - pair + 3) / 4 : 0;
+    const int cnt_max = (nmine + 3) / 4;
+    auto slab_of = [&](int i) { return z + (pair + 4 * i) * a.S; };
     if (producer) {
         // issue slabs 0 .. NB-2, then before barrier i+1 issue slab i+NB-1
         // (into the buffer slab i-1 left) and wait for slab i+1
 #pragma unroll
         for (int i = 0; i < NB - 1; ++i)
-            if (i < cnt) issue_part(slab_geo(s_begin + pair + 4 * i), i, 0, NL);
+            if (i < cnt) issue_part(slab_geo(slab_of(i)), i, 0, NL);
         if (cnt > 0) vm_wait_slabs<NB - 2, NL>(min(cnt - 1, NB - 2));
         __builtin_amdgcn_s_barrier();
         for (int i = 0; i < cnt_max; ++i) {
-            if (i + NB - 1 < cnt) issue_part(slab_geo(s_begin + pair + 4 * (i + NB - 1)), (i + NB - 1) % NB, 0, NL);
+            if (i + NB - 1 < cnt) issue_part(slab_geo(slab_of(i + NB - 1)), (i + NB - 1) % NB, 0, NL);
             if (i + 1 < cnt) vm_wait_slabs<NB - 2, NL>(min(cnt - 2 - i, NB - 2));
             __builtin_amdgcn_s_barrier();
         }

@@ -90,7 +90,7 @@ struct RowSlabArgs {
     int32_t PR, SW;         // slab rows and columns (PR*SW <= the instance's positions)
     int32_t XW;             // X tile columns: (SW-1)*sw + (X-1)*dw + 1
     int32_t nseg, nslabs;   // column segments per row block, slabs in total
-    int32_t spw;            // slabs per workgroup (one split)
+    int32_t spw;            // slabs per split the split count was sized for (split z takes slabs z + m*S)
     int32_t S, total_wg, out_mode, slice_elems;
     uint32_t x_bytes, dy_bytes;   // buffer sizes for the bounds-checked loads
     MagicU32 mSW, mXW, mHo, mDo;
