@@ -205,7 +205,10 @@ def summarize_trace(path, names):
     """Markdown table of the main and reduce kernels of each workload from a
     rocprofv3 kernel-trace CSV: dispatches matched by kernel function and
     workgroup count (from the host plans), with their count and mean,
-    median and min duration."""
+    median and min duration. For split-K workloads the main kernel's
+    dispatches are also split by what runs next: its own reduce (whole
+    steps) or another main launch (the stage-only replays that
+    roofline.kernel_us is measured on)."""
     import csv
     import grouped_convolution_backward_amd as gcb
     import workloads
@@ -217,6 +220,8 @@ def summarize_trace(path, names):
             fn, targs = _kernel_parts(r["Kernel_Name"])
             t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
             disp.append((fn, targs, gx // max(1, wx), (t1 - t0) / 1e3, t0, t1))
+    disp.sort(key=lambda d: d[4])
+    following = {id(d): disp[i + 1] if i + 1 < len(disp) else None for i, d in enumerate(disp)}
     lines = ["| workload | plan | kernel | workgroups | dispatches | mean us | median us | min us |",
              "|---|---|---|---|---|---|---|---|"]
     for name in names:
@@ -231,14 +236,21 @@ def summarize_trace(path, names):
             lo, hi = min(d[4] for d in main), max(d[5] for d in main)
             red = [d for d in disp if d[0] == "reduce_kernel" and d[2] == plan.info["grid_reduce"] and lo <= d[4] <= hi]
             parts.append(("reduce_kernel", plan.info["grid_reduce"], red))
-        for fn, wgs, sel in parts:
+            nxt = lambda d: following[id(d)]
+            in_steps = [d for d in main if nxt(d) is not None and nxt(d)[0] == "reduce_kernel"]
+            alone = [d for d in main if nxt(d) is not None and nxt(d)[0] == fn and nxt(d)[2] == d[2]]
+            parts.insert(1, (fn, plan.info["grid_main"], in_steps, " (followed by its reduce: steps)"))
+            parts.insert(2, (fn, plan.info["grid_main"], alone, " (followed by another main launch)"))
+        for part in parts:
+            fn, wgs, sel = part[:3]
+            note = part[3] if len(part) > 3 else ""
             if not sel:
-                lines.append(f"| {name} | `{plan.name}` | `{fn}` | {wgs} | 0 | | | |")
+                lines.append(f"| {name} | `{plan.name}` | `{fn}`{note} | {wgs} | 0 | | | |")
                 continue
             t = sorted(d[3] for d in sel)
             targs = sorted({d[1] for d in sel})
-            lines.append(f"| {name} | `{plan.name}` | `{fn}{targs[0] if len(targs) == 1 else ''}` | {wgs} | {len(t)} | "
-                         f"{sum(t) / len(t):.2f} | {t[len(t) // 2]:.2f} | {t[0]:.2f} |")
+            lines.append(f"| {name} | `{plan.name}` | `{fn}{targs[0] if len(targs) == 1 else ''}`{note} | {wgs} | "
+                         f"{len(t)} | {sum(t) / len(t):.2f} | {t[len(t) // 2]:.2f} | {t[0]:.2f} |")
     return "\n".join(lines)
 
 
