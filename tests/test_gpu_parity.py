@@ -295,6 +295,19 @@ def test_rowslab_split_sweep(split_k):
     check_exact(cfg, bits.reshape(-1), dw64)
 
 
+@pytest.mark.parametrize("split_k", [1, 2, 3])
+def test_rowslab_interleaved_slabs_uneven(split_k):
+    """Slabs dealt to the splits in turn (strided shape): 11 output rows make
+    11 slabs, which split counts 2 and 3 share unevenly (6 + 5, 4 + 4 + 3),
+    so the four slab streams of a workgroup end on different counts."""
+    cfg = workloads.problem("c3", N=1, in_len=(22, 56), out_len=(11, 28))
+    cfg["name"] = f"rowslab_interleave_s{split_k}"
+    xb, dyb = workloads.inputs(cfg, "int")
+    _, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_ROWSLAB, split_k=split_k)
+    dw64, _ = oracle_ref(cfg, xb, dyb)
+    check_exact(cfg, bits.reshape(-1), dw64)
+
+
 DEPTHWISE_CASES = [
     # windowed depthwise kernel: tails, padding, strides along h, filter heights, fp16
     dict(ndim=2, G=64, N=2, C=64, K=64, in_len=(9, 13), filt_len=(3, 3), stride=(1, 1), dilation=(1, 1),
