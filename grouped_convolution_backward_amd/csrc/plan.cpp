@@ -113,6 +113,7 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
     for (int i = 0; i < kNumRsInstances; ++i) {
         const RsInstance& r = kRsInstances[i];
         if (r.mb != mb || r.cb != cb || r.xf != g.X) continue;
+        if (r.gs != 1 && g.Z == 1) continue;             // slab groups: 3D filters only
         if (r.stride != (g.sw == 2 ? 2 : 1)) continue;   // stride 2 splits the tile into even / odd columns
         if (rs_lds_bytes(r) > kRsLdsMax) continue;
         const int64_t ks = 16 * r.nks;
@@ -128,7 +129,10 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
         // useful fraction of the slab slots over whole rows: a row cut into
         // segments of sw fills ceil(Wo / sw) slabs
         const double eff = double(pr * g.Wo) / double(ceil_div(g.Wo, sw) * ks);
-        if (eff > best + 1e-9) { best = eff; inst = i; PR = pr; SW = sw; }
+        // equal slabs: 3D filters take the instance that deals slabs in
+        // groups (measured faster there, slower on 2D shapes)
+        const bool tie = inst >= 0 && eff > best - 1e-9 && eff < best + 1e-9;
+        if (eff > best + 1e-9 || (tie && r.gs > kRsInstances[inst].gs)) { best = eff; inst = i; PR = pr; SW = sw; }
     }
     if (inst < 0) return no("row-slab: no kernel instance fits this slab geometry");
     const RsInstance& ri = kRsInstances[inst];
@@ -176,6 +180,7 @@ bool plan_rowslab(const wgrad_problem& p, const Geo& g, const wgrad_overrides& o
     a.x_bytes = (uint32_t)(2 * p.N * g.Di * g.Hi * g.Wi * p.C);
     a.dy_bytes = (uint32_t)(2 * NHo * g.Wo * p.K);
     a.mSW = make_magic((uint32_t)SW); a.mXW = make_magic((uint32_t)XW); a.mHo = make_magic((uint32_t)g.Ho);
+    a.mSeg = make_magic((uint32_t)nseg);
     a.mDo = make_magic((uint32_t)g.Do);
     out.rs_inst = inst;
     out.lds_bytes = rs_lds_bytes(ri);
@@ -419,8 +424,8 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
         } else {
             const RowSlabArgs& a = out.rs;
             const RsInstance& ri = kRsInstances[out.rs_inst];
-            snprintf(name, sizeof name, "wgrad_rowslab_%s_m%dc%dx%d_k%d_slab%dx%d_kouter_spk%d_gm%d", dname, ri.mb,
-                     ri.cb, ri.xf, 16 * ri.nks, a.PR, a.SW, a.S, info.group_merge);
+            snprintf(name, sizeof name, "wgrad_rowslab_%s_m%dc%dx%d_k%d_slab%dx%d%s_kouter_spk%d_gm%d", dname, ri.mb,
+                     ri.cb, ri.xf, 16 * ri.nks, a.PR, a.SW, ri.gs == 4 ? "_sg4" : ri.gs == 2 ? "_sg2" : "", a.S, info.group_merge);
         }
     } else if (variant == WGRAD_VARIANT_DEPTHWISE) {
         if (o.group_merge > 1) return fail(msg, U, "group_merge applies to the MFMA variant only");

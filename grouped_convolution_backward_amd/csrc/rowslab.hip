@@ -25,9 +25,10 @@
 //   16-byte chunks are XOR-swizzled by bit 1 of the row (64-channel rows), so
 //   the four rows a 16-lane group reads land on all banks; the loads apply
 //   the swizzle by choosing which source chunk each lane fetches.
-// * Split z of S takes slabs z, z + S, z + 2S, ...: at any moment the splits
-//   read neighbouring slabs, which measured faster per step than one
-//   contiguous range per split.
+// * The slabs are dealt to the S splits in turn (split z takes z, z + S,
+//   z + 2S, ..., or the same for groups of four consecutive slabs on 3D
+//   filters): at any moment the splits read neighbouring slabs, which
+//   measured faster per step than one contiguous range per split.
 // * The workgroup runs four slab streams; stream p takes every fourth slab of
 //   the workgroup's split into its own nb LDS buffers. A stream's MFMA waves
 //   (two, each holding 32 of 64 channels, or one for 32-channel blocks) hold
@@ -76,7 +77,7 @@ __device__ __forceinline__ void vm_wait_slabs(int later) {
     else __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
 }
 
-template <int MB, int CB, int XF, int NKS, int NXR, int XWP, int STRIDE, int NB, int WPS, bool F16>
+template <int MB, int CB, int XF, int NKS, int NXR, int XWP, int STRIDE, int NB, int GS, int WPS, bool F16>
 __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSlabArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     constexpr int NT = 256 * WPS;                  // consumer threads (the MFMA waves)
@@ -116,9 +117,13 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
     const int mbk = t % a.mblocks;
     const int gb = t / a.mblocks;
     const int m0 = mbk * MB, c0 = cbk * CB;
-    // slabs of this split, interleaved with the other splits: z, z + S,
-    // z + 2S, ... (at any moment the splits read neighbouring slabs)
-    const int nmine = z < a.nslabs ? (a.nslabs - z + a.S - 1) / a.S : 0;
+    // slabs of this split, interleaved with the other splits in groups of GS
+    // consecutive slabs: groups z, z + S, z + 2S, ... (at any moment the
+    // splits read neighbouring slabs)
+    static_assert(GS == 1 || GS == 2 || GS == 4, "slab group");
+    constexpr int GPR = 4 / GS;                    // groups per round of the four streams
+    const int ngroups = (a.nslabs + GS - 1) / GS;
+    const int mygroups = z < ngroups ? (ngroups - z + a.S - 1) / a.S : 0;
     const int fz = y / a.Yf, fy = y - fz * a.Yf;
     const int doff = fz * a.dd - a.pd, hoff = fy * a.dh - a.ph;
     const int kreal = a.PR * a.SW;
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
     };
     auto slab_geo = [&](int slab) {
         SlabGeo gq;
-        const int sr = slab / a.nseg;
+        const int sr = (int)magic_div((uint32_t)slab, a.mSeg);
         const int row0 = sr * a.PR, wo0 = (slab - sr * a.nseg) * a.SW;
         const int r0 = row0 * a.Wo + wo0;
         gq.kvalid = min(kreal, a.SW == a.Wo ? a.NHo * a.Wo - r0 : a.Wo - wo0);
@@ -191,11 +196,14 @@ __global__ __launch_bounds__(256 * (WPS + 1), 1) void rowslab_kernel(const RowSl
     // loads of one slab this wave issues (compile-time per half)
     constexpr int NLW0 = (NL + WPS - 1) / WPS, NLW1 = NL / WPS;
 
-    // this stream's slabs: the split's slabs pair + 4*i, i < cnt. Every wave
-    // of the workgroup passes the same cnt_max + 1 barriers.
-    const int cnt = nmine > pair ? (nmine - pair + 3) / 4 : 0;
-    const int cnt_max = (nmine + 3) / 4;
-    auto slab_of = [&](int i) { return z + (pair + 4 * i) * a.S; };
+    // this stream's slabs: slab pair % GS of the split's groups
+    // pair / GS + GPR*i, i < cnt (the last group of all may be short). Every
+    // wave of the workgroup passes the same cnt_max + 1 barriers.
+    const int q = pair / GS, rr = pair % GS;
+    int cnt = mygroups > q ? (mygroups - q + GPR - 1) / GPR : 0;
+    if (GS > 1 && cnt > 0 && GS * (z + (q + (cnt - 1) * GPR) * a.S) + rr >= a.nslabs) --cnt;
+    const int cnt_max = (mygroups + GPR - 1) / GPR;
+    auto slab_of = [&](int i) { return GS * (z + (q + i * GPR) * a.S) + rr; };
     if (producer) {
         // issue slabs 0 .. NB-2, then before barrier i+1 issue slab i+NB-1
         // (into the buffer slab i-1 left) and wait for slab i+1
@@ -382,7 +390,7 @@ template <int I, bool F16>
 int launch_rs(const Plan& plan, const RowSlabArgs& a, hipStream_t s) {
     constexpr RsInstance r = kRsInstances[I];
     constexpr int wps = rs_waves_per_slab(r);
-    auto k = rowslab_kernel<r.mb, r.cb, r.xf, r.nks, r.nxr, r.xwp, r.stride, r.nb, wps, F16>;
+    auto k = rowslab_kernel<r.mb, r.cb, r.xf, r.nks, r.nxr, r.xwp, r.stride, r.nb, r.gs, wps, F16>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes);
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL(k, dim3(a.total_wg), dim3(256 * (wps + 1)), plan.lds_bytes, s, a);
@@ -391,7 +399,7 @@ int launch_rs(const Plan& plan, const RowSlabArgs& a, hipStream_t s) {
 
 template <bool F16>
 int launch_rs_t(const Plan& plan, const RowSlabArgs& a, hipStream_t s) {
-    static_assert(kNumRsInstances == 8, "dispatch table");
+    static_assert(kNumRsInstances == 9, "dispatch table");
     switch (plan.rs_inst) {
         case 0: return launch_rs<0, F16>(plan, a, s);
         case 1: return launch_rs<1, F16>(plan, a, s);
@@ -401,6 +409,7 @@ int launch_rs_t(const Plan& plan, const RowSlabArgs& a, hipStream_t s) {
         case 5: return launch_rs<5, F16>(plan, a, s);
         case 6: return launch_rs<6, F16>(plan, a, s);
         case 7: return launch_rs<7, F16>(plan, a, s);
+        case 8: return launch_rs<8, F16>(plan, a, s);
         default: return (int)hipErrorInvalidValue;
     }
 }

@@ -47,18 +47,21 @@ struct MfmaArgs {
 // elements, filled by 1 KB direct-to-LDS loads (8 rows of 64 channels or 16
 // rows of 32); slabs are loaded nb - 1 ahead of the one computed.
 constexpr int kRsLdsMax = 160 * 1024;
+// gs: the slabs are dealt to the splits in turn, in groups of gs consecutive
+// slabs (1, or 4 = one per slab stream)
 struct RsInstance {
-    int mb, cb, xf, nks, nxr, xwp, stride, nb;
+    int mb, cb, xf, nks, nxr, xwp, stride, nb, gs;
 };
 constexpr RsInstance kRsInstances[] = {
-    {64, 64, 3, 2, 1, 40, 1, 4},    // 32-position row segments
-    {64, 64, 3, 2, 1, 64, 2, 3},    // one row up to 31 wide, stride 2
-    {32, 32, 3, 4, 2, 32, 1, 4},    // two rows up to 30 wide
-    {32, 32, 3, 4, 1, 80, 1, 4},    // one row (or segment) up to 64 wide
-    {32, 32, 5, 8, 1, 144, 1, 2},   // 128-position row segments, width-5 filter
-    {64, 64, 1, 2, 1, 32, 1, 4},    // pointwise (width-1 filter): 32-position row segments
-    {64, 64, 1, 2, 1, 64, 2, 3},    // pointwise, stride 2: 32-position segments
-    {32, 32, 1, 4, 1, 64, 1, 4},    // pointwise, 32-channel blocks
+    {64, 64, 3, 2, 1, 40, 1, 4, 1},    // 32-position row segments
+    {64, 64, 3, 2, 1, 64, 2, 3, 1},    // one row up to 31 wide, stride 2
+    {32, 32, 3, 4, 2, 32, 1, 4, 1},    // two rows up to 30 wide
+    {32, 32, 3, 4, 1, 80, 1, 4, 1},    // one row (or segment) up to 64 wide
+    {32, 32, 5, 8, 1, 144, 1, 2, 1},   // 128-position row segments, width-5 filter
+    {64, 64, 1, 2, 1, 32, 1, 4, 1},    // pointwise (width-1 filter): 32-position row segments
+    {64, 64, 1, 2, 1, 64, 2, 3, 1},    // pointwise, stride 2: 32-position segments
+    {32, 32, 1, 4, 1, 64, 1, 4, 1},    // pointwise, 32-channel blocks
+    {64, 64, 3, 2, 1, 40, 1, 4, 4},    // as the first, slabs dealt four at a time (3D filters)
 };
 constexpr int kNumRsInstances = sizeof(kRsInstances) / sizeof(kRsInstances[0]);
 // MFMA waves per slab stream: two for 64-channel blocks (each holds 32
@@ -93,7 +96,7 @@ struct RowSlabArgs {
     int32_t spw;            // slabs per split the split count was sized for (split z takes slabs z + m*S)
     int32_t S, total_wg, out_mode, slice_elems;
     uint32_t x_bytes, dy_bytes;   // buffer sizes for the bounds-checked loads
-    MagicU32 mSW, mXW, mHo, mDo;
+    MagicU32 mSW, mXW, mHo, mDo, mSeg;   // mSeg: division by nseg
 };
 
 // Filter-row ring kernel (2D, 3x3 filter, dilation 1, h-stride 1 or 2): a

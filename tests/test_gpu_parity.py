@@ -456,6 +456,23 @@ def test_3d(i, variant):
             check_tol(cfg, vals.reshape(-1), dw64, ab64)
 
 
+@pytest.mark.parametrize("split_k", [1, 2, 3, 4])
+def test_3d_slab_groups_with_short_tail(split_k):
+    """3D filters deal the row slabs to the splits four at a time: 5 x 7
+    output rows make 35 slabs, nine groups with a short last one, shared
+    evenly and unevenly between the splits."""
+    cfg = dict(ndim=3, G=1, N=1, C=64, K=64, in_len=(5, 7, 28), filt_len=(3, 3, 3), stride=(1, 1, 1),
+               dilation=(1, 1, 1), pad_lo=(1, 1, 1), pad_hi=(1, 1, 1), in_dtype="bf16", out_dtype="bf16",
+               name=f"3d_groups_s{split_k}")
+    cfg["out_len"] = oracle.out_len(cfg)
+    xb = workloads.draw(workloads.x_shape(cfg), "bf16", "int", 870 + split_k)
+    dyb = workloads.draw(workloads.dy_shape(cfg), "bf16", "int", 880 + split_k)
+    _, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_ROWSLAB, split_k=split_k)
+    assert "_sg4_" in p.name, p.name
+    dw64, _ = oracle_ref(cfg, xb, dyb)
+    check_exact(cfg, bits.reshape(-1), dw64)
+
+
 # the widened rows at full size (pointwise and 3D dense), every element
 @pytest.mark.parametrize("name", list(workloads.WIDER))
 @pytest.mark.parametrize("dist", ["int", "uniform", "ones"])
