@@ -50,7 +50,7 @@ cpu_baseline: the CPU oracle (fp64 direct loop, OpenMP) over the full
 headline dW, timed on this host.
 
 Roofline bound: the dense configurations (the dense split-K shape and the
-strided fp16 shape, and the 3D dense shape) are judged on MFMA throughput,
+strided fp16 shape, and the 3D dense shape) are reported against MFMA throughput,
 the others on HBM bandwidth where their arithmetic intensity puts them;
 the headline roofline block also carries the HBM fraction of the same
 kernel and the MFMA and HBM fractions of the whole step.
@@ -78,12 +78,12 @@ GRAPH_MIN_LAUNCHES = 64
 MAX_GRAPH = 512           # steps per captured graph in the timed region
 FLUSH_BYTES = 512 * 2 ** 20
 ITER_WARMUP, ITER_TIMED = 10, 50
-# workloads judged on MFMA throughput whatever their exact arithmetic
+# workloads reported against MFMA throughput whatever their exact arithmetic
 # intensity (the dense contractions); the others by intensity
 DENSE = ("c2", "c3", "c3d")
 
 
-def judged_bound(name, flops, nbytes):
+def reported_bound(name, flops, nbytes):
     if name.split(":")[-1] in DENSE:
         return "mfma"
     return "mfma" if flops / PEAK_MFMA_16 >= nbytes / PEAK_HBM else "hbm"
@@ -547,7 +547,7 @@ class Case:
             "frac_mfma_peak": round(flops / sec_per_step / PEAK_MFMA_16, 4),
             "frac_hbm_peak": round(nbytes / sec_per_step / PEAK_HBM, 4),
             "frac_attainable": round(floor / sec_per_step, 4),
-            "bound": judged_bound(self.name, flops, nbytes),
+            "bound": reported_bound(self.name, flops, nbytes),
             "main_kernel_us": round(t_main * 1e6, 3),
             "reduce_kernel_us": round(t_red * 1e6, 3),
             "main_kernel_frac_mfma_peak": round(flops / t_main / PEAK_MFMA_16, 4) if t_main else None,

@@ -100,17 +100,17 @@ def test_mfma_counter_record_needs_same_plan_and_sources(tmp_path, monkeypatch):
     assert bench.measured_mfma("c2", plan) is None
 
 
-def test_dense_workloads_are_judged_on_mfma():
+def test_dense_workloads_are_reported_against_mfma():
     # the dense split-K shape sits just under the ridge (HBM floor 3.22 us,
-    # MFMA floor 2.96 us) but is a dense contraction: judged on MFMA
+    # MFMA floor 2.96 us) but is a dense contraction: reported against MFMA
     cfg = workloads.get("c2")
     flops, nbytes = bench.algorithmic(cfg, {"gemm_k": 32 * 56 * 56})
     assert flops / bench.PEAK_MFMA_16 < nbytes / bench.PEAK_HBM
-    assert bench.judged_bound("c2", flops, nbytes) == "mfma"
-    assert bench.judged_bound("dgrad:c3", flops, nbytes) == "mfma"
+    assert bench.reported_bound("c2", flops, nbytes) == "mfma"
+    assert bench.reported_bound("dgrad:c3", flops, nbytes) == "mfma"
     cfg5 = workloads.get("c5")
     f5, b5 = bench.algorithmic(cfg5, {"gemm_k": 16 * 56 * 56})
-    assert bench.judged_bound("c5", f5, b5) == "hbm"
+    assert bench.reported_bound("c5", f5, b5) == "hbm"
 
 
 def test_median_of_even_and_odd_counts():
