@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libwgrad.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kernels.hip", "rowslab.hip", "ring.hip", "depthwise.hip", "dgrad.hip", "dgrad_ring.hip", "noalloc.hip",
+SOURCES = ["kernels.hip", "rowslab.hip", "ring.hip", "depthwise.hip", "dwtile.hip", "dgrad.hip", "dgrad_ring.hip", "noalloc.hip",
            "probe.hip", "plan.cpp", "abi.cpp"]
 
 # Packed fp32 instructions are kept out of every code object.

@@ -164,6 +164,12 @@ int run_stages(const wgrad_plan_t* plan, int first, int last, const void* x, con
             a.dy = static_cast<const uint16_t*>(dy);
             a.out = main_out;
             e = wgrad::launch_rowslab(P, a, stream);
+        } else if (P.variant == WGRAD_VARIANT_DEPTHWISE && P.dwt_cb) {
+            wgrad::DwTileArgs a = P.dwt;
+            a.x = static_cast<const uint16_t*>(x);
+            a.dy = static_cast<const uint16_t*>(dy);
+            a.out = main_out;
+            e = wgrad::launch_dwtile(P, a, stream);
         } else if (P.variant == WGRAD_VARIANT_DEPTHWISE && P.dw3_ty) {
             wgrad::Dw3Args a = P.dw3;
             a.x = static_cast<const uint16_t*>(x);

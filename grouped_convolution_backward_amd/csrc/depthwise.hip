@@ -30,21 +30,6 @@ namespace {
 
 using namespace dev;
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-template <bool F16>
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    if constexpr (F16)
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
-    else
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-// (lo half of a, lo half of b) and (hi half of a, hi half of b)
-__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
 constexpr int kUnit = 4;            // output positions per unit
 constexpr int kWin = kUnit + 2;     // input columns per unit for a width-3 filter
 

@@ -456,8 +456,16 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
         if (R > 0) S = ceil_div(R, kslice);
         // kernel form: strip (3x3, unit stride and dilation), windowed (width 3), or generic
         const bool dw3_ok = dw2_ok && g.Y == 3 && g.sh == 1 && g.dh == 1;
-        int form = o.tile ? o.tile : dw3_ok ? 3 : dw2_ok ? 2 : 1;
-        if (form < 1 || form > 3) return fail(msg, U, "depthwise kernel form %d is not 1, 2 or 3", form);
+        // tile kernel: 256 channels a workgroup, two pixels' 512-byte runs per
+        // 1 KB load (on the 512-channel 56x56 shape whole-pixel 512-channel
+        // workgroups stream 1 % faster but write twice the partials, and the
+        // step is 3 % slower)
+        const int dwt_cb = p.C % 256 == 0 ? 256 : 0;
+        const bool dwt_ok = dw3_ok && dwt_cb != 0;
+        int form = o.tile ? o.tile : dwt_ok ? 4 : dw3_ok ? 3 : dw2_ok ? 2 : 1;
+        if (form < 1 || form > 4) return fail(msg, U, "depthwise kernel form %d is not 1, 2, 3 or 4", form);
+        if (form == 4 && !dwt_ok)
+            return fail(msg, U, "tile depthwise kernel needs a 3x3 filter with unit stride and dilation and C a multiple of 256");
         if (form == 3 && !dw3_ok) return fail(msg, U, "strip depthwise kernel needs a 3x3 filter with unit stride and dilation");
         if (form == 2 && !dw2_ok) return fail(msg, U, "windowed depthwise kernel needs filter width 3, w-stride 1, w-dilation 1 and height 1, 3 or 5");
         if (form == 1 && !((g.Y == 3 && g.X == 3) || (g.Y == 1 && (g.X == 3 || g.X == 5))))
@@ -466,7 +474,44 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
         // 64 x 8 = 512 channels of one pixel, so each load reads one contiguous run
         int cl2 = 64;
         while ((p.C / 8) % cl2) cl2 >>= 1;
-        if (form == 3) {
+        if (form == 4) {
+            DwTileArgs& b = out.dwt;
+            b = DwTileArgs{};
+            b.C = (int32_t)p.C; b.Hi = (int32_t)g.Hi; b.Wi = (int32_t)g.Wi; b.Ho = (int32_t)g.Ho; b.Wo = (int32_t)g.Wo;
+            b.ph = (int32_t)g.ph; b.pw = (int32_t)g.pw;
+            const int64_t tw = dwt_tile_w(dwt_cb);
+            b.tiles_x = (int32_t)ceil_div(g.Wo, tw);
+            b.cblocks = (int32_t)(p.C / dwt_cb);
+            // workgroups per channel block: one per CU unless overridden
+            const int64_t slots = std::max<int64_t>(1, (int64_t)dev.num_cus / b.cblocks);
+            // rows per tile: fewest passes x (rows + 2 halo rows + about 3 rows'
+            // worth of pipeline start and end per tile)
+            int64_t best_th = 1, best_cost = INT64_MAX;
+            for (int64_t th = 1; th <= g.Ho; ++th) {
+                const int64_t tiles = p.N * ceil_div(g.Ho, th) * b.tiles_x;
+                const int64_t passes = ceil_div(std::max<int64_t>(tiles, 1), o.split_k ? o.split_k : slots);
+                const int64_t cost = passes * (th + 5);
+                if (cost < best_cost) { best_cost = cost; best_th = th; }
+            }
+            b.th = (int32_t)best_th;
+            b.tiles_y = (int32_t)ceil_div(g.Ho, best_th);
+            const int64_t tiles = p.N * b.tiles_y * b.tiles_x;
+            if (tiles > kMax31) return fail(msg, U, "too many depthwise tiles");
+            b.tiles = (int32_t)tiles;
+            int64_t St = o.split_k ? o.split_k : slots;
+            St = std::max<int64_t>(1, std::min<int64_t>(St, tiles));
+            if (St > 65535 || St * b.cblocks > kMax31) return fail(msg, U, "split_k too large");
+            b.S = (int32_t)St;
+            b.total_wg = (int32_t)(St * b.cblocks);
+            b.out_mode = St == 1 ? out_final : OUT_WORKSPACE;
+            b.slice_elems = (int32_t)ndw;
+            b.x_bytes = (uint32_t)(2 * nx);
+            b.dy_bytes = (uint32_t)(2 * ndy);
+            out.dwt_cb = dwt_cb;
+            out.lds_bytes = dwt_lds_bytes(dwt_cb);
+            S = St;
+            cl = dwt_cb / 8;
+        } else if (form == 3) {
             Dw3Args& b = out.dw3;
             b = Dw3Args{};
             b.C = (int32_t)p.C; b.Hi = (int32_t)g.Hi; b.Wi = (int32_t)g.Wi; b.Ho = (int32_t)g.Ho; b.Wo = (int32_t)g.Wo;
@@ -555,12 +600,17 @@ int build_plan(const wgrad_problem& p, const wgrad_overrides* ov, const DeviceMo
         info.split_k = (int32_t)S;
         info.group_merge = 8 * cl;   // channels (groups) one workgroup covers
         info.vector_width = 8;
-        info.grid_main = out.dw3_ty ? out.dw3.total_wg : out.dw2_ty ? out.dw2.total_wg : a.total_wg;
-        info.tile = out.dw3_ty ? 3 : out.dw2_ty ? 2 : 1;
+        info.grid_main = out.dwt_cb ? out.dwt.total_wg : out.dw3_ty ? out.dw3.total_wg
+                                                       : out.dw2_ty ? out.dw2.total_wg : a.total_wg;
+        info.tile = out.dwt_cb ? 4 : out.dw3_ty ? 3 : out.dw2_ty ? 2 : 1;
         info.workspace_bytes = S > 1 ? S * ndw * 4 : 0;
-        snprintf(name, sizeof name, "wgrad_dw%s_%s_%lldx%lld_cl%d_spk%lld_gm%d",
-                 out.dw3_ty ? "strip" : out.dw2_ty ? "win" : "", dname,
-                 (long long)g.Y, (long long)g.X, cl, (long long)S, 8 * cl);
+        if (out.dwt_cb)
+            snprintf(name, sizeof name, "wgrad_dwtile_%s_3x3_t%dx%d_spk%lld_gm%d", dname, out.dwt.th,
+                     dwt_tile_w(out.dwt_cb), (long long)S, 8 * cl);
+        else
+            snprintf(name, sizeof name, "wgrad_dw%s_%s_%lldx%lld_cl%d_spk%lld_gm%d",
+                     out.dw3_ty ? "strip" : out.dw2_ty ? "win" : "", dname,
+                     (long long)g.Y, (long long)g.X, cl, (long long)S, 8 * cl);
     } else {
         // ---- group merge degree
         int64_t Gm = o.group_merge;

@@ -211,6 +211,38 @@ struct Dw3Args {
     uint32_t x_bytes, dy_bytes;
 };
 
+// Depthwise tile kernel (3x3 filter, stride and dilation 1 on both axes):
+// a workgroup takes output tiles of th rows x dwt_tile_w(cb) columns x cb
+// channels; one wave streams the tile's input rows into an LDS ring with
+// direct-to-LDS loads and seven waves compute, each on two adjacent output
+// columns, with dY loaded into registers.
+constexpr int kDwtCompute = 7;   // compute waves (one more wave loads)
+constexpr int kDwtRing = 6;      // input rows in the LDS ring
+// output columns per tile: each compute wave takes two columns of each of the
+// 64 / (cb / 8) pixels one wave-load covers
+constexpr int dwt_tile_w(int cb) { return 2 * kDwtCompute * (512 / cb); }
+// bytes of one ring row: tile_w + 2 pixels, rounded up to whole 1 KB loads
+constexpr int dwt_row_bytes(int cb) {
+    return (dwt_tile_w(cb) + 2 + 1024 / (cb * 2) - 1) / (1024 / (cb * 2)) * (1024 / (cb * 2)) * cb * 2;
+}
+// the ring, or in the epilogue one cb-channel x 9-tap fp32 block per compute wave
+constexpr int dwt_lds_bytes(int cb) {
+    return kDwtRing * dwt_row_bytes(cb) > kDwtCompute * cb * 9 * 4 ? kDwtRing * dwt_row_bytes(cb)
+                                                                  : kDwtCompute * cb * 9 * 4;
+}
+struct DwTileArgs {
+    const uint16_t* x;
+    const uint16_t* dy;
+    void* out;
+    int32_t C, Hi, Wi, Ho, Wo, ph, pw;
+    int32_t th;                    // output rows per tile
+    int32_t tiles_x, tiles_y;      // tiles per image row / column
+    int32_t tiles;                 // N * tiles_y * tiles_x
+    int32_t cblocks;               // C / cb
+    int32_t S, total_wg, out_mode, slice_elems;   // S: workgroups per channel block
+    uint32_t x_bytes, dy_bytes;
+};
+
 struct ReduceArgs {
     const float* ws;
     void* dw;
@@ -254,6 +286,8 @@ struct Plan {
     int dw2_ty;                  // filter height of the windowed depthwise instance (0 = not used)
     Dw3Args dw3;
     int dw3_ty;                  // filter height of the strip depthwise instance (0 = not used)
+    DwTileArgs dwt;
+    int dwt_cb;                  // channels per workgroup of the tile depthwise kernel (0 = not used)
     RowSlabArgs rs;
     int rs_inst;                 // index into kRsInstances
     RingArgs ring;
@@ -283,6 +317,7 @@ int launch_rowslab(const Plan& plan, const RowSlabArgs& a, void* stream);
 int launch_ring(const Plan& plan, const RingArgs& a, void* stream);          // ring.hip
 int launch_depthwise2(const Plan& plan, const Dw2Args& a, void* stream);
 int launch_depthwise3(const Plan& plan, const Dw3Args& a, void* stream);
+int launch_dwtile(const Plan& plan, const DwTileArgs& a, void* stream);   // dwtile.hip
 int launch_reduce(const ReduceArgs& a, int64_t grid, void* stream);
 int launch_dgrad(const Plan& plan, const DgradArgs& a, void* stream);   // dgrad.hip
 int launch_dgrad_dw(const Plan& plan, const DgradDwArgs& a, void* stream);

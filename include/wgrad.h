@@ -98,7 +98,8 @@ typedef struct {
     int32_t variant;      /* wgrad_variant */
     int32_t tile;         /* MFMA variant: tile id (see wgrad_plan_info.tile). DEPTHWISE variant:
                              kernel form, 1 = generic filter, 2 = windowed (filter width 3,
-                             w-stride 1, w-dilation 1), 3 = strip (3x3, stride 1, dilation 1).
+                             w-stride 1, w-dilation 1), 3 = strip (3x3, stride 1, dilation 1),
+                             4 = tile (3x3, stride 1, dilation 1, C a multiple of 256).
                              ROWSLAB variant: form, 1 = one filter row per workgroup, 2 = every
                              filter row per workgroup (input-row ring). 0 = auto */
 } wgrad_overrides;
@@ -110,7 +111,7 @@ typedef struct {
     int64_t gemm_n;          /* (C/G)*Z*Y*X */
     int64_t gemm_k;          /* N*Do*Ho*Wo */
     int32_t variant;         /* wgrad_variant actually used */
-    int32_t tile;            /* MFMA tile id, depthwise kernel form (1 generic, 2 windowed, 3 strip),
+    int32_t tile;            /* MFMA tile id, depthwise kernel form (1 generic, 2 windowed, 3 strip, 4 tile),
                                 2 for the row-slab ring form, or 0 (row-slab, one filter row) */
     int32_t tile_m, tile_n, tile_k;
     int32_t split_k;         /* S */

@@ -26,6 +26,7 @@ int launch_rowslab(const Plan&, const RowSlabArgs&, void*) { return no_device();
 int launch_ring(const Plan&, const RingArgs&, void*) { return no_device(); }
 int launch_depthwise2(const Plan&, const Dw2Args&, void*) { return no_device(); }
 int launch_depthwise3(const Plan&, const Dw3Args&, void*) { return no_device(); }
+int launch_dwtile(const Plan&, const DwTileArgs&, void*) { return no_device(); }
 int launch_reduce(const ReduceArgs&, int64_t, void*) { return no_device(); }
 int launch_dgrad(const Plan&, const DgradArgs&, void*) { return no_device(); }
 int launch_dgrad_dw(const Plan&, const DgradDwArgs&, void*) { return no_device(); }

@@ -1,7 +1,7 @@
 """Maximum sizes: the kernels at the largest inputs their plans accept, and
 the fallback just past that limit, checked exactly against the oracle.
 
-The row-slab, ring, strip and row-ring kernels address X and dY through
+The row-slab, ring, strip, tile and row-ring kernels address X and dY through
 32-bit buffer offsets, so their plans take inputs below 2 GiB only; larger
 inputs go to the flat kernels. These tests put X and dY within a few
 hundred KB of 2 GiB (and one case just past it), where a wrapped or
@@ -59,7 +59,7 @@ def zero_one(bits, dtype):
     return np.where(oracle.widen(bits, dtype) != 0, one, np.uint16(0)).astype(np.uint16).reshape(bits.shape)
 
 
-def wgrad_case(base, N, P, out_dtype, want_prefix):
+def wgrad_case(base, N, P, out_dtype, want_prefix, **ov):
     cfg = dict(base, N=N, out_dtype=out_dtype)
     small = dict(cfg, N=P)
     s0, s1 = base["seeds"]
@@ -72,7 +72,7 @@ def wgrad_case(base, N, P, out_dtype, want_prefix):
     assert float(np.max(exact)) < 2 ** 24, "inputs too large for an exact fp32 check"
     assert float(np.max(exact)) > 0
 
-    p = gcb.Plan(cfg)
+    p = gcb.Plan(cfg, **ov)
     assert p.name.startswith(want_prefix), p.name
     x = tiled(xb, cfg["in_dtype"], N // P)
     dy = tiled(dyb, cfg["in_dtype"], N // P)
@@ -114,11 +114,12 @@ def test_just_past_2_gib_takes_the_flat_kernel():
     torch.cuda.empty_cache()
 
 
-def test_depthwise_strip_just_below_2_gib():
+@pytest.mark.parametrize("form,prefix", [(3, "wgrad_dwstrip_"), (4, "wgrad_dwtile_")])
+def test_depthwise_just_below_2_gib(form, prefix):
     base = workloads.CONFIGS["c5"]
     P = 16
     N = (GIB2 - 1) // image_bytes(base, base["C"]) // P * P        # 656 images
-    xbytes, _ = wgrad_case(base, N, P, "fp32", "wgrad_dwstrip_")
+    xbytes, _ = wgrad_case(base, N, P, "fp32", prefix, variant=gcb.VARIANT_DEPTHWISE, tile=form)
     assert GIB2 - 17 * image_bytes(base, base["C"]) < xbytes < GIB2
     torch.cuda.empty_cache()
 

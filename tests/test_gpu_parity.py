@@ -331,7 +331,7 @@ def test_depthwise_windowed(i):
         xb = workloads.draw(workloads.x_shape(cfg), cfg["in_dtype"], dist, seed)
         dyb = workloads.draw(workloads.dy_shape(cfg), cfg["in_dtype"], dist, seed + 1)
         vals, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_DEPTHWISE)
-        assert "dwwin" in p.name or "dwstrip" in p.name
+        assert "dwwin" in p.name or "dwstrip" in p.name or "dwtile" in p.name
         dw64, ab64 = oracle_ref(cfg, xb, dyb)
         if dist == "int":
             check_exact(cfg, bits.reshape(-1), dw64)
@@ -363,7 +363,7 @@ def test_depthwise_strip(i):
     for dist, seed in (("int", 700 + i), ("uniform", 750 + i)):
         xb = workloads.draw(workloads.x_shape(cfg), cfg["in_dtype"], dist, seed)
         dyb = workloads.draw(workloads.dy_shape(cfg), cfg["in_dtype"], dist, seed + 1)
-        vals, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_DEPTHWISE)
+        vals, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_DEPTHWISE, tile=3)
         assert "dwstrip" in p.name
         dw64, ab64 = oracle_ref(cfg, xb, dyb)
         if dist == "int":
@@ -398,9 +398,55 @@ def test_depthwise_strip_xcd_item_order(split_k):
     check_exact(cfg, bits.reshape(-1), dw64)
 
 
-@pytest.mark.parametrize("form", [1, 2, 3])
+# tile depthwise kernel (3x3, unit stride and dilation, C a multiple of 256):
+# 512- and 256-channel workgroups, several channel blocks, ragged tiles in
+# both directions (Wo not a multiple of the tile width, Ho of the tile
+# height), images narrower or shorter than a tile, pads 0, 1 and 2 on either
+# side, fp16 and fp32 outputs
+TILE_CASES = [
+    dict(G=512, N=2, C=512, K=512, in_len=(17, 30), pad_lo=(1, 1), pad_hi=(1, 1), in_dtype="bf16", out_dtype="bf16"),
+    dict(G=256, N=3, C=256, K=256, in_len=(9, 31), pad_lo=(1, 1), pad_hi=(1, 1), in_dtype="fp16", out_dtype="fp16"),
+    dict(G=768, N=1, C=768, K=768, in_len=(12, 29), pad_lo=(0, 2), pad_hi=(2, 0), in_dtype="bf16", out_dtype="fp32"),
+    dict(G=1024, N=2, C=1024, K=1024, in_len=(5, 15), pad_lo=(1, 0), pad_hi=(0, 1), in_dtype="fp16", out_dtype="fp32"),
+    dict(G=512, N=5, C=512, K=512, in_len=(1, 1), pad_lo=(1, 1), pad_hi=(1, 1), in_dtype="bf16", out_dtype="bf16"),
+    dict(G=512, N=1, C=512, K=512, in_len=(3, 60), pad_lo=(0, 0), pad_hi=(0, 0), in_dtype="bf16", out_dtype="bf16"),
+    dict(G=256, N=2, C=256, K=256, in_len=(40, 3), pad_lo=(2, 2), pad_hi=(2, 2), in_dtype="bf16", out_dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(TILE_CASES)))
+def test_depthwise_tile(i):
+    cfg = dict(TILE_CASES[i], name=f"dwtile{i}", ndim=2, filt_len=(3, 3), stride=(1, 1), dilation=(1, 1))
+    cfg["out_len"] = oracle.out_len(cfg)
+    for dist, seed in (("int", 800 + i), ("uniform", 850 + i)):
+        xb = workloads.draw(workloads.x_shape(cfg), cfg["in_dtype"], dist, seed)
+        dyb = workloads.draw(workloads.dy_shape(cfg), cfg["in_dtype"], dist, seed + 1)
+        vals, bits, p = run_gpu(cfg, xb, dyb)
+        assert "dwtile" in p.name
+        dw64, ab64 = oracle_ref(cfg, xb, dyb)
+        if dist == "int":
+            check_exact(cfg, bits.reshape(-1), dw64)
+        else:
+            check_tol(cfg, vals.reshape(-1), dw64, ab64)
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 3, 7, 64, 1000])
+def test_depthwise_tile_split_sweep(split_k):
+    # 2 images of 30 x 29 outputs: tiles of up to 14 x 14 (3 per row, the
+    # last one column wide); a workgroup takes several tiles when the split
+    # is below the tile count, and the split is cut to the tile count above it
+    cfg = workloads.problem("c5", N=2, in_len=(30, 29), out_len=(30, 29))
+    cfg["name"] = f"dwtile_split{split_k}"
+    xb, dyb = workloads.inputs(cfg, "int")
+    _, bits, p = run_gpu(cfg, xb, dyb, variant=gcb.VARIANT_DEPTHWISE, tile=4, split_k=split_k)
+    assert "dwtile" in p.name and p.info["split_k"] <= split_k
+    dw64, _ = oracle_ref(cfg, xb, dyb)
+    check_exact(cfg, bits.reshape(-1), dw64)
+
+
+@pytest.mark.parametrize("form", [1, 2, 3, 4])
 def test_depthwise_forms_agree_bitwise(form):
-    # the three depthwise kernel forms on one shape, integer inputs: each is
+    # the four depthwise kernel forms on one shape, integer inputs: each is
     # exact, so they agree bit for bit
     cfg = workloads.problem("c5", N=2, in_len=(11, 14), out_len=(11, 14))
     xb, dyb = workloads.inputs(cfg, "int")

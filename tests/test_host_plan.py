@@ -66,7 +66,7 @@ def test_plan_sizes_for_configs(name):
 def test_depthwise_config_uses_depthwise_kernel_and_dense_uses_mfma():
     p5 = plan(workloads.CONFIGS["c5"])
     assert p5.info["variant"] == gcb.VARIANT_DEPTHWISE
-    assert p5.info["tile"] == 3 and "dwstrip" in p5.name     # 3x3, unit stride: strip form
+    assert p5.info["tile"] == 4 and "dwtile" in p5.name      # 3x3, unit stride, C % 256 == 0: tile form
     # the tiny golden shape has too few output rows for row slabs
     assert plan(workloads.CONFIGS["c1"]).info["variant"] == gcb.VARIANT_MFMA
     for n in ("c2", "c3", "c4a", "c4b"):
@@ -170,20 +170,47 @@ def test_fp32_output_mode_plans():
 
 
 def test_depthwise_kernel_forms():
-    # tile selects the depthwise kernel form: 1 generic, 2 windowed, 3 strip
+    # tile selects the depthwise kernel form: 1 generic, 2 windowed, 3 strip, 4 tile
     c5 = workloads.CONFIGS["c5"]
-    for form, tag in ((1, "wgrad_dw_"), (2, "wgrad_dwwin_"), (3, "wgrad_dwstrip_")):
+    for form, tag in ((1, "wgrad_dw_"), (2, "wgrad_dwwin_"), (3, "wgrad_dwstrip_"), (4, "wgrad_dwtile_")):
         p = plan(c5, variant=gcb.VARIANT_DEPTHWISE, tile=form)
         assert p.info["tile"] == form and p.name.startswith(tag), (form, p.name)
-    # the strip form needs unit stride and dilation in both axes
+    # the strip and tile forms need unit stride and dilation in both axes
     strided = workloads.problem("c5", stride=(2, 1))
     assert plan(strided).info["tile"] == 2
     _expect(gcb.ERR_UNSUPPORTED, strided, variant=gcb.VARIANT_DEPTHWISE, tile=3)
-    _expect(gcb.ERR_UNSUPPORTED, c5, variant=gcb.VARIANT_DEPTHWISE, tile=4)
+    _expect(gcb.ERR_UNSUPPORTED, strided, variant=gcb.VARIANT_DEPTHWISE, tile=4)
+    _expect(gcb.ERR_UNSUPPORTED, c5, variant=gcb.VARIANT_DEPTHWISE, tile=5)
     # strip form: one 8-wave workgroup per CU, a split per workgroup of a
     # 256-channel block (two blocks for C = 512)
-    p = plan(c5)
+    p = plan(c5, variant=gcb.VARIANT_DEPTHWISE, tile=3)
     assert p.info["grid_main"] == 256 and p.info["split_k"] == 128
+
+
+def test_depthwise_tile_form_plans():
+    # c5: 256-channel workgroups (two blocks), 14 x 28 output tiles (56 / 14 =
+    # 4 rows of tiles, 56 / 28 = 2 columns), 16 x 8 tiles = 128 workgroups per
+    # block, one tile each, one slice per workgroup
+    p = plan(workloads.CONFIGS["c5"])
+    assert p.info["grid_main"] == 256 and p.info["split_k"] == 128
+    assert p.name == "wgrad_dwtile_bf16_3x3_t14x28_spk128_gm256"
+    assert p.workspace_bytes == 128 * 512 * 9 * 4
+    # three blocks for C = 768
+    p = plan(dict(workloads.CONFIGS["c5"], G=768, C=768, K=768))
+    assert p.info["tile"] == 4 and "x28_" in p.name and p.name.endswith("gm256")
+    assert p.info["grid_main"] == 3 * p.info["split_k"] and p.info["split_k"] <= 256 // 3
+    # channels not a multiple of 256: the strip form
+    assert plan(dict(workloads.CONFIGS["c5"], G=96, C=96, K=96)).info["tile"] == 3
+    # split_k: workgroups per channel block, at most one per tile; S = 1 writes dW
+    p = plan(workloads.CONFIGS["c5"], split_k=1)
+    assert p.info["split_k"] == 1 and p.workspace_bytes == 0 and p.info["grid_main"] == 2
+    small = workloads.problem("c5", N=1, in_len=(3, 3), out_len=(3, 3))
+    p = plan(small, split_k=50)
+    assert p.info["split_k"] == 3 and "_t1x28_" in p.name    # three 1-row tiles, one per workgroup
+    # more tiles than workgroups: rows per tile grow before tiles are shared
+    big = workloads.problem("c5", N=64)
+    p = plan(big)
+    assert p.info["split_k"] == 128 and p.info["grid_main"] == 256
 
 
 def test_magic_division_exhaustive(tmp_path):

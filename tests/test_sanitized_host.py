@@ -100,6 +100,10 @@ def _cases():
     for n in (0, 1):
         cases.append((0, workloads.problem("c2", N=n), (0, 0, 0, 0)))
         cases.append((1, workloads.problem("c5", N=n), (0, 0, 0, 0)))
+    # the depthwise tile form: a workgroup over several tiles, and every form override
+    cases.append((0, workloads.problem("c5", N=64), (0, 0, 0, 0)))
+    for form in (1, 2, 3, 4, 5):
+        cases.append((0, workloads.problem("c5", N=3, in_len=(9, 31), out_len=(9, 31)), (5, 0, 2, form)))
     bad = [
         workloads.problem("c1", G=3), workloads.problem("c1", N=-1), workloads.problem("c2", N=20000),
         workloads.problem("c1", in_len=(1, 1), pad_lo=(0, 0), pad_hi=(0, 0)),
