@@ -85,7 +85,8 @@ int wgrad_dgrad_run(const wgrad_plan_t* plan, const void* dy, const void* w, voi
     if (!plan) return set_error(WGRAD_ERR_INVALID_ARG, "plan is NULL");
     const wgrad::Plan& P = plan->plan;
     if (P.op != wgrad::OP_DGRAD) return set_error(WGRAD_ERR_INVALID_ARG, "not a backward-data plan");
-    const int64_t grid = P.dg_ring >= 0 ? P.dgr.total_wg : P.dg_dw ? P.dgdw.total_wg : P.dg.total_wg;
+    const int64_t grid = P.dg_ring >= 0 ? P.dgr.total_wg : P.dg_dwt ? P.dgdwt.total_wg
+                                                    : P.dg_dw ? P.dgdw.total_wg : P.dg.total_wg;
     if (grid == 0) return WGRAD_OK;   // N = 0: dX is empty
     if (!dx || !dy || !w) return set_error(WGRAD_ERR_INVALID_ARG, "dy, w and dx must not be NULL");
     if (!aligned16(dy) || !aligned16(w) || !aligned16(dx))
@@ -97,6 +98,12 @@ int wgrad_dgrad_run(const wgrad_plan_t* plan, const void* dy, const void* w, voi
         a.w = static_cast<const uint16_t*>(w);
         a.dx = dx;
         e = wgrad::launch_dgrad_ring(P, a, stream);
+    } else if (P.dg_dwt) {
+        wgrad::DgradDwTileArgs a = P.dgdwt;
+        a.dy = static_cast<const uint16_t*>(dy);
+        a.w = static_cast<const uint16_t*>(w);
+        a.dx = dx;
+        e = wgrad::launch_dgrad_dwtile(P, a, stream);
     } else if (P.dg_dw) {
         wgrad::DgradDwArgs a = P.dgdw;
         a.dy = static_cast<const uint16_t*>(dy);

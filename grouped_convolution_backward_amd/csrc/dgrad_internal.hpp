@@ -68,6 +68,23 @@ struct DgradDwArgs {
     int32_t nch, items;
     uint32_t dy_bytes;
 };
+// Depthwise backward data, tile form (2D, 3x3 filter, unit stride and
+// dilation, C a multiple of 256): dX tiles of th rows x dwt_tile_w(cb)
+// columns x cb channels (cb = 256); one wave streams the tile's dY
+// rows (halo included) into an LDS ring, seven compute waves write dX rows
+// from registers.
+struct DgradDwTileArgs {
+    const uint16_t* dy;
+    const uint16_t* w;
+    void* dx;
+    int32_t C, Hi, Wi, Ho, Wo, ph, pw;
+    int32_t th;                    // dX rows per tile
+    int32_t tiles_x, tiles_y;      // tiles per dX row / column
+    int32_t tiles;                 // N * tiles_y * tiles_x, per channel block
+    int32_t cblocks;               // C / cb
+    int32_t total_wg, out_mode;    // workgroups (each takes tiles wg, wg + total_wg, ... of all blocks)
+    uint32_t dy_bytes;
+};
 // Row-ring backward data (2D, 3x3 filter, unit stride and dilation): a
 // workgroup owns one group block and one block of cbd dX channels, keeps that
 // block's weights in LDS for the whole launch, and walks its split of input

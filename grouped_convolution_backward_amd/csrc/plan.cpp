@@ -786,6 +786,64 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     // row-walking form: 3x3 in 2D, unit stride and dilation
     const bool ring_ok = dw_cb && g.Di == 1 && g.Z == 1 && g.Y == 3 && g.X == 3 && g.sh == 1 && g.sw == 1 &&
                          g.dh == 1 && g.dw == 1 && 2 * p.N * g.Ho * g.Wo * p.C < (int64_t{1} << 31);
+    // tile form (tile id 7): whole 256-channel runs of the dY rows streamed
+    // into an LDS ring; automatic where it applies
+    const bool dwt_ok = ring_ok && p.C % 256 == 0;
+    if (o.tile == 7 && (!dwt_ok || o.group_merge > 1))
+        return fail(msg, U, "the depthwise dgrad tile kernel needs C/G = K/G = 1, C a multiple of 256 and a 2D 3x3 "
+                            "filter with unit stride and dilation");
+    if (dwt_ok && (o.tile == 7 || (o.tile == 0 && o.group_merge <= 1))) {
+        out = Plan{};
+        out.dg_ring = -1;
+        out.op = OP_DGRAD;
+        out.prob = p;
+        out.in_f16 = p.in_dtype == WGRAD_FP16;
+        out.variant = WGRAD_VARIANT_DGRAD;
+        // 256-channel blocks (512-channel ones, whole pixels per load, measured
+        // the same on the 512-channel 56x56 shape)
+        const int cb = 256;
+        out.dg_dwt = cb;
+        DgradDwTileArgs& a = out.dgdwt;
+        a = DgradDwTileArgs{};
+        a.C = (int32_t)p.C;
+        a.Hi = (int32_t)g.Hi; a.Wi = (int32_t)g.Wi; a.Ho = (int32_t)g.Ho; a.Wo = (int32_t)g.Wo;
+        a.ph = (int32_t)g.ph; a.pw = (int32_t)g.pw;
+        const int64_t tw = dwt_tile_w(cb);
+        a.tiles_x = (int32_t)ceil_div(g.Wi, tw);
+        a.cblocks = (int32_t)(p.C / cb);
+        // dX rows per tile: fewest passes of one workgroup per CU x (rows +
+        // 2 halo rows + about 3 rows' worth of pipeline start and end)
+        int64_t best_th = 1, best_cost = INT64_MAX;
+        for (int64_t th = 1; th <= g.Hi; ++th) {
+            const int64_t tiles = p.N * ceil_div(g.Hi, th) * a.tiles_x * a.cblocks;
+            const int64_t cost = ceil_div(std::max<int64_t>(tiles, 1), (int64_t)dev.num_cus) * (th + 5);
+            if (cost < best_cost) { best_cost = cost; best_th = th; }
+        }
+        a.th = (int32_t)best_th;
+        a.tiles_y = (int32_t)ceil_div(g.Hi, best_th);
+        const int64_t tiles = p.N * a.tiles_y * a.tiles_x;
+        if (tiles * a.cblocks > kMax31) return fail(msg, U, "grid too large");
+        a.tiles = (int32_t)tiles;
+        a.total_wg = (int32_t)std::min<int64_t>(tiles * a.cblocks, dev.num_cus);
+        a.out_mode = p.out_dtype == WGRAD_BF16 ? OUT_BF16 : p.out_dtype == WGRAD_FP16 ? OUT_FP16 : OUT_FP32;
+        a.dy_bytes = (uint32_t)(2 * p.N * g.Ho * g.Wo * p.C);
+        wgrad_plan_info& info = out.info;
+        {
+            const int64_t all[3] = {g.Do, g.Ho, g.Wo};
+            for (int i = 0; i < 3; ++i) info.out_len[i] = i < p.ndim ? all[3 - p.ndim + i] : 0;
+        }
+        info.gemm_m = M; info.gemm_n = 1; info.gemm_k = taps;
+        info.variant = WGRAD_VARIANT_DGRAD;
+        info.tile = 7;
+        info.tile_m = (int32_t)(best_th * tw); info.tile_n = cb; info.tile_k = (int32_t)taps;
+        info.split_k = 1; info.group_merge = 1; info.vector_width = 8;
+        info.grid_main = a.total_wg;
+        info.num_cus = dev.num_cus;
+        char name[160];
+        snprintf(name, sizeof name, "dgrad_dwtile_%s_t%dx%d", out.in_f16 ? "fp16" : "bf16", a.th, (int)tw);
+        out.name = name;
+        return WGRAD_OK;
+    }
     const bool dw_tile = o.tile == 4 || o.tile == 5;
     if (dw_tile && o.group_merge > 1) return fail(msg, U, "the depthwise dgrad kernel does not merge groups");
     if (dw_tile && !dw_cb)

@@ -299,6 +299,8 @@ struct Plan {
     int dg_bn, dg_v, dg_bk;      // dgrad tile width, load vector width, channels per reduction chunk
     DgradDwArgs dgdw;
     int dg_dw;                   // 1: the depthwise dgrad kernel
+    DgradDwTileArgs dgdwt;
+    int dg_dwt;                  // channels per workgroup of the depthwise dgrad tile kernel (0 = not used)
     DgradRingArgs dgr;
     int dg_ring;                 // index into kDgRingInstances, or -1
     std::string name;
@@ -321,6 +323,7 @@ int launch_dwtile(const Plan& plan, const DwTileArgs& a, void* stream);   // dwt
 int launch_reduce(const ReduceArgs& a, int64_t grid, void* stream);
 int launch_dgrad(const Plan& plan, const DgradArgs& a, void* stream);   // dgrad.hip
 int launch_dgrad_dw(const Plan& plan, const DgradDwArgs& a, void* stream);
+int launch_dgrad_dwtile(const Plan& plan, const DgradDwTileArgs& a, void* stream);   // dwtile.hip
 int launch_dgrad_ring(const Plan& plan, const DgradRingArgs& a, void* stream);   // dgrad_ring.hip
 // Device address and size of the library's split-K scratch array on the
 // stream's GPU (noalloc.hip); resolved once per device. Returns a hipError_t

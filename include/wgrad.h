@@ -248,7 +248,10 @@ int wgrad_run_noalloc(const wgrad_plan_t* plan, const void* x, const void* dy, v
  * (positions x channels) tiles; 4 = the depthwise direct kernel (C/G = K/G
  * = 1, C % 8 == 0, at most 2048 taps), which auto picks for such shapes, in
  * its row-walking form for 2D 3x3 filters with unit stride and dilation; 5 =
- * the depthwise kernel's per-tap form for any depthwise shape; 6 = the
+ * the depthwise kernel's per-tap form for any depthwise shape; 7 = the
+ * depthwise tile kernel (2D 3x3 filter, unit stride and dilation, C/G = K/G
+ * = 1 and C a multiple of 256), which auto picks ahead of 4 where it
+ * applies; 6 = the
  * row-ring MFMA kernel (2D 3x3 filter, unit stride and dilation, h pads at
  * most 2 in all, input rows of at most 64 positions, C/G, C and K multiples
  * of 8, Gm*K/G of 32 or 64 and Gm*C/G a multiple of 32), which keeps a group

@@ -30,6 +30,7 @@ int launch_dwtile(const Plan&, const DwTileArgs&, void*) { return no_device(); }
 int launch_reduce(const ReduceArgs&, int64_t, void*) { return no_device(); }
 int launch_dgrad(const Plan&, const DgradArgs&, void*) { return no_device(); }
 int launch_dgrad_dw(const Plan&, const DgradDwArgs&, void*) { return no_device(); }
+int launch_dgrad_dwtile(const Plan&, const DgradDwTileArgs&, void*) { return no_device(); }
 int launch_dgrad_ring(const Plan&, const DgradRingArgs&, void*) { return no_device(); }
 int scratch_workspace(void*, void**, size_t*) { return (int)hipErrorNoDevice; }
 int launch_tr_probe(uint16_t*, void*) { return no_device(); }

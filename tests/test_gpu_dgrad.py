@@ -183,7 +183,7 @@ def test_dgrad_depthwise_kernel(i):
     cfg = prob(*DW[i], name=f"dw{i}")
     dyb, wb = draw(cfg, "int", (700 + i, 800 + i))
     _, bits, p = run_dgrad(cfg, dyb, wb)
-    assert p.info["tile"] in (4, 5) and p.name.startswith("dgrad_dw")
+    assert p.info["tile"] in (4, 5, 7) and p.name.startswith("dgrad_dw")
     # both depthwise forms (row walk where it applies) agree bitwise
     _, bits5, p5 = run_dgrad(cfg, dyb, wb, tile=5)
     assert p5.info["tile"] == 5 and np.array_equal(bits, bits5)
@@ -193,6 +193,37 @@ def test_dgrad_depthwise_kernel(i):
     _, bits_mfma, p1 = run_dgrad(cfg, dyb, wb, tile=1)
     assert p1.info["tile"] == 1 and np.array_equal(bits, bits_mfma)
     dyb, wb = draw(cfg, "uniform", (900 + i, 1000 + i))
+    vals, _, _ = run_dgrad(cfg, dyb, wb)
+    dx64, ab64 = oracle.dgrad(cfg, dyb, wb)
+    check_tol(cfg, vals, dx64, ab64)
+
+
+# depthwise tile kernel (2D 3x3, unit stride and dilation, C a multiple of
+# 256): ragged tiles both ways, images smaller than a tile, pads 0 to 2,
+# several channel blocks, fp16 and fp32 outputs, and more tiles than
+# workgroups (a workgroup walks several, taller tiles)
+DW_TILE = [
+    (2, 256, 2, 1, 1, (17, 30), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+    (2, 512, 1, 1, 1, (9, 31), (3, 3), (1, 1), (0, 2), (2, 0), (1, 1), "fp16", "fp32"),
+    (2, 768, 3, 1, 1, (1, 1), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+    (2, 256, 1, 1, 1, (40, 3), (3, 3), (1, 1), (2, 2), (2, 2), (1, 1), "fp16", None),
+    (2, 256, 2, 1, 1, (6, 60), (3, 3), (1, 1), (0, 0), (0, 0), (1, 1), "bf16", None),
+    (2, 256, 256, 1, 1, (8, 8), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), "bf16", None),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DW_TILE)))
+def test_dgrad_depthwise_tile(i):
+    cfg = prob(*DW_TILE[i], name=f"dwt{i}")
+    dyb, wb = draw(cfg, "int", (1700 + i, 1800 + i))
+    _, bits, p = run_dgrad(cfg, dyb, wb)
+    assert p.info["tile"] == 7 and p.name.startswith("dgrad_dwtile")
+    dx64, _ = oracle.dgrad(cfg, dyb, wb)
+    check_exact(cfg, bits, dx64)
+    # the row-walking form gives the same (exact) bits
+    _, bits4, p4 = run_dgrad(cfg, dyb, wb, tile=4)
+    assert p4.info["tile"] == 4 and np.array_equal(bits, bits4)
+    dyb, wb = draw(cfg, "uniform", (1900 + i, 2000 + i))
     vals, _, _ = run_dgrad(cfg, dyb, wb)
     dx64, ab64 = oracle.dgrad(cfg, dyb, wb)
     check_tol(cfg, vals, dx64, ab64)

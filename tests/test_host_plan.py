@@ -397,10 +397,22 @@ def test_dgrad_plans_sizes_and_tiles():
     for bad in (3, 64):
         with pytest.raises(gcb.WgradError):
             dplan(workloads.CONFIGS["c4a"], group_merge=bad)
-    # depthwise shapes take the direct kernel; forcing it elsewhere is unsupported
-    # 3x3 unit stride: the row-walking form, 256-channel blocks of 4-channel
-    # lanes, 4 strips per workgroup, row chunks per strip from the planner
+    # depthwise shapes take the direct kernels; forcing them elsewhere is unsupported
+    # 3x3 unit stride, C a multiple of 256: the tile form, 14 x 28 dX tiles of
+    # 256 channels, 16 x 4 x 2 x 2 = 256 tiles, one per workgroup
     p = dplan(workloads.CONFIGS["c5"])
+    assert p.info["tile"] == 7 and p.name == "dgrad_dwtile_bf16_t14x28" and p.info["grid_main"] == 256
+    # more tiles than CUs: taller tiles first, then several per workgroup
+    p = dplan(dict(workloads.CONFIGS["c5"], N=64))
+    assert p.info["tile"] == 7 and p.info["grid_main"] == 256 and p.name.endswith("_t56x28")
+    # C not a multiple of 256: the row-walking form
+    assert dplan(dict(workloads.CONFIGS["c5"], G=96, C=96, K=96)).info["tile"] == 4
+    with pytest.raises(gcb.WgradError) as e:
+        dplan(dict(workloads.CONFIGS["c5"], G=96, C=96, K=96), tile=7)
+    assert e.value.code == gcb.ERR_UNSUPPORTED
+    # the row-walking form on c5: 256-channel blocks of 4-channel lanes, 4
+    # strips per workgroup, row chunks per strip from the planner
+    p = dplan(workloads.CONFIGS["c5"], tile=4)
     assert p.info["tile"] == 4 and p.name.startswith("dgrad_dwring") and p.info["tile_n"] == 256
     nch = int(p.name.rsplit("_ch", 1)[1])
     assert p.info["grid_main"] == 2 * ((16 * 14 * nch + 3) // 4)

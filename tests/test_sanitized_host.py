@@ -104,6 +104,11 @@ def _cases():
     cases.append((0, workloads.problem("c5", N=64), (0, 0, 0, 0)))
     for form in (1, 2, 3, 4, 5):
         cases.append((0, workloads.problem("c5", N=3, in_len=(9, 31), out_len=(9, 31)), (5, 0, 2, form)))
+    # backward data: the depthwise tile form (taller tiles, several per
+    # workgroup) and every depthwise form override
+    cases.append((1, workloads.problem("c5", N=64), (0, 0, 0, 0)))
+    for form in (4, 5, 7, 8):
+        cases.append((1, workloads.problem("c5", N=3, in_len=(9, 31), out_len=(9, 31)), (0, 0, 0, form)))
     bad = [
         workloads.problem("c1", G=3), workloads.problem("c1", N=-1), workloads.problem("c2", N=20000),
         workloads.problem("c1", in_len=(1, 1), pad_lo=(0, 0), pad_hi=(0, 0)),
