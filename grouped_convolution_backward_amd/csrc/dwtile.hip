@@ -380,9 +380,12 @@ __global__ __launch_bounds__(64 * (kDwtCompute + 1), 1) void dgrad_dwtile_kernel
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     float lo = 0.f, hi = 0.f;
+                    // ring row s + 2 - ky; the row read at this step last, so
+                    // that its LDS reads are in flight while the other two
+                    // rows are used
 #pragma unroll
-                    for (int ky = 0; ky < 3; ++ky) {
-                        const WinRow& r = win[(U + 2 - ky) % 3];   // ring row s + 2 - ky
+                    for (int ky = 2; ky >= 0; --ky) {
+                        const WinRow& r = win[(U + 2 - ky) % 3];
                         lo = dot2<F16>(r.lo[w][q + 1], wa[2 * w][ky], lo);
                         lo = dot2<F16>(r.lo[w][q], wb[2 * w][ky], lo);
                         hi = dot2<F16>(r.hi[w][q + 1], wa[2 * w + 1][ky], hi);
@@ -402,18 +405,15 @@ __global__ __launch_bounds__(64 * (kDwtCompute + 1), 1) void dgrad_dwtile_kernel
                         __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(d));
                         __builtin_nontemporal_store(f32x4{o[4], o[5], o[6], o[7]}, reinterpret_cast<f32x4*>(d + 4));
                     } else {
+                        // round to nearest even in hardware (v_cvt_pk_bf16_f32,
+                        // v_cvt_f16_f32)
                         u32x4 v;
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
-                            uint32_t l2, h2;
-                            if (a.out_mode == OUT_BF16) {
-                                l2 = f32_to_bf16(o[2 * m]);
-                                h2 = f32_to_bf16(o[2 * m + 1]);
-                            } else {
-                                l2 = __builtin_bit_cast(uint16_t, (_Float16)o[2 * m]);
-                                h2 = __builtin_bit_cast(uint16_t, (_Float16)o[2 * m + 1]);
-                            }
-                            v[m] = l2 | (h2 << 16);
+                            if (a.out_mode == OUT_BF16)
+                                v[m] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)o[2 * m], (__bf16)o[2 * m + 1]});
+                            else
+                                v[m] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)o[2 * m], (_Float16)o[2 * m + 1]});
                         }
                         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.dx) + e));
                     }
