@@ -87,11 +87,10 @@ __device__ __forceinline__ void store8(void* out, int mode, int64_t e, const flo
         if (mode == OUT_FP16) {
             lo = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i]);
             hi = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1]);
+            p[i] = lo | (hi << 16);
         } else {
-            lo = f32_to_bf16(v[2 * i]);
-            hi = f32_to_bf16(v[2 * i + 1]);
+            p[i] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[2 * i], (__bf16)v[2 * i + 1]});   // one v_cvt_pk_bf16_f32
         }
-        p[i] = lo | (hi << 16);
     }
     __builtin_nontemporal_store(p, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e));
 }
@@ -534,11 +533,10 @@ __device__ __forceinline__ void store4v(void* out, int mode, int64_t e, const fl
         if (mode == OUT_FP16) {
             lo = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i]);
             hi = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1]);
+            p[i] = lo | (hi << 16);
         } else {
-            lo = f32_to_bf16(v[2 * i]);
-            hi = f32_to_bf16(v[2 * i + 1]);
+            p[i] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[2 * i], (__bf16)v[2 * i + 1]});   // one v_cvt_pk_bf16_f32
         }
-        p[i] = lo | (hi << 16);
     }
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e) = p;
 }

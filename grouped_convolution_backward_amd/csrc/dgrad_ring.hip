@@ -232,10 +232,11 @@ __global__ __launch_bounds__(384, 1) void dgrad_ring_kernel(const DgradRingArgs 
                         } else {
                             u32x4 p;
                             if (a.out_mode == OUT_BF16) {
+                                // one v_cvt_pk_bf16_f32 per pair
 #pragma unroll
                                 for (int h = 0; h < 2; ++h) {
-                                    p[h] = (uint32_t)f32_to_bf16(lo[2 * h]) | ((uint32_t)f32_to_bf16(lo[2 * h + 1]) << 16);
-                                    p[2 + h] = (uint32_t)f32_to_bf16(hi4[2 * h]) | ((uint32_t)f32_to_bf16(hi4[2 * h + 1]) << 16);
+                                    p[h] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo[2 * h], (__bf16)lo[2 * h + 1]});
+                                    p[2 + h] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)hi4[2 * h], (__bf16)hi4[2 * h + 1]});
                                 }
                             } else {
 #pragma unroll
