@@ -109,7 +109,7 @@ def algorithmic(cfg, info):
 # the exact bytes of these files
 _FAMILY_SOURCES = (("wgrad_rowslab", "rowslab.hip"), ("wgrad_ring", "ring.hip"), ("wgrad_mfma", "kernels.hip"),
                    ("wgrad_dwtile", "dwtile.hip"), ("wgrad_dw", "depthwise.hip"), ("dgrad_ring", "dgrad_ring.hip"),
-                   ("dgrad_", "dgrad.hip"))
+                   ("dgrad_dwtile", "dwtile.hip"), ("dgrad_", "dgrad.hip"))
 _SHARED_SOURCES = ("device_common.hpp", "wgrad_internal.hpp", "dgrad_internal.hpp", "magic.hpp")
 
 
@@ -161,7 +161,8 @@ def measured_mfma(workload, plan_name):
 _KERNEL_FN = (("wgrad_rowslab_", "rowslab_kernel"), ("wgrad_ring_", "ring_kernel"), ("wgrad_mfma_", "mfma_kernel"),
               ("wgrad_dwtile_", "dwtile_kernel"), ("wgrad_dwstrip_", "dw3_kernel"), ("wgrad_dwwin_", "dw2_kernel"),
               ("wgrad_dw_", "dw_kernel"),
-              ("dgrad_ring_", "dgrad_ring_kernel"), ("dgrad_dwring_", "dgrad_dw_ring_kernel"),
+              ("dgrad_ring_", "dgrad_ring_kernel"), ("dgrad_dwtile_", "dgrad_dwtile_kernel"),
+              ("dgrad_dwring_", "dgrad_dw_ring_kernel"),
               ("dgrad_dw_", "dgrad_dw_kernel"), ("dgrad_mfma_", "dgrad_kernel"))
 COPY_BYTES = 256 * 2 ** 20   # --copy-calibration: torch.neg over this many bytes, read and written
 

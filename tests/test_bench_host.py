@@ -171,3 +171,23 @@ def test_counter_ingestion_finds_main_kernels_and_scales_by_the_copy(tmp_path, m
     assert m["busy_frac_of_simd_cycles"] == round(8257536.0 / (4 * 7805507.0), 4)
     with pytest.raises(ValueError):
         bench.ingest_counters([("c3", str(fetch))], out_dir=str(tmp_path / "profiles"))
+
+
+def test_every_benchmarked_plan_maps_to_its_kernel_and_sources():
+    """The trace and counter summaries find each workload's main kernel by
+    the function its plan name maps to, and traffic records are keyed by
+    that kernel's source files: every plan the bench runs (both directions)
+    must map to both."""
+    import grouped_convolution_backward_amd as gcb
+    for name in list(workloads.CONFIGS) + list(workloads.WIDER):
+        cfg = workloads.get(name)
+        for plan in (gcb.Plan(cfg, hip_device=-1), gcb.DgradPlan(cfg, hip_device=-1)):
+            fn = bench.kernel_fn(plan.name)
+            assert fn.endswith("_kernel"), (name, plan.name, fn)
+            assert [f for pre, f in bench._FAMILY_SOURCES if plan.name.startswith(pre)], plan.name
+    # the depthwise forms bench.py reaches through overrides
+    c5 = workloads.get("c5")
+    for tile, fn in ((3, "dw3_kernel"), (4, "dwtile_kernel")):
+        assert bench.kernel_fn(gcb.Plan(c5, hip_device=-1, variant=gcb.VARIANT_DEPTHWISE, tile=tile).name) == fn
+    for tile, fn in ((4, "dgrad_dw_ring_kernel"), (7, "dgrad_dwtile_kernel")):
+        assert bench.kernel_fn(gcb.DgradPlan(c5, hip_device=-1, tile=tile).name) == fn
