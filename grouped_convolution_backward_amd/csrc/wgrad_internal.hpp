@@ -57,7 +57,8 @@ constexpr RsInstance kRsInstances[] = {
     {64, 64, 3, 2, 1, 64, 2, 3, 1},    // one row up to 31 wide, stride 2
     {32, 32, 3, 4, 2, 32, 1, 4, 1},    // two rows up to 30 wide
     {32, 32, 3, 4, 1, 80, 1, 4, 1},    // one row (or segment) up to 64 wide
-    {32, 32, 5, 8, 1, 144, 1, 2, 1},   // 128-position row segments, width-5 filter
+    {32, 32, 5, 4, 1, 80, 1, 4, 1},    // width-5 filter: 64-position segments, 4 buffers (faster than
+                                       // 128-position ones with 2: more slabs in flight per CU)
     {64, 64, 1, 2, 1, 32, 1, 4, 1},    // pointwise (width-1 filter): 32-position row segments
     {64, 64, 1, 2, 1, 64, 2, 3, 1},    // pointwise, stride 2: 32-position segments
     {32, 32, 1, 4, 1, 64, 1, 4, 1},    // pointwise, 32-channel blocks
