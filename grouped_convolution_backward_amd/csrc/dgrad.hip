@@ -121,9 +121,17 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = xcd_logical_id(blockIdx.x, a.total_wg);
     // phase fastest: the phases of one tile read the same dY rows (PH: the
-    // problem has a stride above 1; without, one phase and every tap)
+    // problem has a stride above 1; without, one phase and every tap). The
+    // phases differ in work (1, 2, 2 and 4 taps at stride 2 with a 3x3
+    // filter), and when the whole grid is resident the workgroups that share
+    // a CU are the ones whose logical ids differ by the CUs of one XCD; so the
+    // phase order within each group of tiles is rotated by one per CU round
+    // (ph_rot groups), which gives each CU different phases. Unrotated, every
+    // CU held workgroups of a single phase and the 4-tap CUs ran 2.4x longer
+    // than the 1-tap ones (strided c3: kernel 26.6 us, its CUs ending between
+    // 11 and 26.6 us).
     int r = L;
-    const int phase = PH ? r % a.phases : 0;
+    const int phase = PH ? (r % a.phases + (r / a.phases / a.ph_rot) % a.phases) % a.phases : 0;
     if (PH) r /= a.phases;
     const int mt = r % a.tiles_m;
     r /= a.tiles_m;

@@ -37,6 +37,7 @@ struct DgradArgs {
     int16_t t0[3][kDgMaxStride], nt[3][kDgMaxStride], o0[3][kDgMaxStride];
     int32_t qd, qh, qw;            // phase grid: ceil(Di / sd), ceil(Hi / sh), ceil(Wi / sw)
     int32_t phases;                // sd * sh * sw
+    int32_t ph_rot;                // phase groups per CU round (rotation of the phase order, see the kernel)
     int32_t M;                     // N * qd * qh * qw positions per phase
     int32_t kchunks;               // ceil(gkpg / 32)
     uint32_t dy_bytes, w_bytes;    // buffer sizes for the bounds-checked loads

@@ -1033,6 +1033,7 @@ int build_dgrad_plan(const wgrad_problem& p, const wgrad_overrides* ov, const De
     }
     a.qd = (int32_t)qd; a.qh = (int32_t)qh; a.qw = (int32_t)qw;
     a.phases = (int32_t)phases;
+    a.ph_rot = (int32_t)std::max<int64_t>(1, dev.num_cus / 8 / phases);
     a.M = (int32_t)Mq;
     const int bk = 32;   // channels per reduction chunk (the kernel's BK)
     a.kchunks = (int32_t)ceil_div(gkpg, bk);
