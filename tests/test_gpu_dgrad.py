@@ -151,6 +151,31 @@ def test_dgrad_edge_shapes(i):
     check_tol(cfg, vals, dx64, ab64)
 
 
+# Stride phases with grids large enough that the kernel rotates the phase
+# order within groups of tiles (2D stride 2 and 3, mixed strides, 3D stride
+# 2: 4, 9, 6 and 8 phases). A rotation that were not a permutation would
+# leave some phase of some tile unwritten (NaN) and write another twice.
+PHASED = [
+    (2, 1, 2, 64, 64, (64, 64), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1), "bf16", None),
+    (2, 1, 2, 32, 32, (72, 72), (3, 3), (3, 3), (1, 1), (1, 1), (1, 1), "fp16", None),
+    (2, 1, 2, 32, 32, (48, 72), (3, 3), (2, 3), (1, 1), (1, 1), (1, 1), "bf16", "fp32"),
+    (3, 1, 2, 32, 32, (8, 32, 32), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), (1, 1, 1), "bf16", None),
+]
+
+
+@pytest.mark.parametrize("i", range(len(PHASED)))
+def test_dgrad_stride_phase_rotation(i):
+    cfg = prob(*PHASED[i], name=f"phased{i}")
+    dyb, wb = draw(cfg, "int", (700 + i, 800 + i))
+    _, bits, p = run_dgrad(cfg, dyb, wb)
+    assert p.name.startswith("dgrad_mfma_"), p.name
+    phases = int(np.prod(cfg["stride"]))
+    # more tile groups than one XCD's CUs take per phase: the order rotates
+    assert p.info["grid_main"] // phases > max(1, 32 // phases), p.info["grid_main"]
+    dx64, _ = oracle.dgrad(cfg, dyb, wb)
+    check_exact(cfg, bits, dx64)
+
+
 @pytest.mark.parametrize("tile", [1, 2, 3])
 def test_dgrad_every_tile(tile):
     cfg = prob(2, 2, 2, 72, 40, (11, 13), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1), name=f"tile{tile}")
