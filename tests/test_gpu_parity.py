@@ -259,6 +259,8 @@ ROWSLAB_CASES = [
     ("c3", dict(N=1, K=96, in_len=(20, 30), out_len=(10, 15))),  # fp16, narrow rows
     ("c4a", dict(N=3)),                                          # merged groups, Gm = 4
     ("c4b", dict(N=2, in_len=(300,), out_len=(300,))),           # 1D, row segments with a tail
+    ("c4b", dict(N=3, in_len=(65,), pad_lo=(0,), pad_hi=(4,))),  # width 5: 64-position segment + 1-position tail
+    ("c4b", dict(N=2, in_len=(64,), in_dtype="fp16", out_dtype="fp32")),   # one whole segment per row, S = 1
     ("c2", dict(N=1, C=128, K=64, in_len=(10, 200), out_len=(10, 200))),   # wide rows: segments
     ("c2", dict(N=2, pad_lo=(0, 0), pad_hi=(2, 2))),             # asymmetric pad
     # stride 2 with more M blocks: ragged (136 = 2*64 + 8), whole (256), grouped (G = 2, 192 rows each)
