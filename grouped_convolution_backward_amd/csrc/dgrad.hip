@@ -98,8 +98,17 @@ __device__ __forceinline__ void store8(void* out, int mode, int64_t e, const flo
 template <int BM, int BN, int BK, int WM, int WN, int V, bool PH, bool F16>
 __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     typedef typename VecT<V>::T VT;
-    // BK output channels per reduction chunk; A rows padded by 16 bytes
-    constexpr int PA = BK + 8;
+    // BK output channels per reduction chunk. A rows are BK elements (64
+    // bytes) with their 16-byte chunks XOR-swizzled by bits 2-3 of the row
+    // (a_off): the 16 rows a 16-lane group reads at one chunk, and the 4
+    // rows x 4 chunks a 16-lane group stores, each cover all 64 banks once.
+    // (Rows padded to 80 bytes instead, the stores of 4 rows wrapped onto the
+    // same banks: with the B stores below, a quarter of the LDS-active cycles
+    // of the strided c3 launch were bank conflicts. Removing them took 0.2 us
+    // off the 3D shape and the pointwise one and left c3 where it was: the
+    // conflicts were mostly off the critical path.)
+    constexpr int PA = BK;
+    static_assert(BK == 32, "A swizzle: four 16-byte chunks per row");
     constexpr int PB = BN + kLdsPad;               // B row pitch for the transposed reads
     constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -112,8 +121,23 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
     static_assert(A_LOADS + B_LOADS <= 63, "vmcnt range");
 
     // two LDS stages: chunk c is computed from stage c % 2 while chunk c + 1
-    // is stored into the other one; the epilogue reuses the space
-    constexpr int LDS_ELEMS = 2 * BM * PA + 2 * BK * PB;
+    // is stored into the other one; the epilogue reuses the space (sized as
+    // with 80-byte A rows, so that its passes stay as wide)
+    constexpr int LDS_ELEMS = 2 * BM * (BK + 8) + 2 * BK * PB;
+    auto a_off = [](int row, int e) { return row * PA + ((((e >> 3) ^ (row >> 2)) & 3) << 3) + (e & 7); };
+    // B stores: with 64-channel rows of 16-byte vectors a 16-lane group
+    // stores two rows, and on the 192-byte B pitch rows one apart share banks
+    // while rows two apart do not, so each group takes rows r and r + 2 (a
+    // permutation of the chunk's rows)
+    auto b_row_of = [](int idx) {
+        if constexpr (BN == 64 && V == 8) {
+            static_assert(PB == 96 && BK * BN / V == 256, "B store order: one vector per thread, 192-byte rows");
+            const int g = idx >> 4;
+            return ((g >> 1) << 2) + (g & 1) + (((idx >> 3) & 1) << 1);
+        } else {
+            return idx / (BN / V);
+        }
+    };
     __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
     uint16_t* const sA[2] = {lds, lds + BM * PA};
     uint16_t* const sB[2] = {lds + 2 * BM * PA, lds + 2 * BM * PA + BK * PB};
@@ -184,7 +208,7 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
 #pragma unroll
     for (int p = 0; p < B_LOADS; ++p) {
         const int idx = tid + p * 256;
-        const int row = idx / BVR, cv = (idx - row * BVR) * V;
+        const int row = b_row_of(idx), cv = (idx % BVR) * V;
         const int c = c0 + cv;
         const int gc = (int)magic_div((uint32_t)c, a.mcpg);
         b_row[p] = row;
@@ -268,12 +292,12 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
 #pragma unroll
         for (int p = 0; p < A_LOADS; ++p) {
             const int row = tid / AV + p * (256 / AV);
-            *reinterpret_cast<VT*>(sa + row * PA + a_kv) = ra[p];
+            *reinterpret_cast<VT*>(sa + a_off(row, a_kv)) = ra[p];
         }
 #pragma unroll
         for (int p = 0; p < B_LOADS; ++p) {
             const int idx = tid + p * 256;
-            const int row = idx / BVR, cv = (idx - row * BVR) * V;
+            const int row = b_row_of(idx), cv = (idx % BVR) * V;
             if (row < BK) *reinterpret_cast<VT*>(sb + row * PB + cv) = rb[p];
         }
     };
@@ -305,7 +329,7 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const DgradArgs a) {
             // A operand: row lane%32 of the wave's block, k = 8*(lane/32) .. +7
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const i16x8*>(sa + (wm0 + i * 32 + (lane & 31)) * PA + ks * 16 + 8 * (lane >> 5));
+                af[i] = *reinterpret_cast<const i16x8*>(sa + a_off(wm0 + i * 32 + (lane & 31), ks * 16 + 8 * (lane >> 5)));
 #pragma unroll
             for (int j = 0; j < FN; ++j) bf[j] = tr_frag(sb + (ks * 16 + frag_row) * PB + wn0 + j * 32 + frag_col, PB);
 #pragma unroll
