@@ -173,7 +173,9 @@ size_t wgrad_workspace_bytes(const wgrad_plan_t* plan);
  * atomics, so the same plan on the same inputs gives the same bits.
  * x, dy, dw are device pointers aligned to 16 bytes; ws is a device pointer
  * of at least wgrad_workspace_bytes(plan) bytes (may be NULL when that is 0).
- * Runs on one stream may not share a workspace concurrently.
+ * A plan may be shared by runs on several streams and host threads at once;
+ * runs that may overlap in time must each have a workspace (and dW) of
+ * their own.
  * Errors: WGRAD_ERR_INVALID_ARG (NULL or misaligned pointer, ws too small),
  * WGRAD_ERR_HIP (launch failure).
  */
