@@ -143,7 +143,7 @@ def _cases():
 
 
 def _regular(op, cfg, ov):
-    """The same plan through the regular library: the driver's output line."""
+    """The same plan through the regular library, in the line format plan_driver prints."""
     kw = dict(split_k=ov[0], group_merge=ov[1], variant=ov[2], tile=ov[3])
     try:
         p = (gcb.Plan if op == 0 else gcb.DgradPlan)(cfg, hip_device=-1, **kw)
