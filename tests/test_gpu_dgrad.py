@@ -160,6 +160,9 @@ PHASED = [
     (2, 1, 2, 32, 32, (72, 72), (3, 3), (3, 3), (1, 1), (1, 1), (1, 1), "fp16", None),
     (2, 1, 2, 32, 32, (48, 72), (3, 3), (2, 3), (1, 1), (1, 1), (1, 1), "bf16", "fp32"),
     (3, 1, 2, 32, 32, (8, 32, 32), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), (1, 1, 1), "bf16", None),
+    # grouped: four groups, and eight merged two at a time with one-sided pads
+    (2, 4, 2, 32, 32, (48, 48), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1), "bf16", None),
+    (2, 8, 1, 16, 24, (40, 40), (3, 3), (2, 2), (1, 1), (0, 0), (1, 1), "fp16", "fp32"),
 ]
 
 
